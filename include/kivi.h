@@ -1,0 +1,186 @@
+/*
+ * kivi.h -- C ABI of libkivi, a gfx950 (MI355X) library for single-token
+ * decode attention over a KIVI-style asymmetrically quantized KV cache.
+ *
+ * Sources (web pages; cited by page and section, never by line):
+ *   [P1] discosf.com KIVI tutorial (news/3594501): section 2.1 (KV-cache size
+ *        formula; keys have per-channel outliers, values do not), section 3.1
+ *        (group-wise quantization plus an fp16 remainder window), section 3.2
+ *        (value cache management), section 5.2 (parameters nbits,
+ *        q_group_size, residual_length).
+ *   [P2] unite.ai "KV cache quantization axis selection guide": section on
+ *        what quantization error is made of (uniform min/step quantizer,
+ *        step = range / (2^B - 1), error <= step/2), section on keys (outliers
+ *        sit in fixed channels, so keys are grouped per channel), section on
+ *        values (values are grouped per token), section on the systems tax
+ *        (recent tokens stay full precision until enough accumulate).
+ *
+ * Everything here is asynchronous on the caller's HIP stream.  The library
+ * never allocates, frees or synchronises; every buffer is caller-owned device
+ * memory (for example torch tensors) in the layouts documented below, dense
+ * and contiguous.  No C++ exception crosses this boundary.  Calls on
+ * different caches are independent and reentrant; a cache must not be
+ * touched concurrently from two streams.
+ */
+#ifndef KIVI_H
+#define KIVI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes (host side) ------------------------------------------ */
+#define KIVI_OK            0
+#define KIVI_EINVAL       -1  /* bad dims, null pointer, bad scalar argument  */
+#define KIVI_ENOSPC       -2  /* workspace smaller than kivi_decode_workspace_bytes */
+#define KIVI_EHIP         -3  /* a kernel launch failed (hipGetLastError)      */
+#define KIVI_EUNSUPPORTED -4  /* valid dims that no compiled kernel covers     */
+
+/* ---- sticky device status bits, OR-ed into *status by kernels ----------- */
+#define KIVI_ST_RESIDUAL_FULL 0x1u /* append found r_len == R: token dropped  */
+#define KIVI_ST_CAPACITY      0x2u /* flush/prefill would pass capacity       */
+#define KIVI_ST_BAD_LENGTH    0x4u /* a length array held an impossible value */
+
+/*
+ * Problem dimensions.  The names follow the pages' parameters:
+ *   bits      B, the code width ("nbits", [P1] section 5.2); 2 or 4.
+ *   group     G, tokens per key group and channels per value group
+ *             ("q_group_size", [P1] sections 3.1 and 5.2).  Must divide
+ *             head_dim, residual and capacity.
+ *   residual  R, the fp16 window length ("residual_length", [P1] 3.1/5.2);
+ *             a multiple of G.
+ *   capacity  quantized tokens each sequence can hold; a multiple of G.
+ *   batch, heads, head_dim as in the cache-size formula of [P1] section 2.1.
+ * Host validation (kivi_validate_dims): all > 0 except capacity >= 0,
+ * bits in {2,4}, head_dim % group == 0, residual % group == 0,
+ * capacity % group == 0, (head_dim * bits) % 32 == 0.
+ * Compiled kernels cover head_dim == 128 and group in {32, 64, 128};
+ * other valid dims return KIVI_EUNSUPPORTED.
+ */
+typedef struct {
+  int32_t batch, heads, head_dim, bits, group, residual, capacity;
+} kivi_dims;
+
+/*
+ * The cache.  W = head_dim * bits / 32 words per token; D = head_dim.
+ *
+ *   k_codes  uint32 [batch][heads][capacity/G][W][G]
+ *   v_codes  uint32 [batch][heads][capacity/G][W][G]
+ *       Codes are stored in tiles of G consecutive tokens.  Inside a tile,
+ *       word (w, t) holds the codes of token t of the tile for channels
+ *       w*(32/B) + i, i in [0, 32/B); channel w*(32/B)+i sits at bits
+ *       [i*B, i*B + B) (least significant first).  Token n of a sequence is
+ *       in tile n / G at position n % G.
+ *   k_scale, k_zero  fp16 [batch][heads][capacity/G][D]
+ *       Per key group (G consecutive tokens x 1 channel): the step and the
+ *       group minimum ([P2] keys section; [P1] section 3.1).
+ *   v_scale, v_zero  fp16 [batch][heads][capacity][D/G]
+ *       Per value group (1 token x G consecutive channels): step and minimum
+ *       ([P2] values section; [P1] section 2.1).
+ *   k_res, v_res     fp16 [batch][heads][R][D]   the fp16 window.
+ *   q_len  int32 [batch]  quantized tokens held (multiple of G, <= capacity)
+ *   r_len  int32 [batch]  window tokens held, 0 <= r_len <= R
+ *   status uint32 [1]     sticky KIVI_ST_* bits (caller clears it).
+ * Sequence b's context is its q_len[b] quantized tokens followed by its
+ * r_len[b] window tokens, oldest first.
+ *
+ * Dequantized value of a code c with step s and minimum z: z + c * s.
+ * Quantizer (fixed fp32 sequence, identical in every kernel that encodes):
+ *   mn = min(x) + 0.0f; mx = max(x); s = fp16_rne((mx - mn) / (2^B - 1));
+ *   c = s == 0 ? 0 : clamp(rint_half_even((x - mn) / (float)s), 0, 2^B - 1);
+ *   stored zero = fp16(mn) (exact), stored scale = s.
+ * ([P2] quantization-error section: zero-point = minimum, step = range over
+ *  the number of levels, round to the nearest step.)
+ */
+typedef struct {
+  void *k_codes, *k_scale, *k_zero;
+  void *v_codes, *v_scale, *v_zero;
+  void *k_res, *v_res;
+  int32_t *q_len, *r_len;
+  uint32_t *status;
+} kivi_cache;
+
+/* Host-only check of dims; KIVI_OK, KIVI_EINVAL or KIVI_EUNSUPPORTED. */
+int kivi_validate_dims(const kivi_dims *dims);
+
+/*
+ * Append one new token per sequence to the fp16 window ([P1] section 3.2:
+ * new tokens enter the window in fp16).
+ *   k_new, v_new  fp16 [batch][heads][D], device.
+ * For every b with r_len[b] < R: writes slot r_len[b] of k_res/v_res, then
+ * r_len[b] += 1.  A sequence with r_len[b] >= R (or a negative r_len) is left
+ * unchanged and KIVI_ST_RESIDUAL_FULL (or KIVI_ST_BAD_LENGTH) is set.
+ */
+int kivi_append_kv(const kivi_dims *dims, const kivi_cache *cache,
+                   const void *k_new, const void *v_new, void *stream);
+
+/*
+ * Flush full windows ([P1] section 3.1: once R tokens have accumulated they
+ * are quantized group-wise and the window is emptied; [P2] systems section).
+ * For every b with r_len[b] == R: window tokens [0, R) are quantized (keys as
+ * R/G per-channel groups, values as R per-token groups of G channels) into
+ * quantized token slots [q_len[b], q_len[b] + R); then q_len[b] += R and
+ * r_len[b] = 0.  Sequences with r_len[b] < R are untouched.  If
+ * q_len[b] + R > capacity the sequence is untouched and KIVI_ST_CAPACITY is
+ * set.  Implemented as two kernels (quantize, then commit) on the stream.
+ */
+int kivi_flush_residual(const kivi_dims *dims, const kivi_cache *cache,
+                        void *stream);
+
+/*
+ * Initialise every sequence from a prompt (the remainder split of [P1]
+ * section 3.1).  k, v: fp16 [batch][heads][src_len][D], device.
+ * len: device int32 [batch], tokens of sequence b, 0 <= len[b] <= src_len.
+ * res: device int32 [batch] window tokens to keep, or NULL for len[b] % G.
+ * Tokens [0, len-res) are quantized into slots [0, len-res) and tokens
+ * [len-res, len) are copied to window slots [0, res); then q_len[b] =
+ * len-res, r_len[b] = res.  Sequences whose len-res is not a multiple of G,
+ * or with res outside [0, R] or len outside [0, src_len], are left with
+ * q_len = r_len = 0 and KIVI_ST_BAD_LENGTH set; len-res > capacity sets
+ * KIVI_ST_CAPACITY likewise.  Codes are bit-identical to those that appends
+ * plus flushes of the same tokens produce.
+ */
+int kivi_prefill(const kivi_dims *dims, const kivi_cache *cache,
+                 const void *k, const void *v, int32_t src_len,
+                 const int32_t *len, const int32_t *res, void *stream);
+
+/*
+ * Bytes of workspace kivi_decode_attn needs for these dims (a function of
+ * batch, heads, bits, group, residual and capacity only).
+ */
+size_t kivi_decode_workspace_bytes(const kivi_dims *dims);
+
+/* Number of token splits per (sequence, head) kivi_decode_attn launches. */
+int kivi_decode_splits(const kivi_dims *dims);
+
+/*
+ * Decode attention for one new query token per (sequence, head):
+ *   out[b,h,:] = softmax(sm_scale * q[b,h,:] . Khat^T) . Vhat
+ * over the q_len[b] dequantized tokens followed by the r_len[b] fp16 window
+ * tokens ([P2] values section: the output is a softmax-weighted sum of the
+ * value vectors; [P2] "why the KV cache matters": the whole cache is read for
+ * every generated token).  An empty context gives out = 0.
+ *   q        fp16 [batch][heads][D], device
+ *   out      fp32 [batch][heads][D], device (written)
+ *   workspace  device buffer of at least kivi_decode_workspace_bytes(dims)
+ *            bytes.  It must be zero-filled before its first use; every call
+ *            leaves it zero-filled again.  One workspace must not be used by
+ *            two calls that can run at the same time.
+ * Read-only on the cache.  A sequence whose lengths are impossible (q_len not
+ * a multiple of G or above capacity, r_len outside [0, R]) gets out = 0 and
+ * KIVI_ST_BAD_LENGTH.  Returns KIVI_ENOSPC if workspace_bytes is too small.
+ */
+int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache,
+                     const void *q, float *out, float sm_scale,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a return code. */
+const char *kivi_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KIVI_H */
