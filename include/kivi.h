@@ -89,7 +89,7 @@ typedef struct {
  *
  * Dequantized value of a code c with step s and minimum z: z + c * s.
  * Quantizer (fixed fp32 sequence, identical in every kernel that encodes):
- *   mn = min(x) + 0.0f; mx = max(x); s = fp16_rne((mx - mn) / (2^B - 1));
+ *   mn = min(x) + 0.0f; mx = max(x) + 0.0f; s = fp16_rne((mx - mn) / (2^B - 1));
  *   c = s == 0 ? 0 : clamp(rint_half_even((x - mn) / (float)s), 0, 2^B - 1);
  *   stored zero = fp16(mn) (exact), stored scale = s.
  * ([P2] quantization-error section: zero-point = minimum, step = range over

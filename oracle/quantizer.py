@@ -17,8 +17,10 @@ The exact fp32 operation sequence (one IEEE rounding per operation, round to
 nearest even, no fused multiply-add), which the GPU encoder must reproduce
 bit for bit:
 
-1. ``mn = float32(min x) + 0.0`` (turns -0 into +0), ``mx = float32(max x)``;
-   both exact because x is fp16.
+1. ``mn = float32(min x) + 0.0``, ``mx = float32(max x) + 0.0`` (adding +0
+   turns a -0 into +0, so neither the stored zero-point nor the step of an
+   all-zero group depends on the order of signed zeros); both exact because
+   x is fp16.
 2. ``step32 = (mx - mn) / float32(2^B - 1)``.
 3. ``scale = float16(step32)`` (round to nearest even); ``s = float32(scale)``.
 4. ``code = 0`` if ``s == 0``, else
@@ -47,7 +49,7 @@ def quantize_groups(x, bits):
         raise ValueError("quantizer input must be finite")
     levels = F32(2 ** bits - 1)
     mn = (xf.min(axis=-1) + F32(0.0)).astype(F32)          # step 1
-    mx = xf.max(axis=-1).astype(F32)
+    mx = (xf.max(axis=-1) + F32(0.0)).astype(F32)
     step32 = ((mx - mn).astype(F32) / levels).astype(F32)   # step 2
     scale = step32.astype(np.float16)                       # step 3
     s = scale.astype(F32)
