@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-KV decode hot path on one MI355X.
+
+One step = the whole hot path for one batch: append the new token of every
+(sequence, head) to the fp16 window, decode attention over the full context,
+flush the now-full window into 2-bit codes.  Default workload: the
+Llama-2-7B-shaped layer (batch 8, 32 heads, head_dim 128, 3968 quantized +
+128 window tokens at decode time, B=2, G=32, R=128), synthetic seeded data.
+
+Each timed step runs on its own copy of the cache, all copies in the same
+starting state (3968 quantized + 127 window tokens), so no step re-reads data
+another step left in the 256 MB Infinity Cache.  The K timed steps are
+captured in one HIP graph and replayed once between two synchronisations;
+HIP events captured around every decode launch give the decode kernel's
+average duration for the roofline.  The CPU oracle is timed beside it on a
+bounded sample of (sequence, head) steps.
+
+Prints one JSON line on stdout; diagnostics go to stderr.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn query-heads/sec over 2-bit KV; achieved HBM GB/s vs peak"
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "bit_kv_cache_decode_amd", "csrc", "kivi_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", type=int, default=2, help="workload number (1-5)")
+    p.add_argument("--bits", type=int, default=None)
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--eager", action="store_true", help="launch steps eagerly instead of a graph")
+    return p.parse_args()
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload_name):
+    """Per-launch HBM bytes of the decode kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_hash() or t.get("workload") != workload_name:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s):
+    """Time the CPU oracle on whole steps (append, decode, flush) of single
+    (sequence, head) pairs of the same workload, until the budget is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import cache as ocache
+
+    cfg = w.config
+    G, B, R = cfg.group, w.bits, cfg.residual
+    pairs = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    done, spent = 0, 0.0
+    with threadpool_limits(limits=1):
+        for b, h in pairs:
+            ql, rl = int(w.q_len[b]), int(w.r_len[b])
+            st = ocache.head_state(w.k[b, h], w.v[b, h], ql, rl - 1, G, B, cfg.capacity, R)
+            t0 = time.perf_counter()
+            st["k_res"][rl - 1] = w.k[b, h, ql + rl - 1]          # append
+            st["v_res"][rl - 1] = w.v[b, h, ql + rl - 1]
+            st["r_len"] = rl
+            ocache.decode_head(w.q[b, h], st, cfg.sm_scale, G, B)  # decode
+            if rl == R:                                           # flush
+                enc = ocache.encode_tokens(st["k_res"], st["v_res"], G, B)
+                g0 = ql // G
+                st["k_codes"][g0:g0 + R // G] = enc["k_codes"]
+                st["v_codes"][g0:g0 + R // G] = enc["v_codes"]
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent >= budget_s:
+                break
+    return {"value": done / spent, "unit": "query-heads/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (sequence, head) steps of the same workload "
+                      f"(append + decode + flush each, numpy, 1 BLAS thread), {spent:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py measures one GPU only: this build has no multi-GPU path "
+            "(decode shards by (sequence, head) with no communication; see DESIGN.md).")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bit_kv_cache_decode_amd import kivi
+    from bit_kv_cache_decode_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    w = wl.generate(args.workload, bits=args.bits)
+    cfg = w.config
+    if np.any(w.r_len < 1):
+        raise SystemExit("the step appends into the window: every sequence needs r_len >= 1")
+    dims = w.dims()
+    Bt, H, D = cfg.batch, cfg.heads, cfg.head_dim
+    K, W = args.steps, args.warmup
+
+    # ---- the starting state: q_len quantized + (r_len - 1) window tokens
+    kt = torch.from_numpy(w.k).cuda()
+    vt = torch.from_numpy(w.v).cuda()
+    base = kivi.KiviCache(**dims)
+    q0 = torch.from_numpy(w.q_len).cuda()
+    r0 = torch.from_numpy(w.r_len - 1).cuda()
+    kivi.prefill(base, kt, vt, q0 + r0, r0)
+    last = torch.from_numpy(w.lengths - 1).cuda().long()
+    bidx = torch.arange(Bt, device="cuda")
+    k_new = kt[bidx, :, last].contiguous()   # [batch, heads, D]
+    v_new = vt[bidx, :, last].contiguous()
+    q = torch.from_numpy(w.q).cuda()
+    del kt, vt
+    torch.cuda.synchronize()
+    assert base.status_bits() == 0
+
+    n_copies = max(K, W)
+    copies = [base]
+    for _ in range(n_copies - 1):
+        c = kivi.KiviCache(**dims)
+        for name, t in base.buffers().items():
+            getattr(c, name).copy_(t)
+        copies.append(c)
+    outs = [torch.empty((Bt, H, D), dtype=torch.float32, device="cuda") for _ in range(n_copies)]
+    ws = kivi.new_workspace(base.dims)
+    cache_bytes = base.nbytes()
+    log(f"workload {cfg.name}: {n_copies} cache copies of {cache_bytes / 1e6:.1f} MB")
+
+    def reset():
+        for c in copies:
+            c.q_len.copy_(q0)
+            c.r_len.copy_(r0)
+
+    def step(i, ev=None):
+        c = copies[i]
+        if ev:
+            ev[0].record()
+        kivi.append_kv(c, k_new, v_new)
+        if ev:
+            ev[1].record()
+        kivi.decode_attn(c, q, cfg.sm_scale, out=outs[i], workspace=ws)
+        if ev:
+            ev[2].record()
+        kivi.flush_residual(c)
+        if ev:
+            ev[3].record()
+
+    # ---- warmup (eager), then back to the starting state
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    eager_out0 = outs[0].clone()
+    reset()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(K):
+                step(i, evs[i])
+        torch.cuda.synchronize()
+        reset()
+        torch.cuda.synchronize()
+
+    # ---- timed region
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K):
+            step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    append_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    decode_us = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    flush_us = 1e3 * float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    replay_ok = bool(torch.equal(outs[0], eager_out0))
+    states_ok = bool(all(c.status_bits() == 0 for c in copies[:K]))
+    if not (replay_ok and states_ok):
+        log(f"WARNING: replay output matches eager: {replay_ok}; status clean: {states_ok}")
+
+    step_s = wall / K
+    qheads = Bt * H
+    dec_bytes = wl.decode_bytes(w.q_len, w.r_len, H, D, w.bits, cfg.group)
+    achieved = dec_bytes / (decode_us * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": qheads / step_s,
+        "unit": "query-heads/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}",
+            "batch": Bt, "heads": H, "head_dim": D, "bits": w.bits, "group": cfg.group,
+            "residual": cfg.residual,
+            "context": int(w.lengths.max()), "quantized_tokens": int(w.q_len.max()),
+            "window_tokens": int(w.r_len.max()),
+            "step": "append + decode + flush, one HIP graph of all timed steps"
+                    if graph is not None else "append + decode + flush, eager launches",
+        },
+        "decode": {"us": decode_us, "query_heads_per_s": qheads / (decode_us * 1e-6),
+                   "algorithmic_bytes": int(dec_bytes), "GBps": achieved},
+        "append_us": append_us,
+        "flush_us": flush_us,
+        "graph_replay_matches_eager": replay_ok,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(cfg.name)},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,139 @@
+// C ABI of libkivi: argument validation, the decode work split, and calls
+// into the kernel launchers.  Host-only C++ (no HIP headers): everything that
+// touches the device is in kivi_kernels.hip.
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "kivi_internal.h"
+
+namespace kivi {
+namespace {
+
+constexpr int kTargetWorkgroups = 4096;  // about 16 per compute unit on 256 CUs
+constexpr int kMaxQuantSplits = 64;
+constexpr int kWindowChunk = 64;
+constexpr int kMaxResidual = 4096;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool supported(const kivi_dims &d) {
+  return d.head_dim == 128 && (d.group == 32 || d.group == 64 || d.group == 128) &&
+         d.residual <= kMaxResidual;
+}
+
+int check_dims(const kivi_dims *d) {
+  if (!d) return KIVI_EINVAL;
+  const int rc = kivi_validate_dims(d);
+  if (rc != KIVI_OK) return rc;
+  return supported(*d) ? KIVI_OK : KIVI_EUNSUPPORTED;
+}
+
+bool cache_ok(const kivi_cache *c) {
+  return c && c->k_codes && c->k_scale && c->k_zero && c->v_codes && c->v_scale && c->v_zero &&
+         c->k_res && c->v_res && c->q_len && c->r_len && c->status;
+}
+
+int hip_rc(int rc) { return rc == 0 ? KIVI_OK : KIVI_EHIP; }
+
+}  // namespace
+
+DecodePlan decode_plan(const kivi_dims &d) {
+  DecodePlan p{};
+  p.chunk = d.bits == 2 ? 512 : 256;
+  const long bh = (long)d.batch * d.heads;
+  const int nchunks = (d.capacity + p.chunk - 1) / p.chunk;
+  p.kper = 1;
+  p.sq = 0;
+  if (nchunks > 0) {
+    const long want = std::max<long>(1, (kTargetWorkgroups + bh - 1) / bh);
+    const int sq = (int)std::min<long>(std::min<long>(nchunks, want), kMaxQuantSplits);
+    p.kper = (nchunks + sq - 1) / sq;
+    p.sq = (nchunks + p.kper - 1) / p.kper;
+  }
+  p.win_chunk = kWindowChunk;
+  p.nr = (d.residual + kWindowChunk - 1) / kWindowChunk;
+  p.splits = p.sq + p.nr;
+  p.part_floats = 4 + (size_t)d.head_dim;
+  const size_t parts = (size_t)bh * p.splits * p.part_floats * sizeof(float);
+  p.counters_off = round_up(parts, 256);
+  p.bytes = p.counters_off + round_up((size_t)bh * sizeof(uint32_t), 256);
+  return p;
+}
+
+}  // namespace kivi
+
+extern "C" {
+
+int kivi_validate_dims(const kivi_dims *d) {
+  if (!d) return KIVI_EINVAL;
+  if (d->batch <= 0 || d->heads <= 0 || d->head_dim <= 0 || d->group <= 0 || d->residual <= 0 ||
+      d->capacity < 0)
+    return KIVI_EINVAL;
+  if (d->bits != 2 && d->bits != 4) return KIVI_EINVAL;
+  if (d->head_dim % d->group || d->residual % d->group || d->capacity % d->group)
+    return KIVI_EINVAL;
+  if ((d->head_dim * d->bits) % 32) return KIVI_EINVAL;
+  return KIVI_OK;
+}
+
+int kivi_append_kv(const kivi_dims *dims, const kivi_cache *cache, const void *k_new,
+                   const void *v_new, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache) || !k_new || !v_new) return KIVI_EINVAL;
+  return kivi::hip_rc(kivi::launch_append(*dims, *cache, k_new, v_new, stream));
+}
+
+int kivi_flush_residual(const kivi_dims *dims, const kivi_cache *cache, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache)) return KIVI_EINVAL;
+  return kivi::hip_rc(kivi::launch_flush(*dims, *cache, stream));
+}
+
+int kivi_prefill(const kivi_dims *dims, const kivi_cache *cache, const void *k, const void *v,
+                 int32_t src_len, const int32_t *len, const int32_t *res, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache) || !len || src_len < 0) return KIVI_EINVAL;
+  if (src_len > 0 && (!k || !v)) return KIVI_EINVAL;
+  return kivi::hip_rc(kivi::launch_prefill(*dims, *cache, k, v, src_len, len, res, stream));
+}
+
+size_t kivi_decode_workspace_bytes(const kivi_dims *dims) {
+  if (kivi::check_dims(dims) != KIVI_OK) return 0;
+  return kivi::decode_plan(*dims).bytes;
+}
+
+int kivi_decode_splits(const kivi_dims *dims) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  return kivi::decode_plan(*dims).splits;
+}
+
+int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache, const void *q, float *out,
+                     float sm_scale, void *workspace, size_t workspace_bytes, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache) || !q || !out || !workspace) return KIVI_EINVAL;
+  if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
+    return KIVI_EINVAL;
+  const kivi::DecodePlan p = kivi::decode_plan(*dims);
+  if (workspace_bytes < p.bytes) return KIVI_ENOSPC;
+  return kivi::hip_rc(kivi::launch_decode(*dims, *cache, p, q, out, sm_scale, workspace, stream));
+}
+
+const char *kivi_strerror(int code) {
+  switch (code) {
+    case KIVI_OK: return "success";
+    case KIVI_EINVAL: return "invalid argument";
+    case KIVI_ENOSPC: return "workspace too small";
+    case KIVI_EHIP: return "HIP kernel launch failed";
+    case KIVI_EUNSUPPORTED: return "dimensions not covered by the compiled kernels";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

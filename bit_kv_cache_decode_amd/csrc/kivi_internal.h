@@ -1,0 +1,42 @@
+// Internal interface between the C ABI layer (kivi_api.cpp) and the HIP
+// kernels (kivi_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kivi.h"
+
+namespace kivi {
+
+// Decode work split.  A quantized split covers `kper` chunks of `chunk`
+// consecutive quantized tokens; a window split covers `win_chunk` window
+// tokens.  Each (sequence, head) gets `sq` quantized splits followed by `nr`
+// window splits; their partial softmax states are merged by the last
+// workgroup of that (sequence, head) to finish.
+struct DecodePlan {
+  int chunk;       // quantized tokens per chunk (multiple of G)
+  int kper;        // chunks per quantized split
+  int sq;          // quantized splits per (sequence, head)
+  int win_chunk;   // window tokens per window split
+  int nr;          // window splits per (sequence, head)
+  int splits;      // sq + nr
+  size_t part_floats;     // floats of partial state per split (2 + D)
+  size_t counters_off;    // byte offset of the per-(sequence, head) tickets
+  size_t bytes;           // total workspace bytes
+};
+
+DecodePlan decode_plan(const kivi_dims &d);
+
+// Kernel launchers (return a hipError_t value as int, 0 on success).
+int launch_append(const kivi_dims &d, const kivi_cache &c, const void *k_new,
+                  const void *v_new, void *stream);
+int launch_flush(const kivi_dims &d, const kivi_cache &c, void *stream);
+int launch_prefill(const kivi_dims &d, const kivi_cache &c, const void *k,
+                   const void *v, int32_t src_len, const int32_t *len,
+                   const int32_t *res, void *stream);
+int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
+                  const void *q, float *out, float sm_scale, void *workspace,
+                  void *stream);
+
+}  // namespace kivi

@@ -1,0 +1,92 @@
+"""Host-side checks of the C ABI (no GPU needed): the shared library loads,
+exports every function include/kivi.h declares, validates dimensions, sizes
+the workspace and rejects bad arguments before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_kv_cache_decode_amd import kivi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kivi.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kivi_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 8
+    L = kivi.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(kivi.EXPORTS) == names
+
+
+def test_validate_dims_codes():
+    ok = kivi.make_dims(8, 32, 128, 2, 32, 128, 4096)
+    assert kivi.validate_dims(ok) == kivi.KIVI_OK
+    bad = [
+        (0, 32, 128, 2, 32, 128, 4096),      # batch
+        (8, 32, 128, 3, 32, 128, 4096),      # bits
+        (8, 32, 100, 2, 32, 128, 4096),      # G does not divide head_dim
+        (8, 32, 128, 2, 32, 100, 4096),      # G does not divide R
+        (8, 32, 128, 2, 32, 128, 4016),      # G does not divide capacity
+        (8, 32, 128, 2, 32, 128, -32),       # negative capacity
+        (8, 32, 8, 2, 8, 8, 64),             # head_dim * bits not a multiple of 32
+    ]
+    for args in bad:
+        assert kivi.validate_dims(kivi.make_dims(*args)) == kivi.KIVI_EINVAL, args
+    # valid but not compiled: head_dim 64, group 16
+    assert kivi.decode_splits(kivi.make_dims(8, 32, 64, 2, 32, 128, 4096)) == kivi.KIVI_EUNSUPPORTED
+    assert kivi.decode_splits(kivi.make_dims(8, 32, 128, 4, 16, 128, 4096)) == kivi.KIVI_EUNSUPPORTED
+    assert kivi.workspace_bytes(kivi.make_dims(8, 32, 64, 2, 32, 128, 4096)) == 0
+
+
+@pytest.mark.parametrize("dims,splits", [
+    ((1, 1, 128, 2, 32, 32, 256), 2),         # 1 quantized split + 1 window split
+    ((8, 32, 128, 2, 32, 128, 4096), 10),     # 8 chunks of 512 + 2 window splits
+    ((16, 40, 128, 2, 32, 128, 2048), 6),
+    ((64, 32, 128, 2, 32, 128, 8320), 4),     # many sequences: few, long splits
+    ((1, 32, 128, 2, 128, 128, 131072), 66),  # long context: 64 quantized splits
+    ((1, 32, 128, 4, 128, 128, 131072), 66),
+    ((1, 1, 128, 2, 32, 32, 0), 1),           # window only
+])
+def test_decode_plan(dims, splits):
+    d = kivi.make_dims(*dims)
+    assert kivi.decode_splits(d) == splits
+    bh = dims[0] * dims[1]
+    ws = kivi.workspace_bytes(d)
+    # partial states (4 + head_dim floats per split) plus one ticket per (sequence, head)
+    assert ws >= bh * splits * (4 + 128) * 4 + bh * 4
+    assert ws % 256 == 0
+
+
+def test_entry_points_reject_bad_arguments_without_a_device():
+    L = kivi.lib()
+    d = kivi.make_dims(2, 2, 128, 2, 32, 32, 256)
+    fake = ctypes.c_void_p(0x1000)
+    cs = kivi.CacheStruct(*([0x1000] * 11))
+    null_cache = kivi.CacheStruct()
+    bad = kivi.make_dims(2, 2, 128, 3, 32, 32, 256)
+    assert L.kivi_append_kv(ctypes.byref(bad), ctypes.byref(cs), fake, fake, None) == kivi.KIVI_EINVAL
+    assert L.kivi_append_kv(ctypes.byref(d), ctypes.byref(null_cache), fake, fake, None) == kivi.KIVI_EINVAL
+    assert L.kivi_append_kv(ctypes.byref(d), ctypes.byref(cs), None, fake, None) == kivi.KIVI_EINVAL
+    assert L.kivi_flush_residual(ctypes.byref(bad), ctypes.byref(cs), None) == kivi.KIVI_EINVAL
+    assert L.kivi_prefill(ctypes.byref(d), ctypes.byref(cs), fake, fake, 64, None, None, None) == kivi.KIVI_EINVAL
+    assert L.kivi_prefill(ctypes.byref(d), ctypes.byref(cs), fake, fake, -1, fake, None, None) == kivi.KIVI_EINVAL
+    need = kivi.workspace_bytes(d)
+    assert L.kivi_decode_attn(ctypes.byref(d), ctypes.byref(cs), fake, fake, ctypes.c_float(1.0),
+                              fake, ctypes.c_size_t(need - 1), None) == kivi.KIVI_ENOSPC
+    assert L.kivi_decode_attn(ctypes.byref(d), ctypes.byref(cs), fake, fake, ctypes.c_float(float("nan")),
+                              fake, ctypes.c_size_t(need), None) == kivi.KIVI_EINVAL
+    assert L.kivi_decode_attn(ctypes.byref(d), ctypes.byref(cs), None, fake, ctypes.c_float(1.0),
+                              fake, ctypes.c_size_t(need), None) == kivi.KIVI_EINVAL
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(L.kivi_strerror(code), bytes)

@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Encoder outputs (codes, zero-points, steps, window rows, lengths) must match
+the oracle bit for bit; decode outputs must be within max-abs 2e-3 and
+relative L2 1e-3 of the oracle's fp64 attention on the same dequantized
+values.  Workloads are the seeded synthetic ones of
+``bit_kv_cache_decode_amd.workloads`` at their full sizes; where the oracle
+would be slow, a fixed sample of (sequence, head) pairs is checked.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from bit_kv_cache_decode_amd import kivi
+from bit_kv_cache_decode_amd import workloads as wl
+from oracle import cache as ocache
+from tests.gpu_common import (assert_head_bit_exact, assert_within_tolerance, gpu_cache,
+                              head_buffers, oracle_head, workload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(c, w):
+    q = torch.from_numpy(w.q).cuda()
+    out = kivi.decode_attn(c, q, w.config.sm_scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _check_heads(c, w, heads, encode=True):
+    out = _decode(c, w)
+    G = w.config.group
+    worst = (0.0, 0.0)
+    for b, h in heads:
+        ref_state = oracle_head(w, b, h)
+        if encode:
+            assert_head_bit_exact(head_buffers(c, b, h), ref_state, G)
+        ref = ocache.decode_head(w.q[b, h], ref_state, w.config.sm_scale, G, w.bits)
+        mx, rel = assert_within_tolerance(out[b, h], ref, f"b={b} h={h}")
+        worst = (max(worst[0], mx), max(worst[1], rel))
+    assert c.status_bits() == 0
+    return worst
+
+
+def test_tiny_single_head_prefill_and_decode():
+    w = workload(1)
+    c = gpu_cache(w)
+    ref = ocache.Cache(1, 1, 128, 2, 32, 32, 256)
+    ref.prefill(w.k, w.v, w.lengths, w.r_len)
+    for name in ("k_codes", "v_codes"):
+        assert np.array_equal(getattr(c, name).cpu().numpy().view(np.uint32), getattr(ref, name)), name
+    for name in ("k_scale", "k_zero", "v_scale", "v_zero", "k_res", "v_res"):
+        assert np.array_equal(getattr(c, name).cpu().numpy().view(np.uint16),
+                              getattr(ref, name).view(np.uint16)), name
+    out = _decode(c, w)
+    assert_within_tolerance(out, ref.decode(w.q, w.config.sm_scale), "tiny")
+
+
+def test_llama2_7b_layer_all_heads():
+    w = workload(2)
+    c = gpu_cache(w)
+    heads = [(b, h) for b in range(8) for h in range(32)]
+    _check_heads(c, w, heads)
+
+
+def test_llama2_13b_layer_all_heads():
+    w = workload(3)
+    c = gpu_cache(w)
+    heads = [(b, h) for b in range(16) for h in range(40)]
+    _check_heads(c, w, heads, encode=False)
+    sample = [(0, 0), (5, 17), (15, 39), (9, 3)]
+    for b, h in sample:
+        assert_head_bit_exact(head_buffers(c, b, h), oracle_head(w, b, h), 32)
+
+
+def test_llama2_13b_flush_of_full_window():
+    """Flush of a full 128-token window per head: bit-exact against the
+    oracle's bulk quantization of the same 2048 tokens, every head."""
+    w = workload(3)
+    c = gpu_cache(w)
+    kivi.flush_residual(c)
+    torch.cuda.synchronize()
+    assert c.q_len.cpu().tolist() == [2048] * 16 and c.r_len.cpu().tolist() == [0] * 16
+    kc = c.k_codes.cpu().numpy().view(np.uint32)
+    vc = c.v_codes.cpu().numpy().view(np.uint32)
+    ks, kz = c.k_scale.cpu().numpy(), c.k_zero.cpu().numpy()
+    vs, vz = c.v_scale.cpu().numpy(), c.v_zero.cpu().numpy()
+    for b in range(16):
+        for h in range(40):
+            enc = ocache.encode_tokens(w.k[b, h, 1920:2048], w.v[b, h, 1920:2048], 32, 2)
+            assert np.array_equal(kc[b, h, 60:64], enc["k_codes"])
+            assert np.array_equal(vc[b, h, 60:64], enc["v_codes"])
+            assert np.array_equal(ks[b, h, 60:64].view(np.uint16), enc["k_scale"].view(np.uint16))
+            assert np.array_equal(kz[b, h, 60:64].view(np.uint16), enc["k_zero"].view(np.uint16))
+            assert np.array_equal(vs[b, h, 1920:2048].view(np.uint16), enc["v_scale"].view(np.uint16))
+            assert np.array_equal(vz[b, h, 1920:2048].view(np.uint16), enc["v_zero"].view(np.uint16))
+    assert c.status_bits() == 0
+
+
+def test_ragged_serving_sampled_heads():
+    w = workload(4)
+    c = gpu_cache(w)
+    assert np.array_equal(c.q_len.cpu().numpy(), w.q_len)
+    assert np.array_equal(c.r_len.cpu().numpy(), w.r_len)
+    rng = np.random.default_rng(404)
+    heads = {(int(b), int(h)) for b, h in zip(rng.integers(0, 64, 48), rng.integers(0, 32, 48))}
+    # the shortest and longest sequences, and ones with empty / full-ish windows
+    for b in {int(np.argmin(w.lengths)), int(np.argmax(w.lengths)), int(np.argmin(w.r_len)),
+              int(np.argmax(w.r_len))}:
+        heads.update({(b, 0), (b, 31)})
+    _check_heads(c, w, sorted(heads))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_long_context_sampled_heads(bits):
+    w = workload(5, bits=bits)
+    c = gpu_cache(w)
+    _check_heads(c, w, [(0, 0), (0, 9), (0, 22), (0, 31)])
+
+
+def test_streaming_appends_and_flushes_match_prefill():
+    """Token-by-token appends with a flush after each, on the GPU, give the
+    same buffers as one GPU prefill and as the oracle's streaming cache."""
+    w = workload(1)
+    n = 200
+    kt = torch.from_numpy(w.k).cuda()
+    vt = torch.from_numpy(w.v).cuda()
+    s = kivi.KiviCache(1, 1, 128, 2, 32, 32, 256)
+    ref = ocache.Cache(1, 1, 128, 2, 32, 32, 256)
+    for t in range(n):
+        kivi.append_kv(s, kt[:, :, t].contiguous(), vt[:, :, t].contiguous())
+        kivi.flush_residual(s)
+        ref.append(w.k[:, :, t], w.v[:, :, t])
+        ref.flush()
+    torch.cuda.synchronize()
+    b = kivi.KiviCache(1, 1, 128, 2, 32, 32, 256)
+    kivi.prefill(b, kt, vt, torch.tensor([n], dtype=torch.int32, device="cuda"),
+                 torch.tensor([n % 32], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert s.q_len.item() == 192 and s.r_len.item() == 8
+    for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+        g = getattr(s, name).cpu().numpy()
+        assert np.array_equal(g, getattr(b, name).cpu().numpy()), name
+        assert np.array_equal(g.view(np.uint8), getattr(ref, name).view(np.uint8)), name
+    assert np.array_equal(s.k_res[0, 0, :8].cpu().numpy(), w.k[0, 0, 192:200])
+    q = torch.from_numpy(w.q).cuda()
+    out = kivi.decode_attn(s, q, w.config.sm_scale).cpu().numpy()
+    assert_within_tolerance(out, ref.decode(w.q, w.config.sm_scale), "streamed")
+
+
+@pytest.mark.parametrize("q_len,r_len", [
+    (0, 0), (0, 1), (0, 32), (32, 0), (224, 0), (224, 32), (192, 31), (32, 1), (256, 0),
+])
+def test_edge_lengths(q_len, r_len):
+    """Empty context, window only, quantized only, full capacity, full
+    window, one token: each against the oracle."""
+    w = workload(1)
+    c = gpu_cache(w, q_len=[q_len], r_len=[r_len])
+    out = _decode(c, w)
+    st = ocache.head_state(w.k[0, 0], w.v[0, 0], q_len, r_len, 32, 2, 256, 32)
+    ref = ocache.decode_head(w.q[0, 0], st, w.config.sm_scale, 32, 2)
+    if q_len + r_len == 0:
+        assert np.all(out == 0)
+    else:
+        assert_within_tolerance(out[0, 0], ref, f"{q_len}+{r_len}")
+    assert_head_bit_exact(head_buffers(c, 0, 0), st, 32)
+
+
+@pytest.mark.parametrize("capacity", [4096, 8192, 65536])
+def test_split_count_does_not_change_the_result(capacity):
+    """The same cache contents decoded with different capacities (hence
+    different work splits: 8 to 64 splits, 1 to 2 chunks each) agree with
+    the oracle."""
+    w = workload(2, batch=2)
+    c = gpu_cache(w, capacity=capacity)
+    out = _decode(c, w)
+    for b in range(2):
+        for h in (0, 13, 31):
+            ref = ocache.decode_head(w.q[b, h], oracle_head(w, b, h), 1.0, 32, 2)
+            assert_within_tolerance(out[b, h], ref, f"cap {capacity}")
+
+
+def test_decode_is_deterministic_and_leaves_workspace_clean():
+    w = workload(2)
+    c = gpu_cache(w)
+    q = torch.from_numpy(w.q).cuda()
+    first = kivi.decode_attn(c, q, 1.0).clone()
+    for _ in range(10):
+        again = kivi.decode_attn(c, q, 1.0)
+        assert torch.equal(again, first)
+    torch.cuda.synchronize()
+    d = c.dims
+    ws = c.workspace.cpu().numpy()
+    bh = d.batch * d.heads
+    tickets = ws[len(ws) - ((bh * 4 + 255) // 256 * 256):][: bh * 4]
+    assert np.all(tickets == 0)
+
+
+def test_status_bits_and_skipped_sequences():
+    w = workload(1)
+    # append into a full window: dropped, flagged
+    c = gpu_cache(w, q_len=[224], r_len=[32])
+    k1 = torch.from_numpy(w.k[:, :, 0]).cuda().contiguous()
+    kivi.append_kv(c, k1, k1)
+    torch.cuda.synchronize()
+    assert c.r_len.item() == 32 and c.status_bits() == kivi.ST_RESIDUAL_FULL
+    # flush past capacity: untouched, flagged
+    c.clear_status()
+    kivi.flush_residual(c)
+    torch.cuda.synchronize()
+    assert c.q_len.item() == 224 and c.r_len.item() == 32 and c.status_bits() == kivi.ST_CAPACITY
+    # impossible lengths: output 0, flagged
+    c.clear_status()
+    c.q_len.fill_(33)
+    out = _decode(c, w)
+    assert np.all(out == 0) and c.status_bits() == kivi.ST_BAD_LENGTH
+    c.clear_status()
+    c.q_len.fill_(224)
+    c.r_len.fill_(40)
+    out = _decode(c, w)
+    assert np.all(out == 0) and c.status_bits() == kivi.ST_BAD_LENGTH
+    # prefill with a window that leaves a partial group: rejected
+    c2 = kivi.KiviCache(1, 1, 128, 2, 32, 32, 256)
+    kt = torch.from_numpy(w.k).cuda()
+    kivi.prefill(c2, kt, kt, torch.tensor([100], dtype=torch.int32, device="cuda"),
+                 torch.tensor([5], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert c2.q_len.item() == 0 and c2.status_bits() == kivi.ST_BAD_LENGTH
+    # default window: len % G
+    c3 = kivi.KiviCache(1, 1, 128, 2, 32, 32, 256)
+    kivi.prefill(c3, kt, kt, torch.tensor([100], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert c3.q_len.item() == 96 and c3.r_len.item() == 4 and c3.status_bits() == 0
+
+
+def test_workspace_too_small_is_rejected():
+    w = workload(1)
+    c = gpu_cache(w)
+    q = torch.from_numpy(w.q).cuda()
+    small = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(kivi.KiviError) as e:
+        kivi.decode_attn(c, q, 1.0, workspace=small)
+    assert e.value.code == kivi.KIVI_ENOSPC
+
+
+def test_byte_model_matches_buffers():
+    """The decode byte model counts exactly the cache bytes a decode reads."""
+    w = workload(1)
+    c = gpu_cache(w)
+    per_head = wl.decode_bytes_per_head(224, 32, 128, 2, 32)
+    k_codes = 224 * 128 * 2 // 8
+    assert per_head == 2 * k_codes + 7 * 128 * 4 + 224 * 4 * 4 + 2 * 32 * 256 + 256 + 512
+    assert c.nbytes() >= per_head - 768
