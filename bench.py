@@ -10,9 +10,11 @@ Llama-2-7B-shaped layer (batch 8, 32 heads, head_dim 128, 3968 quantized +
 Each timed step runs on its own copy of the cache, all copies in the same
 starting state (3968 quantized + 127 window tokens), so no step re-reads data
 another step left in the 256 MB Infinity Cache.  The K timed steps are
-captured in one HIP graph and replayed once between two synchronisations;
-HIP events captured around every decode launch give the decode kernel's
-average duration for the roofline.  The CPU oracle is timed beside it on a
+captured in one HIP graph and replayed once between two synchronisations
+(throughput); the same K steps are then launched eagerly from the same
+starting state with HIP events around every kernel on the launch stream,
+which give the per-kernel GPU durations (the decode kernel's average
+duration feeds the roofline).  The CPU oracle is timed beside it on a
 bounded sample of (sequence, head) steps.
 
 Prints one JSON line on stdout; diagnostics go to stderr.
@@ -49,6 +51,9 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch steps eagerly instead of a graph")
+    p.add_argument("--copy-mb", type=int, default=0,
+                   help="after the run, copy a buffer of this many MiB once (a known-size "
+                        "reference dispatch for scaling hardware byte counters)")
     return p.parse_args()
 
 
@@ -184,35 +189,45 @@ def main():
     reset()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    # ---- timed region 1: the K steps as one HIP graph, replayed once
     graph = None
     if not args.eager:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(K):
-                step(i, evs[i])
+                step(i)
         torch.cuda.synchronize()
         reset()
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        replay_ok = bool(torch.equal(outs[0], eager_out0))
+        states_ok = bool(all(c.status_bits() == 0 for c in copies[:K]))
+        reset()
+        torch.cuda.synchronize()
 
-    # ---- timed region
+    # ---- timed region 2: the same K steps launched eagerly, HIP events
+    # around every kernel on the launch stream (per-kernel GPU durations)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(K):
-            step(i, evs[i])
+    for i in range(K):
+        step(i, evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    eager_wall = time.perf_counter() - t0
+    if graph is None:
+        wall = eager_wall
+        replay_ok = bool(torch.equal(outs[0], eager_out0))
+        states_ok = bool(all(c.status_bits() == 0 for c in copies[:K]))
 
     append_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     decode_us = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     flush_us = 1e3 * float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    replay_ok = bool(torch.equal(outs[0], eager_out0))
-    states_ok = bool(all(c.status_bits() == 0 for c in copies[:K]))
+    decode_p = np.percentile([1e3 * e[1].elapsed_time(e[2]) for e in evs], [10, 50, 90])
     if not (replay_ok and states_ok):
-        log(f"WARNING: replay output matches eager: {replay_ok}; status clean: {states_ok}")
+        log(f"WARNING: graph output matches eager: {replay_ok}; status clean: {states_ok}")
 
     step_s = wall / K
     qheads = Bt * H
@@ -240,14 +255,24 @@ def main():
             "step": "append + decode + flush, one HIP graph of all timed steps"
                     if graph is not None else "append + decode + flush, eager launches",
         },
-        "decode": {"us": decode_us, "query_heads_per_s": qheads / (decode_us * 1e-6),
+        "decode": {"us": decode_us, "us_p10_p50_p90": [float(x) for x in decode_p],
+                   "query_heads_per_s": qheads / (decode_us * 1e-6),
                    "algorithmic_bytes": int(dec_bytes), "GBps": achieved},
+        "eager_ms_per_step": eager_wall / K * 1e3,
         "append_us": append_us,
         "flush_us": flush_us,
         "graph_replay_matches_eager": replay_ok,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(cfg.name)},
     }
+    if args.copy_mb:
+        # an elementwise kernel (not a DMA-engine memcpy, which no counter sees)
+        src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        result["copy_reference_bytes"] = int(src.numel() * 4)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -396,6 +396,14 @@ __device__ __forceinline__ uint32_t opaque(uint32_t m) {
   return m;
 }
 
+__device__ __forceinline__ void store_agent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_agent(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Power-of-two factor of channel d's code inside its byte: 2^(B * k).
 template <int BITS>
 __device__ __forceinline__ float inv_pos_scale(int d) {
@@ -765,24 +773,34 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
 
   // ---- publish the partial state and take a ticket
+  // The partial state is written with device-scope atomic stores, which the
+  // gfx950 caches keep coherent across XCDs by themselves (they write
+  // through to the device coherence point).  Waiting for their completion,
+  // then a barrier, then a device-scope ticket, orders them before the
+  // ticket without a device-wide release fence, whose L2 write-back and
+  // invalidate would otherwise run once per wave on a shared L2.
   float *P = a.part + (bh * S + split) * (size_t)a.part_stride;
-  if (L > 0.0f && tid < kD) P[kPartHead + tid] = acc_out;
+  if (L > 0.0f && tid < kD) store_agent(P + kPartHead + tid, acc_out);
   if (tid == 0) {
-    P[0] = M;
-    P[1] = L;
+    store_agent(P, M);
+    store_agent(P + 1, L);
   }
-  __threadfence();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
-  if (tid == 0) sm.ticket = (int)atomicAdd(a.tickets + bh, 1u);
+  if (tid == 0)
+    sm.ticket = (int)__hip_atomic_fetch_add(a.tickets + bh, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (sm.ticket != S - 1) return;
-  __threadfence();
 
-  // ---- last workgroup of this (sequence, head): merge all partials
+  // ---- last workgroup of this (sequence, head): merge all partials, read
+  // with device-scope atomic loads (coherent with the stores above)
   const float *P0 = a.part + bh * S * (size_t)a.part_stride;
   for (int s = tid; s < S; s += kThreads) {
-    sm.u.mg.m[s] = P0[(size_t)s * a.part_stride];
-    sm.u.mg.l[s] = P0[(size_t)s * a.part_stride + 1];
+    sm.u.mg.m[s] = load_agent(P0 + (size_t)s * a.part_stride);
+    sm.u.mg.l[s] = load_agent(P0 + (size_t)s * a.part_stride + 1);
   }
   __syncthreads();
   float mx = -INFINITY;
@@ -797,19 +815,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
   block_sum<1>(lsum, sm.red);
   const int cq = tid & 31, sl = tid >> 5;
-  float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+  float A[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int s = sl; s < S; s += 8) {
     const float e = sm.u.mg.e[s];
     if (e != 0.0f) {
-      const float4 v = *reinterpret_cast<const float4 *>(P0 + (size_t)s * a.part_stride + kPartHead + 4 * cq);
-      A.x = fmaf(e, v.x, A.x);
-      A.y = fmaf(e, v.y, A.y);
-      A.z = fmaf(e, v.z, A.z);
-      A.w = fmaf(e, v.w, A.w);
+      const float *src = P0 + (size_t)s * a.part_stride + kPartHead + 4 * cq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) A[i] = fmaf(e, load_agent(src + i), A[i]);
     }
   }
-  *reinterpret_cast<float4 *>(&sm.u.mg.acc[sl][4 * cq]) = A;
+  *reinterpret_cast<float4 *>(&sm.u.mg.acc[sl][4 * cq]) = make_float4(A[0], A[1], A[2], A[3]);
   __syncthreads();
   if (tid < kD) {
     float s = 0.0f;
@@ -817,7 +833,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     for (int i = 0; i < 8; ++i) s += sm.u.mg.acc[i][tid];
     a.out[bh * kD + tid] = lsum[0] > 0.0f ? s / lsum[0] : 0.0f;
   }
-  if (tid == 0) a.tickets[bh] = 0u;
+  if (tid == 0) __hip_atomic_store(a.tickets + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int BITS, int G>

@@ -87,7 +87,7 @@ class Workload:
 
     def dims(self):
         c = self.config
-        return dict(batch=c.batch, heads=c.heads, head_dim=c.head_dim, bits=self.bits,
+        return dict(batch=int(self.q_len.shape[0]), heads=c.heads, head_dim=c.head_dim, bits=self.bits,
                     group=c.group, residual=c.residual, capacity=c.capacity)
 
 

@@ -199,8 +199,8 @@ def test_decode_is_deterministic_and_leaves_workspace_clean():
 
 def test_status_bits_and_skipped_sequences():
     w = workload(1)
-    # append into a full window: dropped, flagged
-    c = gpu_cache(w, q_len=[224], r_len=[32])
+    # append into a full window: dropped, flagged (capacity 224: no room to flush)
+    c = gpu_cache(w, capacity=224, q_len=[224], r_len=[32])
     k1 = torch.from_numpy(w.k[:, :, 0]).cuda().contiguous()
     kivi.append_kv(c, k1, k1)
     torch.cuda.synchronize()
