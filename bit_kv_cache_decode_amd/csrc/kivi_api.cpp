@@ -11,9 +11,10 @@
 namespace kivi {
 namespace {
 
-constexpr int kTargetWorkgroups = 4096;  // about 16 per compute unit on 256 CUs
+constexpr long kTargetWaves = 5120;  // about 20 waves per compute unit on 256 CUs
+constexpr int kMaxWaveSubchunks = 16;
 constexpr int kMaxQuantSplits = 64;
-constexpr int kWindowChunk = 64;
+constexpr int kWindowSplitTokens = 128;
 constexpr int kMaxResidual = 4096;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -41,19 +42,23 @@ int hip_rc(int rc) { return rc == 0 ? KIVI_OK : KIVI_EHIP; }
 
 DecodePlan decode_plan(const kivi_dims &d) {
   DecodePlan p{};
-  p.chunk = d.bits == 2 ? 512 : 256;
+  const int words = d.head_dim * d.bits / 32;
+  p.sub = 1024 / words;
   const long bh = (long)d.batch * d.heads;
-  const int nchunks = (d.capacity + p.chunk - 1) / p.chunk;
-  p.kper = 1;
+  const long nsub = (d.capacity + p.sub - 1) / p.sub;
+  p.kw = 1;
   p.sq = 0;
-  if (nchunks > 0) {
-    const long want = std::max<long>(1, (kTargetWorkgroups + bh - 1) / bh);
-    const int sq = (int)std::min<long>(std::min<long>(nchunks, want), kMaxQuantSplits);
-    p.kper = (nchunks + sq - 1) / sq;
-    p.sq = (nchunks + p.kper - 1) / p.kper;
+  if (nsub > 0) {
+    const long total = bh * nsub;
+    p.kw = (int)std::min<long>(std::max<long>(1, (total + kTargetWaves - 1) / kTargetWaves),
+                               kMaxWaveSubchunks);
+    p.sq = (int)((nsub + 4L * p.kw - 1) / (4L * p.kw));
+    if (p.sq > kMaxQuantSplits) {
+      p.kw = (int)((nsub + 4L * kMaxQuantSplits - 1) / (4L * kMaxQuantSplits));
+      p.sq = (int)((nsub + 4L * p.kw - 1) / (4L * p.kw));
+    }
   }
-  p.win_chunk = kWindowChunk;
-  p.nr = (d.residual + kWindowChunk - 1) / kWindowChunk;
+  p.nr = (d.residual + kWindowSplitTokens - 1) / kWindowSplitTokens;
   p.splits = p.sq + p.nr;
   p.part_floats = 4 + (size_t)d.head_dim;
   const size_t parts = (size_t)bh * p.splits * p.part_floats * sizeof(float);

@@ -213,9 +213,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
   // ---- values: one group per (token, G consecutive channels)
   load_tile<G>(xs, a.src_v + src_off);
   __syncthreads();
-  const size_t vtok0 = bh * (size_t)a.cap + dst0 + (size_t)tile * G;
+  // value zero-points and steps are tiled like the codes: [tile][group][token]
   if (tid < kD) {
-    const int t = tid / NVG, j = tid % NVG;
+    const int j = tid / G, t = tid % G;
     float mn = INFINITY, mx = -INFINITY;
     for (int c = 0; c < G; ++c) {
       const float x = (float)xs[t][j * G + c];
@@ -223,15 +223,15 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
       mx = fmaxf(mx, x);
     }
     const GroupParams g = group_params(mn, mx, kTop);
-    a.v_zero[vtok0 * NVG + tid] = g.zero16;
-    a.v_scale[vtok0 * NVG + tid] = g.scale16;
+    a.v_zero[ktile * kD + tid] = g.zero16;
+    a.v_scale[ktile * kD + tid] = g.scale16;
     gmn[tid] = g.mn;
     gst[tid] = g.s;
   }
   __syncthreads();
   for (int wi = tid; wi < W * G; wi += kThreads) {
     const int w = wi / G, t = wi % G;
-    const int gi = t * NVG + (w * CPW) / G;
+    const int gi = ((w * CPW) / G) * G + t;
     const float mn = gmn[gi], s = gst[gi];
     uint32_t word = 0;
 #pragma unroll
@@ -316,13 +316,17 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const half_t *k_new, c
 
 // ----------------------------------------------------------------- decode
 //
-// Grid (splits, heads, batch), 256 threads.  Split s < sq covers quantized
-// tokens [s * kper * CH, (s + 1) * kper * CH) in chunks of CH tokens; split
-// s >= sq covers window tokens [(s - sq) * 64, ...).  Each split produces the
-// partial softmax state (max m, sum l, unnormalised weighted value sum) in
-// log2 units, writes it to the workspace and takes a ticket; the workgroup
-// that takes the last ticket of its (sequence, head) merges all partials by
-// log-sum-exp rescaling and writes the output, then resets the ticket.
+// Grid (splits, heads, batch), 256 threads = 4 waves.  Split s < sq is a
+// quantized split: its waves walk 128-token (B=2) or 64-token (B=4)
+// sub-chunks of the quantized tokens, sub-chunk i of the split going to wave
+// i % 4.  Split s >= sq is a window split over 128 fp16 window tokens, 32 per
+// wave.  Every wave works on its own (no block barrier until the end); every
+// lane keeps its own online-softmax state (running max, sum, value sums) for
+// the tokens it sees.  At the end the lanes and waves of the workgroup are
+// combined in LDS into one partial state (max m, sum l, unnormalised value
+// sums) in log2 units, published to the workspace; the workgroup that takes
+// the last ticket of its (sequence, head) merges all partials by log-sum-exp
+// rescaling and writes the output.
 //
 // Dequantization is folded into the dot products:
 //   score_t = sum_d q'_d * K_hat[t,d]
@@ -330,10 +334,14 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const half_t *k_new, c
 //   out_d   = sum_t p_t * (z_{t,j} + s_{t,j} * c_{t,d})
 //           = sum_t (p_t * s_{t,j}) * c_{t,d} + sum_t p_t * z_{t,j}
 // with q' = sm_scale * log2(e) * q, so that p_t = exp2(score_t - max).
-// Codes are converted with a byte mask and v_cvt_f32_ubyteN: the mask keeps
-// one code per byte, shifted left by B*k bits; the factor 2^(B*k) is folded
-// into the per-channel multipliers (keys) or removed from the accumulators
-// at the end (values).
+//
+// Code conversion: one AND of a packed word keeps, in each 16-bit half, the
+// code of one channel at its bit offset e (e < 10, inside the fp16 mantissa;
+// the upper channels of each half are first shifted down).  Each half is
+// then an fp16 subnormal equal to c * 2^(e - 24), exactly, and
+// v_fma_mix_f32 converts it inside the fused multiply-add.  The factor
+// 2^(24 - e) is folded into the key multipliers, and taken out of the value
+// sums at the end.
 
 struct DecodeArgs {
   const uint32_t *k_codes, *v_codes;
@@ -344,57 +352,54 @@ struct DecodeArgs {
   float *out, *part;
   uint32_t *tickets;
   float qscale;  // sm_scale * log2(e)
-  int heads, R, cap, kper, sq, nr, win_chunk, part_stride;
+  int heads, R, cap, kw, sq, nr, part_stride;
 };
 
 constexpr int kMaxSplits = 128;
-constexpr int kPartHead = 4;  // m, l, 2 pad floats before the 128 values
+constexpr int kPartHead = 4;   // m, l, 2 pad floats before the 128 values
+constexpr int kWinWave = 32;   // window tokens per wave
+constexpr int kWinRound = 16;  // window tokens per wave per round
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 template <int BITS, int G>
 struct DecCfg {
-  static constexpr int W = kD * BITS / 32;      // words per token
-  static constexpr int CPW = 32 / BITS;         // channels per word
-  static constexpr int CH = BITS == 2 ? 512 : 256;  // tokens per chunk
-  static constexpr int NT = CH / G;             // tiles per chunk
-  static constexpr int TQS = 64 / W;            // token quads per wave-load
-  static constexpr int LPT = G * W / 256;       // wave-loads per tile
-  static constexpr int NL = CH * W / 1024;      // wave-loads per wave per chunk
+  static constexpr int W = kD * BITS / 32;     // words per token
+  static constexpr int CPW = 32 / BITS;        // channels per word
+  static constexpr int HP = CPW / 2;           // code pairs per word
+  static constexpr int SUB = 1024 / W;         // tokens per sub-chunk
+  static constexpr int TQS = 64 / W;           // token quads per wave-load
+  static constexpr int TPL = 4 * TQS;          // tokens per wave-load
+  static constexpr int NL = SUB / TPL;         // wave-loads per sub-chunk and operand
   static constexpr int NVG = kD / G;            // value groups per token
-  static constexpr int TPT = CH / kThreads;     // chunk tokens per thread
-  static constexpr int KTW = (NT + 3) / 4;      // key tiles staged per wave
-  static_assert(NL == 4, "four 16-byte loads per lane per chunk");
-  static_assert(LPT >= 1 && TPT >= 1, "bad tiling");
+  static constexpr int NTS = SUB >= G ? SUB / G : 1;  // key tiles a sub-chunk touches
+  static_assert(NL == 4, "four 16-byte loads per lane per sub-chunk and operand");
+  static_assert(G % TPL == 0, "a wave-load stays inside one tile");
 };
 
 template <int BITS, int G>
 struct DecSmem {
   using C = DecCfg<BITS, G>;
-  float qs[kD];
-  float sc[C::CH];
-  float cz[C::NT][C::W];
-  float vbias[C::NVG];
-  float red[4 * 8];
-  int ticket;
+  float qs[kD];   // sm_scale * log2(e) * q
+  float qsf[kD];  // qs times the code-position factor 2^(24 - e) of each channel
+  struct {
+    float acc[4][4][kD];  // [wave][row][channel]
+    float bias[4][4][16]; // [wave][row][word]
+    float m[4], l[4];
+  } fin;
   union {
     struct {
-      float qp[C::NT][kD];
-      float pv[C::NVG][C::CH];
-    } s;
-    float accred[4][4][kD];
+      float qp[C::NTS][kD];
+      float cz[C::NTS][C::W];
+    } wave[4];
     struct {
       float m[kMaxSplits], l[kMaxSplits], e[kMaxSplits];
       float acc[8][kD];
     } mg;
   } u;
+  float red[32];
+  int ticket;
 };
-
-// Keeps the compiler from folding the byte mask into per-code bit-field
-// extracts: with the masked word opaque, each (m >> 8j) & 0xff conversion
-// becomes a single v_cvt_f32_ubyte{j} of the whole word.
-__device__ __forceinline__ uint32_t opaque(uint32_t m) {
-  __asm__("" : "+v"(m));
-  return m;
-}
 
 __device__ __forceinline__ void store_agent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -404,57 +409,78 @@ __device__ __forceinline__ float load_agent(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Power-of-two factor of channel d's code inside its byte: 2^(B * k).
+__device__ __forceinline__ float mix_lo(float a, uint32_t m, float c) {
+  return fmaf(a, (float)__builtin_bit_cast(half2_t, m).x, c);
+}
+
+__device__ __forceinline__ float mix_hi(float a, uint32_t m, float c) {
+  return fmaf(a, (float)__builtin_bit_cast(half2_t, m).y, c);
+}
+
+// Bit offset of channel i's code inside its 16-bit half after extraction.
 template <int BITS>
-__device__ __forceinline__ float inv_pos_scale(int d) {
+__device__ __forceinline__ int code_offset(int i) {
+  constexpr int HP = 16 / BITS;
+  const int p = i % HP;
+  if constexpr (BITS == 2) return p <= 4 ? 2 * p : 2 * (p - 5);
+  else return p <= 1 ? 4 * p : 4 * (p - 2);
+}
+
+// 2^(24 - e) for channel i of a word: the factor between an extracted code's
+// fp16 value and the code.
+template <int BITS>
+__device__ __forceinline__ float code_factor(int i) {
+  return __builtin_ldexpf(1.0f, 24 - code_offset<BITS>(i));
+}
+
+// Word u masked to code pair p (channels p and p + HP), each half holding its
+// code at bit offset code_offset(p).  uh is u shifted right by 10 (B = 2) or
+// 8 (B = 4), which brings the upper pairs of each half into the mantissa.
+template <int BITS, int P>
+__device__ __forceinline__ uint32_t pair_bits(uint32_t u, uint32_t uh) {
   if constexpr (BITS == 2) {
-    const int k = d & 3;
-    return k == 0 ? 1.0f : k == 1 ? 0.25f : k == 2 ? 0.0625f : 0.015625f;
+    if constexpr (P <= 4) return u & (0x00030003u << (2 * P));
+    else return uh & (0x00030003u << (2 * (P - 5)));
   } else {
-    return (d & 1) ? 0.0625f : 1.0f;
+    if constexpr (P <= 1) return u & (0x000F000Fu << (4 * P));
+    else return uh & (0x000F000Fu << (4 * (P - 2)));
   }
 }
 
-// acc + sum over the word's channels of q[i] * code_i * 2^(B * pos_i).
 template <int BITS>
-__device__ __forceinline__ float dot_word(uint32_t u, const float *q, float acc) {
-  if constexpr (BITS == 2) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t m = opaque(u & (0x03030303u << (2 * k)));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = fmaf(q[4 * j + k], (float)((m >> (8 * j)) & 0xFFu), acc);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint32_t m = opaque(u & (0x0F0F0F0Fu << (4 * k)));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = fmaf(q[2 * j + k], (float)((m >> (8 * j)) & 0xFFu), acc);
-    }
-  }
-  return acc;
+__device__ __forceinline__ uint32_t upper_pairs(uint32_t u) {
+  return u >> (BITS == 2 ? 10 : 8);
 }
 
-// acc[i] += p * code_i * 2^(B * pos_i) over the word's channels.
+// c0 + sum_i q[i] * code_i * 2^(e_i - 24) over the word's channels.
+template <int BITS, int P = 0>
+__device__ __forceinline__ void dot_pairs(uint32_t u, uint32_t uh, const float *q, float &a0,
+                                          float &a1) {
+  constexpr int HP = 16 / BITS;
+  if constexpr (P < HP) {
+    const uint32_t m = pair_bits<BITS, P>(u, uh);
+    a0 = mix_lo(q[P], m, a0);
+    a1 = mix_hi(q[P + HP], m, a1);
+    dot_pairs<BITS, P + 1>(u, uh, q, a0, a1);
+  }
+}
+
 template <int BITS>
-__device__ __forceinline__ void axpy_word(uint32_t u, float p, float *acc) {
-  if constexpr (BITS == 2) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t m = opaque(u & (0x03030303u << (2 * k)));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[4 * j + k] = fmaf(p, (float)((m >> (8 * j)) & 0xFFu), acc[4 * j + k]);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint32_t m = opaque(u & (0x0F0F0F0Fu << (4 * k)));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[2 * j + k] = fmaf(p, (float)((m >> (8 * j)) & 0xFFu), acc[2 * j + k]);
-    }
+__device__ __forceinline__ float dot_word(uint32_t u, const float *q, float c0) {
+  float a0 = c0, a1 = 0.0f;
+  dot_pairs<BITS>(u, upper_pairs<BITS>(u), q, a0, a1);
+  return a0 + a1;
+}
+
+// acc[i] += pp * code_i * 2^(e_i - 24) over the word's channels.
+template <int BITS, int P = 0>
+__device__ __forceinline__ void axpy_pairs(uint32_t u, uint32_t uh, float pp, float *acc) {
+  constexpr int HP = 16 / BITS;
+  if constexpr (P < HP) {
+    const uint32_t m = pair_bits<BITS, P>(u, uh);
+    acc[P] = mix_lo(pp, m, acc[P]);
+    acc[P + HP] = mix_hi(pp, m, acc[P + HP]);
+    axpy_pairs<BITS, P + 1>(u, uh, pp, acc);
   }
 }
 
@@ -462,287 +488,260 @@ __device__ __forceinline__ uint32_t u4_get(const uint4 &v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-template <int NVG>
-__device__ __forceinline__ void load_vmeta(const half_t *p, float (&out)[NVG]) {
-  if constexpr (NVG == 4) {
-    const uint2 r = *reinterpret_cast<const uint2 *>(p);
-    const half_t *h = reinterpret_cast<const half_t *>(&r);
+// Combine the per-lane states of one wave and publish them to sm.fin.
+// CPW: channels per lane; WPR: lanes per token slot; FOLD8: lanes l and l^8
+// hold the same channels (two slots per 16-lane row).
+template <int CPW, int WPR, bool FOLD8>
+__device__ __forceinline__ void wave_publish(float (&fin_acc)[4][kD], float (&fin_bias)[4][16],
+                                             float &fin_m, float &fin_l, float m, float l,
+                                             float *acc, float bias) {
+  const int lane = threadIdx.x & 63;
+  const int w = lane % WPR, row = lane >> 4;
+  const float M = wave_max(m);
+  const float e = (m == -INFINITY) ? 0.0f : exp2f(m - M);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = (float)h[i];
-  } else if constexpr (NVG == 2) {
-    const uint32_t r = *reinterpret_cast<const uint32_t *>(p);
-    const half_t *h = reinterpret_cast<const half_t *>(&r);
-    out[0] = (float)h[0];
-    out[1] = (float)h[1];
-  } else {
-    out[0] = (float)p[0];
+  for (int i = 0; i < CPW; ++i) acc[i] *= e;
+  bias *= e;
+  const float lw = wave_sum(w == 0 ? l * e : 0.0f);
+  if constexpr (FOLD8) {
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) acc[i] += dpp<0x128>(acc[i]);  // row_ror:8
+    bias += dpp<0x128>(bias);
+  }
+  if (!FOLD8 || (lane & 8) == 0) {
+#pragma unroll
+    for (int i = 0; i < CPW; i += 4)
+      *reinterpret_cast<float4 *>(&fin_acc[row][w * CPW + i]) =
+          make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+    fin_bias[row][w] = bias;
+  }
+  if (lane == 0) {
+    fin_m = M;
+    fin_l = lw;
   }
 }
 
-// Quantized split: chunks of CH tokens with an online softmax across chunks.
-// Leaves M, L (log2-domain running max and sum) and, for threads < 128, the
-// unnormalised output of channel tid in *acc_out.
 template <int BITS, int G>
 __device__ __forceinline__ void quantized_split(const DecodeArgs &a, DecSmem<BITS, G> &sm, size_t bh,
-                                                int split, int ql, float &M, float &L,
-                                                float &acc_out) {
+                                                int split, int ql) {
   using C = DecCfg<BITS, G>;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int w = lane % C::W, slot = lane / C::W;
+  const int jg = (w * C::CPW) / G;  // value group of this lane's channels
+  const size_t tps = (size_t)(a.cap / G);
+  const uint32_t *kcb = a.k_codes + bh * tps * (C::W * G);
+  const uint32_t *vcb = a.v_codes + bh * tps * (C::W * G);
+  const half_t *ksb = a.k_scale + bh * tps * kD;
+  const half_t *kzb = a.k_zero + bh * tps * kD;
+  const half_t *vsb = a.v_scale + bh * tps * kD;
+  const half_t *vzb = a.v_zero + bh * tps * kD;
+  auto &st = sm.u.wave[wv];
+  const float qs0 = sm.qs[2 * lane], qs1 = sm.qs[2 * lane + 1];
+  const float qf0 = sm.qsf[2 * lane], qf1 = sm.qsf[2 * lane + 1];
+
+  float m = -INFINITY, l = 0.0f, bias = 0.0f;
   float acc[C::CPW];
 #pragma unroll
   for (int i = 0; i < C::CPW; ++i) acc[i] = 0.0f;
-  if (tid < C::NVG) sm.vbias[tid] = 0.0f;
 
-  const int tok_begin = split * a.kper * C::CH;
-  const size_t tiles_per_seq = (size_t)(a.cap / G);
-  bool any = false;
-  for (int c = 0; c < a.kper; ++c) {
-    const int t0 = tok_begin + c * C::CH;
-    const int ntok = min(C::CH, ql - t0);
-    if (ntok <= 0) break;
-    any = true;
-    const int ntv = ntok / G;
-    const size_t tile0 = bh * tiles_per_seq + t0 / G;
+  const int sub0 = split * 4 * a.kw;
+  for (int c = 0; c < a.kw; ++c) {
+    const int T0 = (sub0 + wv + 4 * c) * C::SUB;
+    if (T0 >= ql) break;
+    const int nvl = min(C::NL, (ql - T0) / C::TPL);
+    const int tile0 = T0 / G;
 
-    // ---- issue every load of the chunk: key meta, value meta, codes
-    uint32_t ksr[C::KTW], kzr[C::KTW];
+    // ---- key metadata (2 channels per lane per touched tile) and key codes
+    uint32_t ksr[C::NTS], kzr[C::NTS];
 #pragma unroll
-    for (int i = 0; i < C::KTW; ++i) {
-      const int g = wv + 4 * i;
-      if (g < ntv) {
-        const size_t off = (tile0 + g) * kD + 2 * lane;
-        ksr[i] = *reinterpret_cast<const uint32_t *>(a.k_scale + off);
-        kzr[i] = *reinterpret_cast<const uint32_t *>(a.k_zero + off);
+    for (int k = 0; k < C::NTS; ++k) {
+      if ((tile0 + k) * G < ql) {
+        ksr[k] = *reinterpret_cast<const uint32_t *>(ksb + (size_t)(tile0 + k) * kD + 2 * lane);
+        kzr[k] = *reinterpret_cast<const uint32_t *>(kzb + (size_t)(tile0 + k) * kD + 2 * lane);
       } else {
-        ksr[i] = kzr[i] = 0u;
+        ksr[k] = kzr[k] = 0u;
       }
     }
-    float vsr[C::TPT][C::NVG], vzr[C::TPT][C::NVG];
-#pragma unroll
-    for (int i = 0; i < C::TPT; ++i) {
-      const int t = tid + kThreads * i;
-      if (t < ntok) {
-        const size_t off = (bh * a.cap + t0 + t) * C::NVG;
-        load_vmeta<C::NVG>(a.v_scale + off, vsr[i]);
-        load_vmeta<C::NVG>(a.v_zero + off, vzr[i]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < C::NVG; ++j) vsr[i][j] = vzr[i][j] = 0.0f;
-      }
-    }
-    uint4 kc[C::NL], vc[C::NL];
+    uint4 kc[C::NL];
 #pragma unroll
     for (int j = 0; j < C::NL; ++j) {
-      const int n = wv * C::NL + j, tile = n / C::LPT;
-      const int tq = (n % C::LPT) * C::TQS + slot;
-      if (tile < ntv) {
-        const size_t off = (tile0 + tile) * (C::W * G) + w * G + 4 * tq;
-        kc[j] = *reinterpret_cast<const uint4 *>(a.k_codes + off);
-        vc[j] = *reinterpret_cast<const uint4 *>(a.v_codes + off);
+      if (j < nvl) {
+        const int t = T0 + j * C::TPL;
+        const int tile = t / G, pos = t % G + 4 * slot;
+        kc[j] = *reinterpret_cast<const uint4 *>(kcb + ((size_t)tile * C::W + w) * G + pos);
       } else {
-        kc[j] = vc[j] = make_uint4(0u, 0u, 0u, 0u);
+        kc[j] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
 
-    // ---- key staging: q'_{g,d} = qs_d * s_{g,d} / 2^(B*pos), zero term per word
+    // ---- stage q'' = qsf * s and the zero terms of the touched tiles
 #pragma unroll
-    for (int i = 0; i < C::KTW; ++i) {
-      const int g = wv + 4 * i;
-      if (g < ntv) {
-        const half_t *hs = reinterpret_cast<const half_t *>(&ksr[i]);
-        const half_t *hz = reinterpret_cast<const half_t *>(&kzr[i]);
-        const int d0 = 2 * lane;
-        const float q0 = sm.qs[d0], q1 = sm.qs[d0 + 1];
-        sm.u.s.qp[g][d0] = q0 * (float)hs[0] * inv_pos_scale<BITS>(d0);
-        sm.u.s.qp[g][d0 + 1] = q1 * (float)hs[1] * inv_pos_scale<BITS>(d0 + 1);
-        float zc = q0 * (float)hz[0] + q1 * (float)hz[1];
+    for (int k = 0; k < C::NTS; ++k) {
+      if ((tile0 + k) * G < ql) {
+        st.qp[k][2 * lane] = mix_lo(qf0, ksr[k], 0.0f);
+        st.qp[k][2 * lane + 1] = mix_hi(qf1, ksr[k], 0.0f);
+        float zc = mix_lo(qs0, kzr[k], mix_hi(qs1, kzr[k], 0.0f));
         zc = lane_group_sum<C::CPW / 2>(zc);
-        if ((lane % (C::CPW / 2)) == 0) sm.cz[g][lane / (C::CPW / 2)] = zc;
+        if ((lane % (C::CPW / 2)) == 0) st.cz[k][lane / (C::CPW / 2)] = zc;
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
 
-    // ---- scores of the chunk
+    // ---- scores (every lane of a token slot ends with the full sums)
+    float s[C::NL][4];
 #pragma unroll
     for (int j = 0; j < C::NL; ++j) {
-      const int n = wv * C::NL + j, tile = n / C::LPT;
-      if (tile < ntv) {
-        const int tq = (n % C::LPT) * C::TQS + slot;
+      if (j < nvl) {
+        const int k = ((T0 % G) + j * C::TPL) / G;
         float qv[C::CPW];
 #pragma unroll
         for (int i = 0; i < C::CPW; i += 4) {
-          const float4 t4 = *reinterpret_cast<const float4 *>(&sm.u.s.qp[tile][w * C::CPW + i]);
+          const float4 t4 = *reinterpret_cast<const float4 *>(&st.qp[k][w * C::CPW + i]);
           qv[i] = t4.x;
           qv[i + 1] = t4.y;
           qv[i + 2] = t4.z;
           qv[i + 3] = t4.w;
         }
-        const float c0 = sm.cz[tile][w];
-        float s4[4];
+        const float c0 = st.cz[k][w];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s4[i] = lane_group_sum<C::W>(dot_word<BITS>(u4_get(kc[j], i), qv, c0));
-        if (w == 0)
-          *reinterpret_cast<float4 *>(&sm.sc[tile * G + 4 * tq]) = make_float4(s4[0], s4[1], s4[2], s4[3]);
+        for (int i = 0; i < 4; ++i)
+          s[j][i] = lane_group_sum<C::W>(dot_word<BITS>(u4_get(kc[j], i), qv, c0));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[j][i] = -INFINITY;
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
 
-    // ---- chunk softmax (online across chunks), value staging
-    float mloc = -INFINITY;
+    // ---- value codes and this lane's value-group metadata
+    uint4 vc[C::NL];
+    uint2 vsr[C::NL], vzr[C::NL];
 #pragma unroll
-    for (int i = 0; i < C::TPT; ++i) {
-      const int t = tid + kThreads * i;
-      if (t < ntok) mloc = fmaxf(mloc, sm.sc[t]);
-    }
-    mloc = block_max(mloc, sm.red);
-    const float Mn = fmaxf(M, mloc);
-    const float corr = exp2f(M - Mn);  // 0 on the first chunk (M = -inf)
-    float sums[1 + C::NVG];
-#pragma unroll
-    for (int j = 0; j <= C::NVG; ++j) sums[j] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < C::TPT; ++i) {
-      const int t = tid + kThreads * i;
-      if (t < ntok) {
-        const float p = exp2f(sm.sc[t] - Mn);
-        sums[0] += p;
-#pragma unroll
-        for (int j = 0; j < C::NVG; ++j) {
-          sm.u.s.pv[j][t] = p * vsr[i][j];
-          sums[1 + j] += p * vzr[i][j];
-        }
+    for (int j = 0; j < C::NL; ++j) {
+      if (j < nvl) {
+        const int t = T0 + j * C::TPL;
+        const int tile = t / G, pos = t % G + 4 * slot;
+        vc[j] = *reinterpret_cast<const uint4 *>(vcb + ((size_t)tile * C::W + w) * G + pos);
+        const size_t mo = ((size_t)tile * C::NVG + jg) * G + pos;
+        vsr[j] = *reinterpret_cast<const uint2 *>(vsb + mo);
+        vzr[j] = *reinterpret_cast<const uint2 *>(vzb + mo);
+      } else {
+        vc[j] = make_uint4(0u, 0u, 0u, 0u);
+        vsr[j] = vzr[j] = make_uint2(0u, 0u);
       }
     }
-    block_sum<1 + C::NVG>(sums, sm.red);  // also orders the pv writes before the reads below
-    L = L * corr + sums[0];
-    M = Mn;
-    if (tid < C::NVG) sm.vbias[tid] = sm.vbias[tid] * corr + sums[1 + tid];
+
+    // ---- per-lane online softmax over this lane's tokens
+    float mc = m;
+#pragma unroll
+    for (int j = 0; j < C::NL; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mc = fmaxf(mc, s[j][i]);
+    const float corr = exp2f(m - mc);  // 0 on the first sub-chunk (m = -inf)
+    m = mc;
+    l *= corr;
+    bias *= corr;
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) acc[i] *= corr;
 
     // ---- weighted value sum
 #pragma unroll
     for (int j = 0; j < C::NL; ++j) {
-      const int n = wv * C::NL + j, tile = n / C::LPT;
-      if (tile < ntv) {
-        const int tq = (n % C::LPT) * C::TQS + slot;
-        const int jg = (w * C::CPW) / G;
-        const float4 pp = *reinterpret_cast<const float4 *>(&sm.u.s.pv[jg][tile * G + 4 * tq]);
-        axpy_word<BITS>(vc[j].x, pp.x, acc);
-        axpy_word<BITS>(vc[j].y, pp.y, acc);
-        axpy_word<BITS>(vc[j].z, pp.z, acc);
-        axpy_word<BITS>(vc[j].w, pp.w, acc);
+      if (j < nvl) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2f(s[j][i] - m);
+          l += p;
+          const uint32_t sw = i < 2 ? vsr[j].x : vsr[j].y;
+          const uint32_t zw = i < 2 ? vzr[j].x : vzr[j].y;
+          const float pp = (i & 1) ? mix_hi(p, sw, 0.0f) : mix_lo(p, sw, 0.0f);
+          bias = (i & 1) ? mix_hi(p, zw, bias) : mix_lo(p, zw, bias);
+          const uint32_t u = u4_get(vc[j], i);
+          axpy_pairs<BITS>(u, upper_pairs<BITS>(u), pp, acc);
+        }
       }
     }
-    __syncthreads();  // qp / pv / sc are rewritten by the next chunk
   }
-  if (!any) return;
-
-  // ---- reduce the per-lane channel sums over lanes and waves
-  const int row = lane >> 4;
-  if constexpr (C::W == 8) {
-#pragma unroll
-    for (int i = 0; i < C::CPW; ++i) acc[i] += dpp<0x128>(acc[i]);  // row_ror:8 pairs lanes l, l^8
-    if ((lane & 8) == 0) {
-#pragma unroll
-      for (int i = 0; i < C::CPW; i += 4)
-        *reinterpret_cast<float4 *>(&sm.u.accred[wv][row][w * C::CPW + i]) =
-            make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < C::CPW; i += 4)
-      *reinterpret_cast<float4 *>(&sm.u.accred[wv][row][w * C::CPW + i]) =
-          make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
-  }
-  __syncthreads();
-  if (tid < kD) {
-    float s = 0.0f;
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) s += sm.u.accred[x][y][tid];
-    acc_out = s * inv_pos_scale<BITS>(tid) + sm.vbias[tid / G];
-  }
+  wave_publish<C::CPW, C::W, C::W == 8>(sm.fin.acc[wv], sm.fin.bias[wv], sm.fin.m[wv],
+                                         sm.fin.l[wv], m, l, acc, bias);
 }
 
-// Window split: up to 64 fp16 tokens, 16 lanes per token (8 channels each).
+// Window split: up to 128 fp16 window tokens, 32 per wave in two rounds of
+// 16; 16 lanes per token, 8 channels per lane.
 template <int BITS, int G>
 __device__ __forceinline__ void window_split(const DecodeArgs &a, DecSmem<BITS, G> &sm, size_t bh,
-                                             int rs, int n, float &M, float &L, float &acc_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+                                             int rs, int rl) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane >> 4, part = lane & 15;
-  const half_t *kr = a.k_res + (bh * a.R + rs) * kD;
-  const half_t *vr = a.v_res + (bh * a.R + rs) * kD;
-  uint4 kx[4], vx[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tok = (wv * 4 + j) * 4 + slot;
-    if (tok < n) {
-      kx[j] = *reinterpret_cast<const uint4 *>(kr + (size_t)tok * kD + part * 8);
-      vx[j] = *reinterpret_cast<const uint4 *>(vr + (size_t)tok * kD + part * 8);
-    } else {
-      kx[j] = vx[j] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
   float qv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) qv[i] = sm.qs[part * 8 + i];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if ((wv * 4 + j) * 4 < n) {
-      const int tok = (wv * 4 + j) * 4 + slot;
-      const half_t *hk = reinterpret_cast<const half_t *>(&kx[j]);
-      float s = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s = fmaf(qv[i], (float)hk[i], s);
-      s = lane_group_sum<16>(s);
-      if (part == 0 && tok < n) sm.sc[tok] = s;
-    }
-  }
-  __syncthreads();
-  float m = tid < n ? sm.sc[tid] : -INFINITY;
-  m = block_max(m, sm.red);
-  float sums[1] = {0.0f};
-  if (tid < n) {
-    const float p = exp2f(sm.sc[tid] - m);
-    sm.sc[tid] = p;
-    sums[0] = p;
-  }
-  block_sum<1>(sums, sm.red);
-  M = m;
-  L = sums[0];
+  float m = -INFINITY, l = 0.0f;
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int r = 0; r < kWinWave / kWinRound; ++r) {
+    const int t0 = rs + wv * kWinWave + r * kWinRound;
+    const int n = min(kWinRound, rl - t0);
+    if (n <= 0) break;
+    uint4 kx[4], vx[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tok = (wv * 4 + j) * 4 + slot;
-    if (tok < n) {
-      const float p = sm.sc[tok];
-      const half_t *hv = reinterpret_cast<const half_t *>(&vx[j]);
+    for (int j = 0; j < 4; ++j) {
+      const int tok = j * 4 + slot;
+      if (tok < n) {
+        const size_t off = (bh * a.R + t0 + tok) * kD + part * 8;
+        kx[j] = *reinterpret_cast<const uint4 *>(a.k_res + off);
+        vx[j] = *reinterpret_cast<const uint4 *>(a.v_res + off);
+      } else {
+        kx[j] = vx[j] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    float s[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(p, (float)hv[i], acc[i]);
+    for (int j = 0; j < 4; ++j) {
+      if (j * 4 < n) {
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t u = u4_get(kx[j], i);
+          a0 = mix_lo(qv[2 * i], u, a0);
+          a1 = mix_hi(qv[2 * i + 1], u, a1);
+        }
+        const float t = lane_group_sum<16>(a0 + a1);
+        s[j] = (j * 4 + slot < n) ? t : -INFINITY;
+      } else {
+        s[j] = -INFINITY;
+      }
+    }
+    float mc = m;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mc = fmaxf(mc, s[j]);
+    if (mc != -INFINITY) {
+      const float corr = exp2f(m - mc);
+      m = mc;
+      l *= corr;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= corr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = exp2f(s[j] - m);  // 0 for absent tokens
+        l += p;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t u = u4_get(vx[j], i);
+          acc[2 * i] = mix_lo(p, u, acc[2 * i]);
+          acc[2 * i + 1] = mix_hi(p, u, acc[2 * i + 1]);
+        }
+      }
     }
   }
-#pragma unroll
-  for (int i = 0; i < 8; i += 4)
-    *reinterpret_cast<float4 *>(&sm.u.accred[wv][slot][part * 8 + i]) =
-        make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
-  __syncthreads();
-  if (tid < kD) {
-    float s = 0.0f;
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) s += sm.u.accred[x][y][tid];
-    acc_out = s;
-  }
+  wave_publish<8, 16, false>(sm.fin.acc[wv], sm.fin.bias[wv], sm.fin.m[wv], sm.fin.l[wv], m, l,
+                             acc, 0.0f);
 }
 
 template <int BITS, int G>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+  using C = DecCfg<BITS, G>;
   __shared__ DecSmem<BITS, G> sm;
   const int tid = threadIdx.x;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -755,21 +754,44 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     ql = 0;
     rl = 0;
   }
+  const bool quant = split < a.sq;
   if (tid < kD / 2) {
     const uint32_t r = reinterpret_cast<const uint32_t *>(a.q + bh * kD)[tid];
-    const half_t *hq = reinterpret_cast<const half_t *>(&r);
-    sm.qs[2 * tid] = (float)hq[0] * a.qscale;
-    sm.qs[2 * tid + 1] = (float)hq[1] * a.qscale;
+    const half2_t hq = __builtin_bit_cast(half2_t, r);
+    const float q0 = (float)hq.x * a.qscale, q1 = (float)hq.y * a.qscale;
+    sm.qs[2 * tid] = q0;
+    sm.qs[2 * tid + 1] = q1;
+    sm.qsf[2 * tid] = q0 * code_factor<BITS>((2 * tid) % C::CPW);
+    sm.qsf[2 * tid + 1] = q1 * code_factor<BITS>((2 * tid + 1) % C::CPW);
   }
   __syncthreads();
 
-  float M = -INFINITY, L = 0.0f, acc_out = 0.0f;
-  if (split < a.sq) {
-    quantized_split<BITS, G>(a, sm, bh, split, ql, M, L, acc_out);
-  } else {
-    const int rs = (split - a.sq) * a.win_chunk;
-    const int n = min(a.win_chunk, rl - rs);
-    if (n > 0) window_split<BITS, G>(a, sm, bh, rs, n, M, L, acc_out);
+  if (quant) quantized_split<BITS, G>(a, sm, bh, split, ql);
+  else window_split<BITS, G>(a, sm, bh, (split - a.sq) * 4 * kWinWave, rl);
+  __syncthreads();
+
+  // ---- combine the four waves into the workgroup's partial state
+  float M = -INFINITY;
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    if (sm.fin.l[x] > 0.0f) M = fmaxf(M, sm.fin.m[x]);
+  float L = 0.0f, acc_out = 0.0f;
+  if (M != -INFINITY) {
+    const int cpw = quant ? C::CPW : 8;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float e = sm.fin.l[x] > 0.0f ? exp2f(sm.fin.m[x] - M) : 0.0f;
+      L += e * sm.fin.l[x];
+      if (tid < kD && e != 0.0f) {
+        float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          sa += sm.fin.acc[x][y][tid];
+          sb += sm.fin.bias[x][y][tid / cpw];
+        }
+        acc_out += e * (quant ? fmaf(sa, code_factor<BITS>(tid % C::CPW), sb) : sa);
+      }
+    }
   }
 
   // ---- publish the partial state and take a ticket
@@ -948,10 +970,9 @@ int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, 
   da.heads = d.heads;
   da.R = d.residual;
   da.cap = d.capacity;
-  da.kper = p.kper;
+  da.kw = p.kw;
   da.sq = p.sq;
   da.nr = p.nr;
-  da.win_chunk = p.win_chunk;
   da.part_stride = (int)p.part_floats;
   const dim3 grid(p.splits, d.heads, d.batch);
   const int G = d.group;

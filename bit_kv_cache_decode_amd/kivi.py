@@ -129,8 +129,8 @@ class KiviCache:
         self.v_codes = torch.zeros((batch, heads, cap // G, W, G), dtype=i32, device=dev)
         self.k_scale = torch.zeros((batch, heads, cap // G, D), dtype=f16, device=dev)
         self.k_zero = torch.zeros((batch, heads, cap // G, D), dtype=f16, device=dev)
-        self.v_scale = torch.zeros((batch, heads, cap, D // G), dtype=f16, device=dev)
-        self.v_zero = torch.zeros((batch, heads, cap, D // G), dtype=f16, device=dev)
+        self.v_scale = torch.zeros((batch, heads, cap // G, D // G, G), dtype=f16, device=dev)
+        self.v_zero = torch.zeros((batch, heads, cap // G, D // G, G), dtype=f16, device=dev)
         self.k_res = torch.zeros((batch, heads, R, D), dtype=f16, device=dev)
         self.v_res = torch.zeros((batch, heads, R, D), dtype=f16, device=dev)
         self.q_len = torch.zeros((batch,), dtype=i32, device=dev)

@@ -77,9 +77,11 @@ typedef struct {
  *   k_scale, k_zero  fp16 [batch][heads][capacity/G][D]
  *       Per key group (G consecutive tokens x 1 channel): the step and the
  *       group minimum ([P2] keys section; [P1] section 3.1).
- *   v_scale, v_zero  fp16 [batch][heads][capacity][D/G]
+ *   v_scale, v_zero  fp16 [batch][heads][capacity/G][D/G][G]
  *       Per value group (1 token x G consecutive channels): step and minimum
- *       ([P2] values section; [P1] section 2.1).
+ *       ([P2] values section; [P1] section 2.1).  Stored in the same tiles
+ *       of G tokens as the codes, group-major inside a tile: the value of
+ *       token n, channel group j is at [n / G][j][n % G].
  *   k_res, v_res     fp16 [batch][heads][R][D]   the fp16 window.
  *   q_len  int32 [batch]  quantized tokens held (multiple of G, <= capacity)
  *   r_len  int32 [batch]  window tokens held, 0 <= r_len <= R

@@ -33,12 +33,26 @@ def encode_tokens(k, v, group, bits):
     """Quantize n fp16 tokens (n a multiple of G) of one (sequence, head).
 
     k, v: fp16 [n, D].  Returns a dict with k_codes/v_codes uint32
-    [n/G, W, G], k_zero/k_scale fp16 [n/G, D], v_zero/v_scale fp16 [n, D/G].
+    [n/G, W, G], k_zero/k_scale fp16 [n/G, D] and v_zero/v_scale fp16
+    [n/G, D/G, G] (value groups stored per tile of G tokens, group-major).
     """
     ck, zk, sk = quantize_keys(k, group, bits)
     cv, zv, sv = quantize_values(v, group, bits)
     return dict(k_codes=pack_tiles(ck, group, bits), k_zero=zk, k_scale=sk,
-                v_codes=pack_tiles(cv, group, bits), v_zero=zv, v_scale=sv)
+                v_codes=pack_tiles(cv, group, bits), v_zero=tile_value_groups(zv, group),
+                v_scale=tile_value_groups(sv, group))
+
+
+def tile_value_groups(a, group):
+    """Per-token value-group array [n, D/G] -> tiles [n/G, D/G, G]."""
+    n, ng = a.shape
+    return np.ascontiguousarray(a.reshape(n // group, group, ng).transpose(0, 2, 1))
+
+
+def untile_value_groups(a):
+    """Tiles [T, D/G, G] -> per-token value-group array [T*G, D/G]."""
+    t, ng, group = a.shape
+    return a.transpose(0, 2, 1).reshape(t * group, ng)
 
 
 def context(state, group, bits):
@@ -49,7 +63,8 @@ def context(state, group, bits):
     ck = unpack_tiles(state["k_codes"][:nt], bits)
     cv = unpack_tiles(state["v_codes"][:nt], bits)
     kq = dequantize_keys(ck, state["k_zero"][:nt], state["k_scale"][:nt], group)
-    vq = dequantize_values(cv, state["v_zero"][:ql], state["v_scale"][:ql], group)
+    vq = dequantize_values(cv, untile_value_groups(state["v_zero"][:nt]),
+                           untile_value_groups(state["v_scale"][:nt]), group)
     kr = state["k_res"][:rl].astype(np.float64)
     vr = state["v_res"][:rl].astype(np.float64)
     return np.concatenate([kq, kr], axis=0), np.concatenate([vq, vr], axis=0)
@@ -65,18 +80,16 @@ def head_state(k, v, q_len, r_len, group, bits, capacity, residual):
         v_codes=np.zeros((capacity // group, W, group), np.uint32),
         k_zero=np.zeros((capacity // group, D), np.float16),
         k_scale=np.zeros((capacity // group, D), np.float16),
-        v_zero=np.zeros((capacity, D // group), np.float16),
-        v_scale=np.zeros((capacity, D // group), np.float16),
+        v_zero=np.zeros((capacity // group, D // group, group), np.float16),
+        v_scale=np.zeros((capacity // group, D // group, group), np.float16),
         k_res=np.zeros((residual, D), np.float16),
         v_res=np.zeros((residual, D), np.float16),
         q_len=q_len, r_len=r_len)
     if q_len:
         enc = encode_tokens(k[:q_len], v[:q_len], group, bits)
         nt = q_len // group
-        for name in ("k_codes", "v_codes", "k_zero", "k_scale"):
+        for name in ("k_codes", "v_codes", "k_zero", "k_scale", "v_zero", "v_scale"):
             st[name][:nt] = enc[name]
-        st["v_zero"][:q_len] = enc["v_zero"]
-        st["v_scale"][:q_len] = enc["v_scale"]
     st["k_res"][:r_len] = k[q_len:q_len + r_len]
     st["v_res"][:r_len] = v[q_len:q_len + r_len]
     return st
@@ -94,8 +107,8 @@ class Cache:
         self.v_codes = np.zeros((batch, heads, nt, W, group), np.uint32)
         self.k_zero = np.zeros((batch, heads, nt, head_dim), np.float16)
         self.k_scale = np.zeros((batch, heads, nt, head_dim), np.float16)
-        self.v_zero = np.zeros((batch, heads, capacity, head_dim // group), np.float16)
-        self.v_scale = np.zeros((batch, heads, capacity, head_dim // group), np.float16)
+        self.v_zero = np.zeros((batch, heads, nt, head_dim // group, group), np.float16)
+        self.v_scale = np.zeros((batch, heads, nt, head_dim // group, group), np.float16)
         self.k_res = np.zeros((batch, heads, residual, head_dim), np.float16)
         self.v_res = np.zeros((batch, heads, residual, head_dim), np.float16)
         self.q_len = np.zeros(batch, np.int32)
@@ -104,13 +117,9 @@ class Cache:
 
     def _store(self, b, h, pos, k, v):
         enc = encode_tokens(k, v, self.G, self.bits)
-        t0, nt, n = pos // self.G, k.shape[0] // self.G, k.shape[0]
-        self.k_codes[b, h, t0:t0 + nt] = enc["k_codes"]
-        self.k_zero[b, h, t0:t0 + nt] = enc["k_zero"]
-        self.k_scale[b, h, t0:t0 + nt] = enc["k_scale"]
-        self.v_codes[b, h, t0:t0 + nt] = enc["v_codes"]
-        self.v_zero[b, h, pos:pos + n] = enc["v_zero"]
-        self.v_scale[b, h, pos:pos + n] = enc["v_scale"]
+        t0, nt = pos // self.G, k.shape[0] // self.G
+        for name in ("k_codes", "k_zero", "k_scale", "v_codes", "v_zero", "v_scale"):
+            getattr(self, name)[b, h, t0:t0 + nt] = enc[name]
 
     def prefill(self, k, v, lens, res=None):
         """k, v: fp16 [batch, heads, src_len, D]; lens/res: int [batch]."""

@@ -51,12 +51,13 @@ def test_validate_dims_codes():
 
 @pytest.mark.parametrize("dims,splits", [
     ((1, 1, 128, 2, 32, 32, 256), 2),         # 1 quantized split + 1 window split
-    ((8, 32, 128, 2, 32, 128, 4096), 10),     # 8 chunks of 512 + 2 window splits
-    ((16, 40, 128, 2, 32, 128, 2048), 6),
-    ((64, 32, 128, 2, 32, 128, 8320), 4),     # many sequences: few, long splits
-    ((1, 32, 128, 2, 128, 128, 131072), 66),  # long context: 64 quantized splits
-    ((1, 32, 128, 4, 128, 128, 131072), 66),
+    ((8, 32, 128, 2, 32, 128, 4096), 5),      # 4 splits of 1024 tokens + 1 window split
+    ((16, 40, 128, 2, 32, 128, 2048), 3),
+    ((64, 32, 128, 2, 32, 128, 8320), 3),     # many sequences: few, long splits
+    ((1, 32, 128, 2, 128, 128, 131072), 38),  # long context: 37 quantized splits
+    ((1, 32, 128, 4, 128, 128, 131072), 41),
     ((1, 1, 128, 2, 32, 32, 0), 1),           # window only
+    ((1, 1, 128, 2, 32, 4096, 1 << 24), 96),  # capped at 64 quantized splits + 32 window
 ])
 def test_decode_plan(dims, splits):
     d = kivi.make_dims(*dims)
