@@ -11,10 +11,10 @@
 namespace kivi {
 namespace {
 
-constexpr long kTargetWaves = 5120;  // about 20 waves per compute unit on 256 CUs
-constexpr int kMaxWaveSubchunks = 16;
-constexpr int kMaxQuantSplits = 64;
-constexpr int kWindowSplitTokens = 128;
+// Resident decode workgroups on the device: 256 compute units x 4 (the
+// decode kernel is compiled for at least 4 waves per SIMD).
+constexpr long kWorkgroupSlots = 256 * 4;
+constexpr int kMaxSplits = 64;
 constexpr int kMaxResidual = 4096;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -43,23 +43,18 @@ int hip_rc(int rc) { return rc == 0 ? KIVI_OK : KIVI_EHIP; }
 DecodePlan decode_plan(const kivi_dims &d) {
   DecodePlan p{};
   const int words = d.head_dim * d.bits / 32;
-  p.sub = 1024 / words;
+  p.sub = 512 / words;
   const long bh = (long)d.batch * d.heads;
   const long nsub = (d.capacity + p.sub - 1) / p.sub;
-  p.kw = 1;
-  p.sq = 0;
-  if (nsub > 0) {
-    const long total = bh * nsub;
-    p.kw = (int)std::min<long>(std::max<long>(1, (total + kTargetWaves - 1) / kTargetWaves),
-                               kMaxWaveSubchunks);
-    p.sq = (int)((nsub + 4L * p.kw - 1) / (4L * p.kw));
-    if (p.sq > kMaxQuantSplits) {
-      p.kw = (int)((nsub + 4L * kMaxQuantSplits - 1) / (4L * kMaxQuantSplits));
-      p.sq = (int)((nsub + 4L * p.kw - 1) / (4L * p.kw));
-    }
-  }
-  p.nr = (d.residual + kWindowSplitTokens - 1) / kWindowSplitTokens;
-  p.splits = p.sq + p.nr;
+  // Enough workgroups to fill every resident slot once (no second round, no
+  // tail), but no more than the work supports (about 2 sub-chunks per wave)
+  // and at most kMaxSplits.
+  long splits = (kWorkgroupSlots + bh - 1) / bh;
+  splits = std::min<long>(splits, std::max<long>(1, (nsub + 7) / 8));
+  splits = std::max<long>(1, std::min<long>(splits, kMaxSplits));
+  p.splits = (int)splits;
+  const long waves = 4 * splits;
+  p.win_per_wave = (int)(((d.residual + waves - 1) / waves + 3) / 4 * 4);
   p.part_floats = 4 + (size_t)d.head_dim;
   const size_t parts = (size_t)bh * p.splits * p.part_floats * sizeof(float);
   p.counters_off = round_up(parts, 256);

@@ -9,19 +9,16 @@
 
 namespace kivi {
 
-// Decode work split.  Quantized tokens are walked in sub-chunks of `sub`
-// tokens (1024 / words-per-token: four 16-byte loads per lane per operand).
-// A quantized split is one workgroup of 4 waves covering 4 * kw consecutive
-// sub-chunks (sub-chunk i of the split goes to wave i % 4); a window split
-// covers 128 window tokens (32 per wave).  Each (sequence, head) gets `sq`
-// quantized splits followed by `nr` window splits; their partial softmax
-// states are merged by the last workgroup of that (sequence, head) to finish.
+// Decode work split.  Each (sequence, head) gets `splits` workgroups of 4
+// waves.  Its quantized tokens are walked in sub-chunks of `sub` tokens
+// (512 / words-per-token: two 16-byte loads per lane per operand), dealt
+// round-robin to the 4 * splits waves; each wave also takes `win_per_wave`
+// consecutive fp16 window tokens.  The workgroups' partial softmax states are
+// merged by the last workgroup of that (sequence, head) to finish.
 struct DecodePlan {
-  int sub;         // quantized tokens per sub-chunk
-  int kw;          // sub-chunks per wave in a quantized split
-  int sq;          // quantized splits per (sequence, head)
-  int nr;          // window splits per (sequence, head)
-  int splits;      // sq + nr
+  int sub;           // quantized tokens per sub-chunk
+  int splits;        // workgroups per (sequence, head)
+  int win_per_wave;  // window tokens per wave (multiple of 4)
   size_t part_floats;     // floats of partial state per split (4 + D)
   size_t counters_off;    // byte offset of the per-(sequence, head) tickets
   size_t bytes;           // total workspace bytes

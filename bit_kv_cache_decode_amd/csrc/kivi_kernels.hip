@@ -47,6 +47,11 @@ __device__ __forceinline__ float lane_group_sum(float v) {
   return v;
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -316,17 +321,18 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const half_t *k_new, c
 
 // ----------------------------------------------------------------- decode
 //
-// Grid (splits, heads, batch), 256 threads = 4 waves.  Split s < sq is a
-// quantized split: its waves walk 128-token (B=2) or 64-token (B=4)
-// sub-chunks of the quantized tokens, sub-chunk i of the split going to wave
-// i % 4.  Split s >= sq is a window split over 128 fp16 window tokens, 32 per
-// wave.  Every wave works on its own (no block barrier until the end); every
-// lane keeps its own online-softmax state (running max, sum, value sums) for
-// the tokens it sees.  At the end the lanes and waves of the workgroup are
-// combined in LDS into one partial state (max m, sum l, unnormalised value
-// sums) in log2 units, published to the workspace; the workgroup that takes
-// the last ticket of its (sequence, head) merges all partials by log-sum-exp
-// rescaling and writes the output.
+// Grid (splits, heads, batch), 256 threads = 4 waves.  The 4 * splits waves
+// of one (sequence, head) share its work evenly: quantized sub-chunks of 64
+// (B=2) or 32 (B=4) tokens are dealt round-robin to the waves, and each wave
+// also takes an equal slice of the fp16 window tokens.  Every wave works on
+// its own (no block barrier until the end), and every lane keeps its own
+// online-softmax state (running max, sum, value sums) for the tokens it
+// sees; window tokens use the same lane layout and state as codes.  At the
+// end the lanes and waves of the workgroup are combined in LDS into one
+// partial state (max m, sum l, unnormalised value sums) in log2 units,
+// published to the workspace; the workgroup that takes the last ticket of
+// its (sequence, head) merges all partials by log-sum-exp rescaling and
+// writes the output.
 //
 // Dequantization is folded into the dot products:
 //   score_t = sum_d q'_d * K_hat[t,d]
@@ -341,7 +347,8 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const half_t *k_new, c
 // then an fp16 subnormal equal to c * 2^(e - 24), exactly, and
 // v_fma_mix_f32 converts it inside the fused multiply-add.  The factor
 // 2^(24 - e) is folded into the key multipliers, and taken out of the value
-// sums at the end.
+// sums at the end (window values enter the sums pre-multiplied by
+// 2^(e - 24)).
 
 struct DecodeArgs {
   const uint32_t *k_codes, *v_codes;
@@ -352,13 +359,11 @@ struct DecodeArgs {
   float *out, *part;
   uint32_t *tickets;
   float qscale;  // sm_scale * log2(e)
-  int heads, R, cap, kw, sq, nr, part_stride;
+  int heads, R, cap, splits, win_per_wave, part_stride;
 };
 
 constexpr int kMaxSplits = 128;
 constexpr int kPartHead = 4;   // m, l, 2 pad floats before the 128 values
-constexpr int kWinWave = 32;   // window tokens per wave
-constexpr int kWinRound = 16;  // window tokens per wave per round
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -367,13 +372,14 @@ struct DecCfg {
   static constexpr int W = kD * BITS / 32;     // words per token
   static constexpr int CPW = 32 / BITS;        // channels per word
   static constexpr int HP = CPW / 2;           // code pairs per word
-  static constexpr int SUB = 1024 / W;         // tokens per sub-chunk
+  static constexpr int SUB = 512 / W;          // tokens per sub-chunk
   static constexpr int TQS = 64 / W;           // token quads per wave-load
   static constexpr int TPL = 4 * TQS;          // tokens per wave-load
   static constexpr int NL = SUB / TPL;         // wave-loads per sub-chunk and operand
   static constexpr int NVG = kD / G;            // value groups per token
   static constexpr int NTS = SUB >= G ? SUB / G : 1;  // key tiles a sub-chunk touches
-  static_assert(NL == 4, "four 16-byte loads per lane per sub-chunk and operand");
+  static constexpr int QPW = CPW + 4;          // padded LDS stride of one word's multipliers
+  static_assert(NL == 2, "two 16-byte loads per lane per sub-chunk and operand");
   static_assert(G % TPL == 0, "a wave-load stays inside one tile");
 };
 
@@ -389,7 +395,7 @@ struct DecSmem {
   } fin;
   union {
     struct {
-      float qp[C::NTS][kD];
+      float qp[C::NTS][C::W * C::QPW];  // key multipliers, word-padded
       float cz[C::NTS][C::W];
     } wave[4];
     struct {
@@ -498,7 +504,7 @@ __device__ __forceinline__ void wave_publish(float (&fin_acc)[4][kD], float (&fi
   const int lane = threadIdx.x & 63;
   const int w = lane % WPR, row = lane >> 4;
   const float M = wave_max(m);
-  const float e = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+  const float e = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
 #pragma unroll
   for (int i = 0; i < CPW; ++i) acc[i] *= e;
   bias *= e;
@@ -521,232 +527,234 @@ __device__ __forceinline__ void wave_publish(float (&fin_acc)[4][kD], float (&fi
   }
 }
 
+// Registers holding every load of one sub-chunk of one wave.
 template <int BITS, int G>
-__device__ __forceinline__ void quantized_split(const DecodeArgs &a, DecSmem<BITS, G> &sm, size_t bh,
-                                                int split, int ql) {
+struct SubLoads {
   using C = DecCfg<BITS, G>;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int w = lane % C::W, slot = lane / C::W;
-  const int jg = (w * C::CPW) / G;  // value group of this lane's channels
-  const size_t tps = (size_t)(a.cap / G);
-  const uint32_t *kcb = a.k_codes + bh * tps * (C::W * G);
-  const uint32_t *vcb = a.v_codes + bh * tps * (C::W * G);
-  const half_t *ksb = a.k_scale + bh * tps * kD;
-  const half_t *kzb = a.k_zero + bh * tps * kD;
-  const half_t *vsb = a.v_scale + bh * tps * kD;
-  const half_t *vzb = a.v_zero + bh * tps * kD;
-  auto &st = sm.u.wave[wv];
-  const float qs0 = sm.qs[2 * lane], qs1 = sm.qs[2 * lane + 1];
-  const float qf0 = sm.qsf[2 * lane], qf1 = sm.qsf[2 * lane + 1];
+  uint4 kc[C::NL], vc[C::NL];      // key and value codes
+  uint32_t ks[C::NTS], kz[C::NTS]; // key steps / zero-points of 2 channels per touched tile
+  uint2 vs[C::NL], vz[C::NL];      // value steps / zero-points of this lane's 4 tokens
+};
 
-  float m = -INFINITY, l = 0.0f, bias = 0.0f;
-  float acc[C::CPW];
+// Wave-uniform v_exp_f32: 2^x (0 for x = -inf).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Per-lane online-softmax state of one wave.
+template <int CPW>
+struct LaneState {
+  float m, l, bias;
+  float acc[CPW];
+};
+
+// Fold new scores s[0..N) (already in the lane's max bookkeeping) into the
+// state: if any lane's running max grows, every lane rescales (by 1 where its
+// own max did not move).
+template <int CPW, int N>
+__device__ __forceinline__ void update_max(LaneState<CPW> &st, const float *s) {
+  float mc = st.m;
 #pragma unroll
-  for (int i = 0; i < C::CPW; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < N; ++i) mc = fmaxf(mc, s[i]);
+  if (__ballot(mc > st.m) != 0) {
+    // 1 where this lane's max did not move (also when it is still -inf),
+    // 0 on a lane's first tokens (m = -inf)
+    const float corr = mc > st.m ? exp2_fast(st.m - mc) : 1.0f;
+    st.m = mc;
+    st.l *= corr;
+    st.bias *= corr;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) st.acc[i] *= corr;
+  }
+}
 
-  const int sub0 = split * 4 * a.kw;
-  for (int c = 0; c < a.kw; ++c) {
-    const int T0 = (sub0 + wv + 4 * c) * C::SUB;
-    if (T0 >= ql) break;
-    const int nvl = min(C::NL, (ql - T0) / C::TPL);
+// Per-wave streaming over the quantized tokens of one (sequence, head).
+template <int BITS, int G>
+struct QuantStream {
+  using C = DecCfg<BITS, G>;
+  const uint32_t *kcb, *vcb;
+  const half_t *ksb, *kzb, *vsb, *vzb;
+  uint32_t code_off, vmeta_off, kmeta_off;
+  int ql, last_tile, gw, nw;
+
+  // first token of this wave's c-th sub-chunk (sub-chunks dealt round-robin)
+  __device__ __forceinline__ int t0(int c) const { return (gw + c * nw) * C::SUB; }
+
+  // Issue every load of sub-chunk c, back to back.  Indices past the last
+  // valid token are clamped to valid ones; their data is never used.
+  __device__ __forceinline__ void issue(SubLoads<BITS, G> &b, int c) const {
+    const int T0 = t0(c);
+    const int nvl = max(1, min(C::NL, (ql - T0) / C::TPL));
     const int tile0 = T0 / G;
-
-    // ---- key metadata (2 channels per lane per touched tile) and key codes
-    uint32_t ksr[C::NTS], kzr[C::NTS];
 #pragma unroll
     for (int k = 0; k < C::NTS; ++k) {
-      if ((tile0 + k) * G < ql) {
-        ksr[k] = *reinterpret_cast<const uint32_t *>(ksb + (size_t)(tile0 + k) * kD + 2 * lane);
-        kzr[k] = *reinterpret_cast<const uint32_t *>(kzb + (size_t)(tile0 + k) * kD + 2 * lane);
-      } else {
-        ksr[k] = kzr[k] = 0u;
-      }
+      const size_t tk = (size_t)min(tile0 + k, last_tile) * kD;
+      b.ks[k] = *reinterpret_cast<const uint32_t *>(ksb + tk + kmeta_off);
+      b.kz[k] = *reinterpret_cast<const uint32_t *>(kzb + tk + kmeta_off);
     }
-    uint4 kc[C::NL];
 #pragma unroll
     for (int j = 0; j < C::NL; ++j) {
-      if (j < nvl) {
-        const int t = T0 + j * C::TPL;
-        const int tile = t / G, pos = t % G + 4 * slot;
-        kc[j] = *reinterpret_cast<const uint4 *>(kcb + ((size_t)tile * C::W + w) * G + pos);
-      } else {
-        kc[j] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      const int t = T0 + min(j, nvl - 1) * C::TPL;
+      const size_t tile = (size_t)(t / G);
+      b.kc[j] = *reinterpret_cast<const uint4 *>(kcb + tile * (C::W * G) + t % G + code_off);
     }
-
-    // ---- stage q'' = qsf * s and the zero terms of the touched tiles
-#pragma unroll
-    for (int k = 0; k < C::NTS; ++k) {
-      if ((tile0 + k) * G < ql) {
-        st.qp[k][2 * lane] = mix_lo(qf0, ksr[k], 0.0f);
-        st.qp[k][2 * lane + 1] = mix_hi(qf1, ksr[k], 0.0f);
-        float zc = mix_lo(qs0, kzr[k], mix_hi(qs1, kzr[k], 0.0f));
-        zc = lane_group_sum<C::CPW / 2>(zc);
-        if ((lane % (C::CPW / 2)) == 0) st.cz[k][lane / (C::CPW / 2)] = zc;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // ---- scores (every lane of a token slot ends with the full sums)
-    float s[C::NL][4];
 #pragma unroll
     for (int j = 0; j < C::NL; ++j) {
-      if (j < nvl) {
-        const int k = ((T0 % G) + j * C::TPL) / G;
-        float qv[C::CPW];
-#pragma unroll
-        for (int i = 0; i < C::CPW; i += 4) {
-          const float4 t4 = *reinterpret_cast<const float4 *>(&st.qp[k][w * C::CPW + i]);
-          qv[i] = t4.x;
-          qv[i + 1] = t4.y;
-          qv[i + 2] = t4.z;
-          qv[i + 3] = t4.w;
-        }
-        const float c0 = st.cz[k][w];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s[j][i] = lane_group_sum<C::W>(dot_word<BITS>(u4_get(kc[j], i), qv, c0));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[j][i] = -INFINITY;
-      }
+      const int t = T0 + min(j, nvl - 1) * C::TPL;
+      const size_t tile = (size_t)(t / G);
+      b.vc[j] = *reinterpret_cast<const uint4 *>(vcb + tile * (C::W * G) + t % G + code_off);
+      const size_t mo = tile * kD + t % G + vmeta_off;
+      b.vs[j] = *reinterpret_cast<const uint2 *>(vsb + mo);
+      b.vz[j] = *reinterpret_cast<const uint2 *>(vzb + mo);
     }
-    __builtin_amdgcn_wave_barrier();
+  }
+};
 
-    // ---- value codes and this lane's value-group metadata
-    uint4 vc[C::NL];
-    uint2 vsr[C::NL], vzr[C::NL];
+template <int BITS, int G>
+__device__ __forceinline__ void process_sub(const SubLoads<BITS, G> &b, int T0, int ql, int lane,
+                                            float qs0, float qs1, float qf0, float qf1,
+                                            float (&qp)[DecCfg<BITS, G>::NTS][DecCfg<BITS, G>::W *
+                                                                             DecCfg<BITS, G>::QPW],
+                                            float (&cz)[DecCfg<BITS, G>::NTS][DecCfg<BITS, G>::W],
+                                            LaneState<DecCfg<BITS, G>::CPW> &st) {
+  using C = DecCfg<BITS, G>;
+  const int w = lane % C::W;
+  const int nvl = min(C::NL, (ql - T0) / C::TPL);
+
+  // ---- stage q'' = qsf * s and the zero terms of the touched tiles
+  const int d0 = 2 * lane;
+  const int qpo = (d0 / C::CPW) * C::QPW + d0 % C::CPW;
 #pragma unroll
-    for (int j = 0; j < C::NL; ++j) {
-      if (j < nvl) {
-        const int t = T0 + j * C::TPL;
-        const int tile = t / G, pos = t % G + 4 * slot;
-        vc[j] = *reinterpret_cast<const uint4 *>(vcb + ((size_t)tile * C::W + w) * G + pos);
-        const size_t mo = ((size_t)tile * C::NVG + jg) * G + pos;
-        vsr[j] = *reinterpret_cast<const uint2 *>(vsb + mo);
-        vzr[j] = *reinterpret_cast<const uint2 *>(vzb + mo);
-      } else {
-        vc[j] = make_uint4(0u, 0u, 0u, 0u);
-        vsr[j] = vzr[j] = make_uint2(0u, 0u);
+  for (int k = 0; k < C::NTS; ++k) {
+    qp[k][qpo] = mix_lo(qf0, b.ks[k], 0.0f);
+    qp[k][qpo + 1] = mix_hi(qf1, b.ks[k], 0.0f);
+    float zc = mix_lo(qs0, b.kz[k], mix_hi(qs1, b.kz[k], 0.0f));
+    zc = lane_group_sum<C::CPW / 2>(zc);
+    if ((lane % (C::CPW / 2)) == 0) cz[k][lane / (C::CPW / 2)] = zc;
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- scores (every lane of a token slot ends with the full sums)
+  float s[C::NL * 4];
+#pragma unroll
+  for (int j = 0; j < C::NL; ++j) {
+    if (j < nvl) {
+      const int k = ((T0 % G) + j * C::TPL) / G;
+      float qv[C::CPW];
+#pragma unroll
+      for (int i = 0; i < C::CPW; i += 4) {
+        const float4 t4 = *reinterpret_cast<const float4 *>(&qp[k][w * C::QPW + i]);
+        qv[i] = t4.x;
+        qv[i + 1] = t4.y;
+        qv[i + 2] = t4.z;
+        qv[i + 3] = t4.w;
       }
+      const float c0 = cz[k][w];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s[4 * j + i] = lane_group_sum<C::W>(dot_word<BITS>(u4_get(b.kc[j], i), qv, c0));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[4 * j + i] = -INFINITY;
     }
+  }
+  __builtin_amdgcn_wave_barrier();
 
-    // ---- per-lane online softmax over this lane's tokens
-    float mc = m;
-#pragma unroll
-    for (int j = 0; j < C::NL; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mc = fmaxf(mc, s[j][i]);
-    const float corr = exp2f(m - mc);  // 0 on the first sub-chunk (m = -inf)
-    m = mc;
-    l *= corr;
-    bias *= corr;
-#pragma unroll
-    for (int i = 0; i < C::CPW; ++i) acc[i] *= corr;
+  update_max<C::CPW, C::NL * 4>(st, s);
 
-    // ---- weighted value sum
+  // ---- weighted value sum
 #pragma unroll
-    for (int j = 0; j < C::NL; ++j) {
-      if (j < nvl) {
+  for (int j = 0; j < C::NL; ++j) {
+    if (j < nvl) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(s[j][i] - m);
-          l += p;
-          const uint32_t sw = i < 2 ? vsr[j].x : vsr[j].y;
-          const uint32_t zw = i < 2 ? vzr[j].x : vzr[j].y;
-          const float pp = (i & 1) ? mix_hi(p, sw, 0.0f) : mix_lo(p, sw, 0.0f);
-          bias = (i & 1) ? mix_hi(p, zw, bias) : mix_lo(p, zw, bias);
-          const uint32_t u = u4_get(vc[j], i);
-          axpy_pairs<BITS>(u, upper_pairs<BITS>(u), pp, acc);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2_fast(s[4 * j + i] - st.m);
+        st.l += p;
+        const uint32_t sw = i < 2 ? b.vs[j].x : b.vs[j].y;
+        const uint32_t zw = i < 2 ? b.vz[j].x : b.vz[j].y;
+        const float pp = (i & 1) ? mix_hi(p, sw, 0.0f) : mix_lo(p, sw, 0.0f);
+        st.bias = (i & 1) ? mix_hi(p, zw, st.bias) : mix_lo(p, zw, st.bias);
+        const uint32_t u = u4_get(b.vc[j], i);
+        axpy_pairs<BITS>(u, upper_pairs<BITS>(u), pp, st.acc);
       }
     }
   }
-  wave_publish<C::CPW, C::W, C::W == 8>(sm.fin.acc[wv], sm.fin.bias[wv], sm.fin.m[wv],
-                                         sm.fin.l[wv], m, l, acc, bias);
 }
 
-// Window split: up to 128 fp16 window tokens, 32 per wave in two rounds of
-// 16; 16 lanes per token, 8 channels per lane.
+// Window tokens [t_begin, t_end) of this wave, in the codes' lane layout:
+// lane (slot, w) takes tokens t_begin + 4 * slot + i (i < 4) and channels
+// w * CPW .. w * CPW + CPW - 1 of each.
 template <int BITS, int G>
-__device__ __forceinline__ void window_split(const DecodeArgs &a, DecSmem<BITS, G> &sm, size_t bh,
-                                             int rs, int rl) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int slot = lane >> 4, part = lane & 15;
-  float qv[8];
+__device__ __forceinline__ void window_tokens(const DecodeArgs &a, const DecSmem<BITS, G> &sm,
+                                              size_t bh, int t_begin, int t_end, int lane,
+                                              LaneState<DecCfg<BITS, G>::CPW> &st) {
+  using C = DecCfg<BITS, G>;
+  constexpr int CPW = C::CPW, NV = CPW / 8;  // 16-byte vectors per token and lane
+  const int w = lane % C::W, slot = lane / C::W;
+  float qv[CPW];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) qv[i] = sm.qs[part * 8 + i];
-  float m = -INFINITY, l = 0.0f;
-  float acc[8];
+  for (int i = 0; i < CPW; ++i) qv[i] = sm.qs[w * CPW + i];
+  for (int t0 = t_begin; t0 < t_end; t0 += C::TPL) {
+    // keys first (scores), then values: keeps the live registers small
+    uint4 x[4][NV];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  for (int r = 0; r < kWinWave / kWinRound; ++r) {
-    const int t0 = rs + wv * kWinWave + r * kWinRound;
-    const int n = min(kWinRound, rl - t0);
-    if (n <= 0) break;
-    uint4 kx[4], vx[4];
+    for (int i = 0; i < 4; ++i) {
+      const int t = min(t0 + 4 * slot + i, t_end - 1);  // clamped: data of absent tokens unused
+      const half_t *kr = a.k_res + (bh * a.R + t) * kD + w * CPW;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tok = j * 4 + slot;
-      if (tok < n) {
-        const size_t off = (bh * a.R + t0 + tok) * kD + part * 8;
-        kx[j] = *reinterpret_cast<const uint4 *>(a.k_res + off);
-        vx[j] = *reinterpret_cast<const uint4 *>(a.v_res + off);
-      } else {
-        kx[j] = vx[j] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int v = 0; v < NV; ++v) x[i][v] = reinterpret_cast<const uint4 *>(kr)[v];
     }
     float s[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j * 4 < n) {
-        float a0 = 0.0f, a1 = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t u = u4_get(kx[j], i);
-          a0 = mix_lo(qv[2 * i], u, a0);
-          a1 = mix_hi(qv[2 * i + 1], u, a1);
+      for (int v = 0; v < NV; ++v) {
+        const uint32_t *u = reinterpret_cast<const uint32_t *>(&x[i][v]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a0 = mix_lo(qv[8 * v + 2 * e], u[e], a0);
+          a1 = mix_hi(qv[8 * v + 2 * e + 1], u[e], a1);
         }
-        const float t = lane_group_sum<16>(a0 + a1);
-        s[j] = (j * 4 + slot < n) ? t : -INFINITY;
-      } else {
-        s[j] = -INFINITY;
       }
+      const float tot = lane_group_sum<C::W>(a0 + a1);
+      s[i] = (t0 + 4 * slot + i < t_end) ? tot : -INFINITY;
     }
-    float mc = m;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mc = fmaxf(mc, s[j]);
-    if (mc != -INFINITY) {
-      const float corr = exp2f(m - mc);
-      m = mc;
-      l *= corr;
+    for (int i = 0; i < 4; ++i) {
+      const int t = min(t0 + 4 * slot + i, t_end - 1);
+      const half_t *vr = a.v_res + (bh * a.R + t) * kD + w * CPW;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] *= corr;
+      for (int v = 0; v < NV; ++v) x[i][v] = reinterpret_cast<const uint4 *>(vr)[v];
+    }
+    update_max<CPW, 4>(st, s);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = exp2f(s[j] - m);  // 0 for absent tokens
-        l += p;
+    for (int i = 0; i < 4; ++i) {
+      // absent tokens contribute 0 (and the lane's max may still be -inf)
+      const float p = s[i] > -INFINITY ? exp2_fast(s[i] - st.m) : 0.0f;
+      st.l += p;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t u = u4_get(vx[j], i);
-          acc[2 * i] = mix_lo(p, u, acc[2 * i]);
-          acc[2 * i + 1] = mix_hi(p, u, acc[2 * i + 1]);
+      for (int v = 0; v < NV; ++v) {
+        const uint32_t *u = reinterpret_cast<const uint32_t *>(&x[i][v]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // value sums hold channel values times 2^(e - 24) (see above)
+          const int c0 = 8 * v + 2 * e;
+          st.acc[c0] = mix_lo(p * __builtin_ldexpf(1.0f, code_offset<BITS>(c0) - 24), u[e], st.acc[c0]);
+          st.acc[c0 + 1] =
+              mix_hi(p * __builtin_ldexpf(1.0f, code_offset<BITS>(c0 + 1) - 24), u[e], st.acc[c0 + 1]);
         }
       }
     }
   }
-  wave_publish<8, 16, false>(sm.fin.acc[wv], sm.fin.bias[wv], sm.fin.m[wv], sm.fin.l[wv], m, l,
-                             acc, 0.0f);
 }
 
 template <int BITS, int G>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeArgs a) {
   using C = DecCfg<BITS, G>;
   __shared__ DecSmem<BITS, G> sm;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * a.heads + h;
-  const int S = a.sq + a.nr;
+  const int S = a.splits;
 
   int ql = a.q_len[b], rl = a.r_len[b];
   if (!(ql >= 0 && ql <= a.cap && (ql % G) == 0 && rl >= 0 && rl <= a.R)) {
@@ -754,7 +762,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     ql = 0;
     rl = 0;
   }
-  const bool quant = split < a.sq;
   if (tid < kD / 2) {
     const uint32_t r = reinterpret_cast<const uint32_t *>(a.q + bh * kD)[tid];
     const half2_t hq = __builtin_bit_cast(half2_t, r);
@@ -766,8 +773,55 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  if (quant) quantized_split<BITS, G>(a, sm, bh, split, ql);
-  else window_split<BITS, G>(a, sm, bh, (split - a.sq) * 4 * kWinWave, rl);
+  // ---- this wave's share: quantized sub-chunks gw, gw + nw, ... and
+  // window tokens [gw * win_per_wave, (gw + 1) * win_per_wave)
+  const int w = lane % C::W, slot = lane / C::W;
+  const int jg = (w * C::CPW) / G;
+  const size_t tps = (size_t)(a.cap / G);
+  QuantStream<BITS, G> qs;
+  qs.kcb = a.k_codes + bh * tps * (C::W * G);
+  qs.vcb = a.v_codes + bh * tps * (C::W * G);
+  qs.ksb = a.k_scale + bh * tps * kD;
+  qs.kzb = a.k_zero + bh * tps * kD;
+  qs.vsb = a.v_scale + bh * tps * kD;
+  qs.vzb = a.v_zero + bh * tps * kD;
+  qs.code_off = (uint32_t)(w * G + 4 * slot);     // words, within a tile
+  qs.vmeta_off = (uint32_t)(jg * G + 4 * slot);   // halfs, within a tile
+  qs.kmeta_off = (uint32_t)(2 * lane);            // halfs, within a tile
+  qs.ql = ql;
+  qs.last_tile = ql / G - 1;
+  qs.gw = split * 4 + wv;
+  qs.nw = 4 * S;
+  auto &stg = sm.u.wave[wv];
+  const float qs0 = sm.qs[2 * lane], qs1 = sm.qs[2 * lane + 1];
+  const float qf0 = sm.qsf[2 * lane], qf1 = sm.qsf[2 * lane + 1];
+
+  LaneState<C::CPW> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+  st.bias = 0.0f;
+#pragma unroll
+  for (int i = 0; i < C::CPW; ++i) st.acc[i] = 0.0f;
+
+  int n = 0;  // quantized sub-chunks of this wave
+  if (qs.gw * C::SUB < ql) n = (ql - qs.gw * C::SUB + qs.nw * C::SUB - 1) / (qs.nw * C::SUB);
+  const int w_begin = qs.gw * a.win_per_wave;
+  const int w_end = min(rl, w_begin + a.win_per_wave);
+
+  // The first quantized loads go out before the window tokens are read, and
+  // the loads of sub-chunk c + 1 are in flight while sub-chunk c is computed.
+  SubLoads<BITS, G> A, B;
+  if (n > 0) qs.issue(A, 0);
+  if (w_begin < w_end) window_tokens<BITS, G>(a, sm, bh, w_begin, w_end, lane, st);
+  for (int c = 0; c < n; c += 2) {
+    qs.issue(B, min(c + 1, n - 1));
+    process_sub<BITS, G>(A, qs.t0(c), ql, lane, qs0, qs1, qf0, qf1, stg.qp, stg.cz, st);
+    if (c + 1 >= n) break;
+    qs.issue(A, min(c + 2, n - 1));
+    process_sub<BITS, G>(B, qs.t0(c + 1), ql, lane, qs0, qs1, qf0, qf1, stg.qp, stg.cz, st);
+  }
+  wave_publish<C::CPW, C::W, C::W == 8>(sm.fin.acc[wv], sm.fin.bias[wv], sm.fin.m[wv],
+                                         sm.fin.l[wv], st.m, st.l, st.acc, st.bias);
   __syncthreads();
 
   // ---- combine the four waves into the workgroup's partial state
@@ -777,19 +831,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     if (sm.fin.l[x] > 0.0f) M = fmaxf(M, sm.fin.m[x]);
   float L = 0.0f, acc_out = 0.0f;
   if (M != -INFINITY) {
-    const int cpw = quant ? C::CPW : 8;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const float e = sm.fin.l[x] > 0.0f ? exp2f(sm.fin.m[x] - M) : 0.0f;
+      const float e = sm.fin.l[x] > 0.0f ? exp2_fast(sm.fin.m[x] - M) : 0.0f;
       L += e * sm.fin.l[x];
       if (tid < kD && e != 0.0f) {
         float sa = 0.0f, sb = 0.0f;
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
           sa += sm.fin.acc[x][y][tid];
-          sb += sm.fin.bias[x][y][tid / cpw];
+          sb += sm.fin.bias[x][y][tid / C::CPW];
         }
-        acc_out += e * (quant ? fmaf(sa, code_factor<BITS>(tid % C::CPW), sb) : sa);
+        acc_out += e * fmaf(sa, code_factor<BITS>(tid % C::CPW), sb);
       }
     }
   }
@@ -831,23 +884,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   mx = block_max(mx, sm.red);
   float lsum[1] = {0.0f};
   for (int s = tid; s < S; s += kThreads) {
-    const float e = sm.u.mg.l[s] > 0.0f ? exp2f(sm.u.mg.m[s] - mx) : 0.0f;
+    const float e = sm.u.mg.l[s] > 0.0f ? exp2_fast(sm.u.mg.m[s] - mx) : 0.0f;
     sm.u.mg.e[s] = e;
     lsum[0] += e * sm.u.mg.l[s];
   }
   block_sum<1>(lsum, sm.red);
   const int cq = tid & 31, sl = tid >> 5;
-  float A[4] = {0.f, 0.f, 0.f, 0.f};
+  float macc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int s = sl; s < S; s += 8) {
     const float e = sm.u.mg.e[s];
     if (e != 0.0f) {
       const float *src = P0 + (size_t)s * a.part_stride + kPartHead + 4 * cq;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) A[i] = fmaf(e, load_agent(src + i), A[i]);
+      for (int i = 0; i < 4; ++i) macc[i] = fmaf(e, load_agent(src + i), macc[i]);
     }
   }
-  *reinterpret_cast<float4 *>(&sm.u.mg.acc[sl][4 * cq]) = make_float4(A[0], A[1], A[2], A[3]);
+  *reinterpret_cast<float4 *>(&sm.u.mg.acc[sl][4 * cq]) =
+      make_float4(macc[0], macc[1], macc[2], macc[3]);
   __syncthreads();
   if (tid < kD) {
     float s = 0.0f;
@@ -970,9 +1024,8 @@ int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, 
   da.heads = d.heads;
   da.R = d.residual;
   da.cap = d.capacity;
-  da.kw = p.kw;
-  da.sq = p.sq;
-  da.nr = p.nr;
+  da.splits = p.splits;
+  da.win_per_wave = p.win_per_wave;
   da.part_stride = (int)p.part_floats;
   const dim3 grid(p.splits, d.heads, d.batch);
   const int G = d.group;

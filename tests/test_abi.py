@@ -50,14 +50,14 @@ def test_validate_dims_codes():
 
 
 @pytest.mark.parametrize("dims,splits", [
-    ((1, 1, 128, 2, 32, 32, 256), 2),         # 1 quantized split + 1 window split
-    ((8, 32, 128, 2, 32, 128, 4096), 5),      # 4 splits of 1024 tokens + 1 window split
-    ((16, 40, 128, 2, 32, 128, 2048), 3),
-    ((64, 32, 128, 2, 32, 128, 8320), 3),     # many sequences: few, long splits
-    ((1, 32, 128, 2, 128, 128, 131072), 38),  # long context: 37 quantized splits
-    ((1, 32, 128, 4, 128, 128, 131072), 41),
+    ((1, 1, 128, 2, 32, 32, 256), 1),         # one workgroup does it all
+    ((8, 32, 128, 2, 32, 128, 4096), 4),      # 4 per (sequence, head): 1024 resident workgroups
+    ((16, 40, 128, 2, 32, 128, 2048), 2),
+    ((64, 32, 128, 2, 32, 128, 8320), 1),     # many sequences: one workgroup each
+    ((1, 32, 128, 2, 128, 128, 131072), 32),  # long context: 32 workgroups per head
+    ((1, 32, 128, 4, 128, 128, 131072), 32),
     ((1, 1, 128, 2, 32, 32, 0), 1),           # window only
-    ((1, 1, 128, 2, 32, 4096, 1 << 24), 96),  # capped at 64 quantized splits + 32 window
+    ((1, 1, 128, 2, 32, 4096, 1 << 24), 64),  # capped at 64
 ])
 def test_decode_plan(dims, splits):
     d = kivi.make_dims(*dims)
