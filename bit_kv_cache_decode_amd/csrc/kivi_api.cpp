@@ -11,17 +11,23 @@
 namespace kivi {
 namespace {
 
-// Resident decode workgroups on the device: 256 compute units x 4 (the
-// decode kernel is compiled for at least 4 waves per SIMD).
-constexpr long kWorkgroupSlots = 256 * 4;
+// Resident decode workgroups on the device: 256 compute units (MI355X) x
+// the decode kernel's workgroups per compute unit.
+constexpr long kWorkgroupSlots = 256L * kDecodeWorkgroupsPerCU;
+// Fixed cost of one decode workgroup (prologue, combine, publish, merge) in
+// units of one sub-chunk per wave, for choosing the split count.
+constexpr double kWorkgroupOverhead = 2.0;
 constexpr int kMaxSplits = 64;
 constexpr int kMaxResidual = 4096;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool supported(const kivi_dims &d) {
+  // one (sequence, head) region of any cache array must stay below 2 GiB
+  // (32-bit buffer offsets in the decode kernel)
+  const long code_bytes = (long)d.capacity * (d.head_dim * d.bits / 32) * 4;
   return d.head_dim == 128 && (d.group == 32 || d.group == 64 || d.group == 128) &&
-         d.residual <= kMaxResidual;
+         d.residual <= kMaxResidual && code_bytes < (1L << 31);
 }
 
 int check_dims(const kivi_dims *d) {
@@ -46,15 +52,24 @@ DecodePlan decode_plan(const kivi_dims &d) {
   p.sub = 512 / words;
   const long bh = (long)d.batch * d.heads;
   const long nsub = (d.capacity + p.sub - 1) / p.sub;
-  // Enough workgroups to fill every resident slot once (no second round, no
-  // tail), but no more than the work supports (about 2 sub-chunks per wave)
-  // and at most kMaxSplits.
-  long splits = (kWorkgroupSlots + bh - 1) / bh;
-  splits = std::min<long>(splits, std::max<long>(1, (nsub + 7) / 8));
-  splits = std::max<long>(1, std::min<long>(splits, kMaxSplits));
-  p.splits = (int)splits;
-  const long waves = 4 * splits;
-  p.win_per_wave = (int)(((d.residual + waves - 1) / waves + 3) / 4 * 4);
+  // Split count: minimise (rounds of resident workgroups) x (per-workgroup
+  // time), per-workgroup time = its share of sub-chunks per wave plus a
+  // fixed overhead; the first (smallest) split count wins ties.
+  int best = 1;
+  double best_cost = 0.0;
+  for (int s = 1; s <= kMaxSplits; ++s) {
+    const long waves = (long)kDecodeWavesPerWorkgroup * s;
+    if (s > 1 && nsub < waves) break;  // at least one sub-chunk per wave
+    const long rounds = (bh * s + kWorkgroupSlots - 1) / kWorkgroupSlots;
+    const double cost = (double)rounds * ((double)nsub / (double)waves + kWorkgroupOverhead);
+    if (s == 1 || cost < best_cost - 1e-9) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  p.splits = best;
+  const long waves = (long)kDecodeWavesPerWorkgroup * p.splits;
+  p.win_per_wave = (int)(((d.residual + waves - 1) / waves + 7) / 8 * 8);
   p.part_floats = 4 + (size_t)d.head_dim;
   const size_t parts = (size_t)bh * p.splits * p.part_floats * sizeof(float);
   p.counters_off = round_up(parts, 256);

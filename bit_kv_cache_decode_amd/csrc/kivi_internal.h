@@ -9,16 +9,28 @@
 
 namespace kivi {
 
-// Decode work split.  Each (sequence, head) gets `splits` workgroups of 4
-// waves.  Its quantized tokens are walked in sub-chunks of `sub` tokens
+// Decode workgroup shape: waves per workgroup (a multiple of 4, spread
+// evenly over the 4 SIMDs of a compute unit) and resident workgroups per
+// compute unit; the kernel is compiled for the resulting waves per SIMD.
+#ifndef KIVI_DECODE_WAVES
+#define KIVI_DECODE_WAVES 8
+#endif
+#ifndef KIVI_DECODE_WG_PER_CU
+#define KIVI_DECODE_WG_PER_CU 1
+#endif
+constexpr int kDecodeWavesPerWorkgroup = KIVI_DECODE_WAVES;
+constexpr int kDecodeWorkgroupsPerCU = KIVI_DECODE_WG_PER_CU;
+
+// Decode work split.  Each (sequence, head) gets `splits` workgroups of
+// kDecodeWavesPerWorkgroup waves.  Its quantized tokens are walked in sub-chunks of `sub` tokens
 // (512 / words-per-token: two 16-byte loads per lane per operand), dealt
-// round-robin to the 4 * splits waves; each wave also takes `win_per_wave`
-// consecutive fp16 window tokens.  The workgroups' partial softmax states are
+// round-robin to the waves; each wave also takes `win_per_wave`
+// consecutive fp16 window tokens (a multiple of 8).  The workgroups' partial softmax states are
 // merged by the last workgroup of that (sequence, head) to finish.
 struct DecodePlan {
   int sub;           // quantized tokens per sub-chunk
   int splits;        // workgroups per (sequence, head)
-  int win_per_wave;  // window tokens per wave (multiple of 4)
+  int win_per_wave;  // window tokens per wave (multiple of 8)
   size_t part_floats;     // floats of partial state per split (4 + D)
   size_t counters_off;    // byte offset of the per-(sequence, head) tickets
   size_t bytes;           // total workspace bytes

@@ -24,6 +24,20 @@ namespace {
 
 constexpr int kD = 128;        // head_dim covered by the compiled kernels
 constexpr int kThreads = 256;  // 4 waves of 64
+// Decode shape and pipelining: waves per workgroup and workgroups per
+// compute unit (shared with the host-side work split), hence waves per SIMD;
+// sub-chunks whose loads are kept in flight per wave; whether waves raise
+// their issue priority while they are behind.
+#ifndef KIVI_DECODE_DEPTH
+#define KIVI_DECODE_DEPTH 2
+#endif
+#ifndef KIVI_DECODE_PRIORITY
+#define KIVI_DECODE_PRIORITY 1
+#endif
+constexpr int kDecodeWaves = kDecodeWavesPerWorkgroup;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+constexpr int kDecodeWavesPerSimd = kDecodeWorkgroupsPerCU * kDecodeWaves / 4;
+constexpr int kDecodeDepth = KIVI_DECODE_DEPTH;
 
 using half_t = _Float16;
 
@@ -386,24 +400,21 @@ struct DecCfg {
 template <int BITS, int G>
 struct DecSmem {
   using C = DecCfg<BITS, G>;
-  float qs[kD];   // sm_scale * log2(e) * q
-  float qsf[kD];  // qs times the code-position factor 2^(24 - e) of each channel
   struct {
-    float acc[4][4][kD];  // [wave][row][channel]
-    float bias[4][4][16]; // [wave][row][word]
-    float m[4], l[4];
+    float acc[kDecodeWaves][4][kD];  // [wave][row][channel]
+    float bias[kDecodeWaves][4][16]; // [wave][row][word]
+    float m[kDecodeWaves], l[kDecodeWaves];
   } fin;
   union {
     struct {
+      float qs[kD];                     // sm_scale * log2(e) * q
       float qp[C::NTS][C::W * C::QPW];  // key multipliers, word-padded
       float cz[C::NTS][C::W];
-    } wave[4];
+    } wave[kDecodeWaves];
     struct {
-      float m[kMaxSplits], l[kMaxSplits], e[kMaxSplits];
-      float acc[8][kD];
+      float m[kMaxSplits], l[kMaxSplits];
     } mg;
   } u;
-  float red[32];
   int ticket;
 };
 
@@ -527,6 +538,35 @@ __device__ __forceinline__ void wave_publish(float (&fin_acc)[4][kD], float (&fi
   }
 }
 
+// ------------------------------------------------------- decode: streaming
+// All decode loads are raw buffer loads.  A descriptor covers one
+// (sequence, head) region of one array; the per-lane part of an offset is a
+// loop-invariant VGPR and the per-sub-chunk part a wave-uniform SGPR, so
+// issuing loads needs no vector instructions.  A descriptor with zero
+// records makes every load through it return 0 without touching memory.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+
+__device__ __forceinline__ uint2 bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+  return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ uint4 bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Registers holding every load of one sub-chunk of one wave.
 template <int BITS, int G>
 struct SubLoads {
@@ -546,9 +586,8 @@ struct LaneState {
   float acc[CPW];
 };
 
-// Fold new scores s[0..N) (already in the lane's max bookkeeping) into the
-// state: if any lane's running max grows, every lane rescales (by 1 where its
-// own max did not move).
+// Fold new scores s[0..N) into the state: if any lane's running max grows,
+// every lane rescales (by 1 where its own max did not move).
 template <int CPW, int N>
 __device__ __forceinline__ void update_max(LaneState<CPW> &st, const float *s) {
   float mc = st.m;
@@ -566,44 +605,62 @@ __device__ __forceinline__ void update_max(LaneState<CPW> &st, const float *s) {
   }
 }
 
-// Per-wave streaming over the quantized tokens of one (sequence, head).
+// Issue priority of a wave that has done `done` of its `total` sub-chunks:
+// 3 at the start, falling to 0 near the end.  The SIMD's arbiter prefers
+// higher priority and then older waves; without this the older wave of a
+// SIMD races ahead and the younger one finishes alone, its memory latency
+// then no longer hidden by any other wave.  With it, the waves sharing a
+// SIMD stay within about a quarter of their work of each other.
+__device__ __forceinline__ void set_progress_priority(int done, int total) {
+  const int lvl = total > 0 ? 3 - min(3, (4 * done) / total) : 0;
+  if (lvl >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
+  else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+// Per-wave stream over the quantized tokens of one (sequence, head): this
+// wave's sub-chunks are gw, gw + nw, gw + 2 nw, ... (n of them).
 template <int BITS, int G>
 struct QuantStream {
   using C = DecCfg<BITS, G>;
-  const uint32_t *kcb, *vcb;
-  const half_t *ksb, *kzb, *vsb, *vzb;
-  uint32_t code_off, vmeta_off, kmeta_off;
-  int ql, last_tile, gw, nw;
+  const void *kc, *vc, *ks, *kz, *vs, *vz;  // (sequence, head) regions
+  uint32_t code_bytes, meta_bytes;          // region sizes
+  uint32_t code_voff, vmeta_voff, kmeta_voff;  // per-lane byte offsets inside a tile
+  int ql, last_tile, gw, nw, n;
 
-  // first token of this wave's c-th sub-chunk (sub-chunks dealt round-robin)
   __device__ __forceinline__ int t0(int c) const { return (gw + c * nw) * C::SUB; }
 
-  // Issue every load of sub-chunk c, back to back.  Indices past the last
-  // valid token are clamped to valid ones; their data is never used.
+  // Issue every load of sub-chunk c, back to back.  For c >= n the loads go
+  // through zero-record descriptors (no memory traffic).  Token indices past
+  // the last valid one are clamped to valid ones; their data is never used.
   __device__ __forceinline__ void issue(SubLoads<BITS, G> &b, int c) const {
-    const int T0 = t0(c);
+    const bool live = c < n;
+    const uint32_t cb = live ? code_bytes : 0u, mb = live ? meta_bytes : 0u;
+    const int T0 = live ? t0(c) : 0;
     const int nvl = max(1, min(C::NL, (ql - T0) / C::TPL));
     const int tile0 = T0 / G;
+    const rsrc_t rks = make_rsrc(ks, mb), rkz = make_rsrc(kz, mb);
+    const rsrc_t rkc = make_rsrc(kc, cb), rvc = make_rsrc(vc, cb);
+    const rsrc_t rvs = make_rsrc(vs, mb), rvz = make_rsrc(vz, mb);
 #pragma unroll
     for (int k = 0; k < C::NTS; ++k) {
-      const size_t tk = (size_t)min(tile0 + k, last_tile) * kD;
-      b.ks[k] = *reinterpret_cast<const uint32_t *>(ksb + tk + kmeta_off);
-      b.kz[k] = *reinterpret_cast<const uint32_t *>(kzb + tk + kmeta_off);
+      const uint32_t so = (uint32_t)max(0, min(tile0 + k, last_tile)) * (kD * 2);
+      b.ks[k] = bload1(rks, kmeta_voff, so);
+      b.kz[k] = bload1(rkz, kmeta_voff, so);
     }
 #pragma unroll
     for (int j = 0; j < C::NL; ++j) {
       const int t = T0 + min(j, nvl - 1) * C::TPL;
-      const size_t tile = (size_t)(t / G);
-      b.kc[j] = *reinterpret_cast<const uint4 *>(kcb + tile * (C::W * G) + t % G + code_off);
+      b.kc[j] = bload4(rkc, code_voff, (uint32_t)((t / G) * (C::W * G) + t % G) * 4);
     }
 #pragma unroll
     for (int j = 0; j < C::NL; ++j) {
       const int t = T0 + min(j, nvl - 1) * C::TPL;
-      const size_t tile = (size_t)(t / G);
-      b.vc[j] = *reinterpret_cast<const uint4 *>(vcb + tile * (C::W * G) + t % G + code_off);
-      const size_t mo = tile * kD + t % G + vmeta_off;
-      b.vs[j] = *reinterpret_cast<const uint2 *>(vsb + mo);
-      b.vz[j] = *reinterpret_cast<const uint2 *>(vzb + mo);
+      b.vc[j] = bload4(rvc, code_voff, (uint32_t)((t / G) * (C::W * G) + t % G) * 4);
+      const uint32_t mo = (uint32_t)((t / G) * kD + t % G) * 2;
+      b.vs[j] = bload2(rvs, vmeta_voff, mo);
+      b.vz[j] = bload2(rvz, vmeta_voff, mo);
     }
   }
 };
@@ -679,77 +736,81 @@ __device__ __forceinline__ void process_sub(const SubLoads<BITS, G> &b, int T0, 
   }
 }
 
-// Window tokens [t_begin, t_end) of this wave, in the codes' lane layout:
-// lane (slot, w) takes tokens t_begin + 4 * slot + i (i < 4) and channels
-// w * CPW .. w * CPW + CPW - 1 of each.
+// ------------------------------------------------------- decode: fp16 window
+// Window tokens of one wave, one token per lane slot per step: lane
+// (slot, w) holds channels w * CPW .. w * CPW + CPW - 1 of token
+// begin + step * STEP + slot.  The loads of the first PF steps are issued
+// before any quantized load, so they are the first to arrive.
 template <int BITS, int G>
-__device__ __forceinline__ void window_tokens(const DecodeArgs &a, const DecSmem<BITS, G> &sm,
-                                              size_t bh, int t_begin, int t_end, int lane,
-                                              LaneState<DecCfg<BITS, G>::CPW> &st) {
+struct WinCfg {
   using C = DecCfg<BITS, G>;
-  constexpr int CPW = C::CPW, NV = CPW / 8;  // 16-byte vectors per token and lane
-  const int w = lane % C::W, slot = lane / C::W;
-  float qv[CPW];
+  static constexpr int NV = C::CPW / 8;  // 16-byte vectors per lane and token
+  static constexpr int STEP = C::TQS;    // tokens per step
+  static constexpr int PF = 16 / STEP;   // steps loaded up front (16 tokens)
+};
+
+template <int BITS, int G>
+struct WinStep {
+  uint4 k[WinCfg<BITS, G>::NV], v[WinCfg<BITS, G>::NV];
+};
+
+template <int BITS, int G>
+struct WinStream {
+  using WC = WinCfg<BITS, G>;
+  const void *kr, *vr;  // (sequence, head) window rows
+  uint32_t bytes;       // rows at or past this wave's end read as 0
+  uint32_t lane_voff;   // byte offset of this lane's channels in its token row
+  int begin, end;
+
+  __device__ __forceinline__ void issue(WinStep<BITS, G> &x, int step) const {
+    const rsrc_t rk = make_rsrc(kr, bytes), rv = make_rsrc(vr, bytes);
+    const uint32_t vo = lane_voff + (uint32_t)(begin + step * WC::STEP) * (kD * 2);
 #pragma unroll
-  for (int i = 0; i < CPW; ++i) qv[i] = sm.qs[w * CPW + i];
-  for (int t0 = t_begin; t0 < t_end; t0 += C::TPL) {
-    // keys first (scores), then values: keeps the live registers small
-    uint4 x[4][NV];
+    for (int v = 0; v < WC::NV; ++v) x.k[v] = bload4(rk, vo + 16 * v, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = min(t0 + 4 * slot + i, t_end - 1);  // clamped: data of absent tokens unused
-      const half_t *kr = a.k_res + (bh * a.R + t) * kD + w * CPW;
+    for (int v = 0; v < WC::NV; ++v) x.v[v] = bload4(rv, vo + 16 * v, 0);
+  }
+};
+
+template <int BITS, int G>
+__device__ __forceinline__ void window_step(const WinStep<BITS, G> &x, bool valid, const float *qv,
+                                            LaneState<DecCfg<BITS, G>::CPW> &st) {
+  using C = DecCfg<BITS, G>;
+  using WC = WinCfg<BITS, G>;
+  float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-      for (int v = 0; v < NV; ++v) x[i][v] = reinterpret_cast<const uint4 *>(kr)[v];
+  for (int v = 0; v < WC::NV; ++v) {
+    const uint32_t u[4] = {x.k[v].x, x.k[v].y, x.k[v].z, x.k[v].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a0 = mix_lo(qv[8 * v + 2 * e], u[e], a0);
+      a1 = mix_hi(qv[8 * v + 2 * e + 1], u[e], a1);
     }
-    float s[4];
+  }
+  float s = lane_group_sum<C::W>(a0 + a1);
+  s = valid ? s : -INFINITY;
+  update_max<C::CPW, 1>(st, &s);
+  // absent tokens contribute 0 (and the lane's max may still be -inf)
+  const float p = s > -INFINITY ? exp2_fast(s - st.m) : 0.0f;
+  st.l += p;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float a0 = 0.0f, a1 = 0.0f;
+  for (int v = 0; v < WC::NV; ++v) {
+    const uint32_t u[4] = {x.v[v].x, x.v[v].y, x.v[v].z, x.v[v].w};
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const uint32_t *u = reinterpret_cast<const uint32_t *>(&x[i][v]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a0 = mix_lo(qv[8 * v + 2 * e], u[e], a0);
-          a1 = mix_hi(qv[8 * v + 2 * e + 1], u[e], a1);
-        }
-      }
-      const float tot = lane_group_sum<C::W>(a0 + a1);
-      s[i] = (t0 + 4 * slot + i < t_end) ? tot : -INFINITY;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = min(t0 + 4 * slot + i, t_end - 1);
-      const half_t *vr = a.v_res + (bh * a.R + t) * kD + w * CPW;
-#pragma unroll
-      for (int v = 0; v < NV; ++v) x[i][v] = reinterpret_cast<const uint4 *>(vr)[v];
-    }
-    update_max<CPW, 4>(st, s);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // absent tokens contribute 0 (and the lane's max may still be -inf)
-      const float p = s[i] > -INFINITY ? exp2_fast(s[i] - st.m) : 0.0f;
-      st.l += p;
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const uint32_t *u = reinterpret_cast<const uint32_t *>(&x[i][v]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // value sums hold channel values times 2^(e - 24) (see above)
-          const int c0 = 8 * v + 2 * e;
-          st.acc[c0] = mix_lo(p * __builtin_ldexpf(1.0f, code_offset<BITS>(c0) - 24), u[e], st.acc[c0]);
-          st.acc[c0 + 1] =
-              mix_hi(p * __builtin_ldexpf(1.0f, code_offset<BITS>(c0 + 1) - 24), u[e], st.acc[c0 + 1]);
-        }
-      }
+    for (int e = 0; e < 4; ++e) {
+      // value sums hold channel values times 2^(e - 24) (see above)
+      const int c0 = 8 * v + 2 * e;
+      st.acc[c0] = mix_lo(p * __builtin_ldexpf(1.0f, code_offset<BITS>(c0) - 24), u[e], st.acc[c0]);
+      st.acc[c0 + 1] =
+          mix_hi(p * __builtin_ldexpf(1.0f, code_offset<BITS>(c0 + 1) - 24), u[e], st.acc[c0 + 1]);
     }
   }
 }
 
 template <int BITS, int G>
-__global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_kernel(DecodeArgs a) {
   using C = DecCfg<BITS, G>;
+  using WC = WinCfg<BITS, G>;
   __shared__ DecSmem<BITS, G> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -762,16 +823,6 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeArgs a) {
     ql = 0;
     rl = 0;
   }
-  if (tid < kD / 2) {
-    const uint32_t r = reinterpret_cast<const uint32_t *>(a.q + bh * kD)[tid];
-    const half2_t hq = __builtin_bit_cast(half2_t, r);
-    const float q0 = (float)hq.x * a.qscale, q1 = (float)hq.y * a.qscale;
-    sm.qs[2 * tid] = q0;
-    sm.qs[2 * tid + 1] = q1;
-    sm.qsf[2 * tid] = q0 * code_factor<BITS>((2 * tid) % C::CPW);
-    sm.qsf[2 * tid + 1] = q1 * code_factor<BITS>((2 * tid + 1) % C::CPW);
-  }
-  __syncthreads();
 
   // ---- this wave's share: quantized sub-chunks gw, gw + nw, ... and
   // window tokens [gw * win_per_wave, (gw + 1) * win_per_wave)
@@ -779,22 +830,53 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeArgs a) {
   const int jg = (w * C::CPW) / G;
   const size_t tps = (size_t)(a.cap / G);
   QuantStream<BITS, G> qs;
-  qs.kcb = a.k_codes + bh * tps * (C::W * G);
-  qs.vcb = a.v_codes + bh * tps * (C::W * G);
-  qs.ksb = a.k_scale + bh * tps * kD;
-  qs.kzb = a.k_zero + bh * tps * kD;
-  qs.vsb = a.v_scale + bh * tps * kD;
-  qs.vzb = a.v_zero + bh * tps * kD;
-  qs.code_off = (uint32_t)(w * G + 4 * slot);     // words, within a tile
-  qs.vmeta_off = (uint32_t)(jg * G + 4 * slot);   // halfs, within a tile
-  qs.kmeta_off = (uint32_t)(2 * lane);            // halfs, within a tile
+  qs.kc = a.k_codes + bh * tps * (C::W * G);
+  qs.vc = a.v_codes + bh * tps * (C::W * G);
+  qs.ks = a.k_scale + bh * tps * kD;
+  qs.kz = a.k_zero + bh * tps * kD;
+  qs.vs = a.v_scale + bh * tps * kD;
+  qs.vz = a.v_zero + bh * tps * kD;
+  qs.code_bytes = (uint32_t)(tps * (C::W * G) * 4);
+  qs.meta_bytes = (uint32_t)(tps * kD * 2);
+  qs.code_voff = (uint32_t)(w * G + 4 * slot) * 4;
+  qs.vmeta_voff = (uint32_t)(jg * G + 4 * slot) * 2;
+  qs.kmeta_voff = (uint32_t)lane * 4;
   qs.ql = ql;
   qs.last_tile = ql / G - 1;
-  qs.gw = split * 4 + wv;
-  qs.nw = 4 * S;
+  qs.gw = split * kDecodeWaves + wv;
+  qs.nw = kDecodeWaves * S;
+  qs.n = qs.gw * C::SUB < ql ? (ql - qs.gw * C::SUB + qs.nw * C::SUB - 1) / (qs.nw * C::SUB) : 0;
+
+  WinStream<BITS, G> ws;
+  ws.kr = a.k_res + bh * a.R * kD;
+  ws.vr = a.v_res + bh * a.R * kD;
+  ws.begin = qs.gw * a.win_per_wave;
+  ws.end = min(rl, ws.begin + a.win_per_wave);
+  ws.bytes = (uint32_t)max(0, ws.end) * (kD * 2);
+  ws.lane_voff = (uint32_t)(slot * kD + w * C::CPW) * 2;
+  const int wsteps = ws.end > ws.begin ? (ws.end - ws.begin + WC::STEP - 1) / WC::STEP : 0;
+
+  // The query (every wave reads it: lane i holds channels 2i, 2i + 1),
+  // then kDecodeDepth quantized sub-chunks.  Each sub-chunk's registers are
+  // refilled with sub-chunk c + kDecodeDepth as soon as sub-chunk c is done,
+  // so kDecodeDepth - 1 stay in flight while one is computed.  The fp16
+  // window tokens come last: their loads are issued once the quantized
+  // loads are all out, and they are computed after the quantized tokens.
+  // (Issuing everything up front would not help: the memory system serves
+  // all waves' requests interleaved, so the first data a wave needs would
+  // arrive no sooner than the rest.)
+  const uint32_t qraw = bload1(make_rsrc(a.q + bh * kD, kD * 2), (uint32_t)lane * 4, 0);
+  SubLoads<BITS, G> ring[kDecodeDepth];
+#pragma unroll
+  for (int k = 0; k < kDecodeDepth; ++k) qs.issue(ring[k], k);
+
   auto &stg = sm.u.wave[wv];
-  const float qs0 = sm.qs[2 * lane], qs1 = sm.qs[2 * lane + 1];
-  const float qf0 = sm.qsf[2 * lane], qf1 = sm.qsf[2 * lane + 1];
+  const half2_t hq = __builtin_bit_cast(half2_t, qraw);
+  const float qs0 = (float)hq.x * a.qscale, qs1 = (float)hq.y * a.qscale;
+  const float qf0 = qs0 * code_factor<BITS>((2 * lane) % C::CPW);
+  const float qf1 = qs1 * code_factor<BITS>((2 * lane + 1) % C::CPW);
+  stg.qs[2 * lane] = qs0;  // for the window tokens, read back at the end
+  stg.qs[2 * lane + 1] = qs1;
 
   LaneState<C::CPW> st;
   st.m = -INFINITY;
@@ -803,36 +885,64 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < C::CPW; ++i) st.acc[i] = 0.0f;
 
-  int n = 0;  // quantized sub-chunks of this wave
-  if (qs.gw * C::SUB < ql) n = (ql - qs.gw * C::SUB + qs.nw * C::SUB - 1) / (qs.nw * C::SUB);
-  const int w_begin = qs.gw * a.win_per_wave;
-  const int w_end = min(rl, w_begin + a.win_per_wave);
+  // Whole rounds of kDecodeDepth sub-chunks (no branch inside a round, so
+  // the wait before each sub-chunk only covers its own loads), then the
+  // remaining n mod kDecodeDepth, whose loads are already in flight.
+  int c0 = 0;
+  for (; c0 + kDecodeDepth <= qs.n; c0 += kDecodeDepth) {
+#pragma unroll
+    for (int k = 0; k < kDecodeDepth; ++k) {
+#if KIVI_DECODE_PRIORITY
+      set_progress_priority(c0 + k, qs.n);
+#endif
+      process_sub<BITS, G>(ring[k], qs.t0(c0 + k), ql, lane, qs0, qs1, qf0, qf1, stg.qp, stg.cz,
+                           st);
+      qs.issue(ring[k], c0 + k + kDecodeDepth);
+    }
+  }
+  WinStep<BITS, G> wpf[WC::PF];
+#pragma unroll
+  for (int i = 0; i < WC::PF; ++i) ws.issue(wpf[i], i);
+#pragma unroll
+  for (int k = 0; k < kDecodeDepth - 1; ++k)
+    if (c0 + k < qs.n) {
+#if KIVI_DECODE_PRIORITY
+      set_progress_priority(c0 + k, qs.n);
+#endif
+      process_sub<BITS, G>(ring[k], qs.t0(c0 + k), ql, lane, qs0, qs1, qf0, qf1, stg.qp, stg.cz,
+                           st);
+    }
+#if KIVI_DECODE_PRIORITY
+  __builtin_amdgcn_s_setprio(0);
+#endif
 
-  // The first quantized loads go out before the window tokens are read, and
-  // the loads of sub-chunk c + 1 are in flight while sub-chunk c is computed.
-  SubLoads<BITS, G> A, B;
-  if (n > 0) qs.issue(A, 0);
-  if (w_begin < w_end) window_tokens<BITS, G>(a, sm, bh, w_begin, w_end, lane, st);
-  for (int c = 0; c < n; c += 2) {
-    qs.issue(B, min(c + 1, n - 1));
-    process_sub<BITS, G>(A, qs.t0(c), ql, lane, qs0, qs1, qf0, qf1, stg.qp, stg.cz, st);
-    if (c + 1 >= n) break;
-    qs.issue(A, min(c + 2, n - 1));
-    process_sub<BITS, G>(B, qs.t0(c + 1), ql, lane, qs0, qs1, qf0, qf1, stg.qp, stg.cz, st);
+  if (wsteps > 0) {
+    __builtin_amdgcn_wave_barrier();
+    float qv[C::CPW];
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) qv[i] = stg.qs[w * C::CPW + i];
+#pragma unroll
+    for (int i = 0; i < WC::PF; ++i)
+      if (i < wsteps) window_step<BITS, G>(wpf[i], ws.begin + i * WC::STEP + slot < ws.end, qv, st);
+    for (int i = WC::PF; i < wsteps; ++i) {  // windows longer than the prefetched steps
+      WinStep<BITS, G> x;
+      ws.issue(x, i);
+      window_step<BITS, G>(x, ws.begin + i * WC::STEP + slot < ws.end, qv, st);
+    }
   }
   wave_publish<C::CPW, C::W, C::W == 8>(sm.fin.acc[wv], sm.fin.bias[wv], sm.fin.m[wv],
                                          sm.fin.l[wv], st.m, st.l, st.acc, st.bias);
   __syncthreads();
 
-  // ---- combine the four waves into the workgroup's partial state
+  // ---- combine the waves into the workgroup's state (channel tid)
   float M = -INFINITY;
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < kDecodeWaves; ++x)
     if (sm.fin.l[x] > 0.0f) M = fmaxf(M, sm.fin.m[x]);
   float L = 0.0f, acc_out = 0.0f;
   if (M != -INFINITY) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < kDecodeWaves; ++x) {
       const float e = sm.fin.l[x] > 0.0f ? exp2_fast(sm.fin.m[x] - M) : 0.0f;
       L += e * sm.fin.l[x];
       if (tid < kD && e != 0.0f) {
@@ -845,6 +955,10 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeArgs a) {
         acc_out += e * fmaf(sa, code_factor<BITS>(tid % C::CPW), sb);
       }
     }
+  }
+  if (S == 1) {  // the workgroup saw every token: finish here
+    if (tid < kD) a.out[bh * kD + tid] = L > 0.0f ? acc_out / L : 0.0f;
+    return;
   }
 
   // ---- publish the partial state and take a ticket
@@ -873,41 +987,23 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeArgs a) {
   // ---- last workgroup of this (sequence, head): merge all partials, read
   // with device-scope atomic loads (coherent with the stores above)
   const float *P0 = a.part + bh * S * (size_t)a.part_stride;
-  for (int s = tid; s < S; s += kThreads) {
-    sm.u.mg.m[s] = load_agent(P0 + (size_t)s * a.part_stride);
-    sm.u.mg.l[s] = load_agent(P0 + (size_t)s * a.part_stride + 1);
+  if (tid < S) {
+    sm.u.mg.m[tid] = load_agent(P0 + (size_t)tid * a.part_stride);
+    sm.u.mg.l[tid] = load_agent(P0 + (size_t)tid * a.part_stride + 1);
   }
-  __syncthreads();
-  float mx = -INFINITY;
-  for (int s = tid; s < S; s += kThreads)
-    if (sm.u.mg.l[s] > 0.0f) mx = fmaxf(mx, sm.u.mg.m[s]);
-  mx = block_max(mx, sm.red);
-  float lsum[1] = {0.0f};
-  for (int s = tid; s < S; s += kThreads) {
-    const float e = sm.u.mg.l[s] > 0.0f ? exp2_fast(sm.u.mg.m[s] - mx) : 0.0f;
-    sm.u.mg.e[s] = e;
-    lsum[0] += e * sm.u.mg.l[s];
-  }
-  block_sum<1>(lsum, sm.red);
-  const int cq = tid & 31, sl = tid >> 5;
-  float macc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = sl; s < S; s += 8) {
-    const float e = sm.u.mg.e[s];
-    if (e != 0.0f) {
-      const float *src = P0 + (size_t)s * a.part_stride + kPartHead + 4 * cq;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) macc[i] = fmaf(e, load_agent(src + i), macc[i]);
-    }
-  }
-  *reinterpret_cast<float4 *>(&sm.u.mg.acc[sl][4 * cq]) =
-      make_float4(macc[0], macc[1], macc[2], macc[3]);
   __syncthreads();
   if (tid < kD) {
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s += sm.u.mg.acc[i][tid];
-    a.out[bh * kD + tid] = lsum[0] > 0.0f ? s / lsum[0] : 0.0f;
+    float mx = -INFINITY;
+    for (int s = 0; s < S; ++s)
+      if (sm.u.mg.l[s] > 0.0f) mx = fmaxf(mx, sm.u.mg.m[s]);
+    float lsum = 0.0f, macc = 0.0f;
+    for (int s = 0; s < S; ++s) {
+      const float e = sm.u.mg.l[s] > 0.0f ? exp2_fast(sm.u.mg.m[s] - mx) : 0.0f;
+      lsum += e * sm.u.mg.l[s];
+      if (e != 0.0f)
+        macc = fmaf(e, load_agent(P0 + (size_t)s * a.part_stride + kPartHead + tid), macc);
+    }
+    a.out[bh * kD + tid] = lsum > 0.0f ? macc / lsum : 0.0f;
   }
   if (tid == 0) __hip_atomic_store(a.tickets + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -930,7 +1026,7 @@ int launch_encode(int bits, int G, const EncodeArgs &ea, dim3 grid, hipStream_t 
 
 template <int BITS, int G>
 int launch_decode_t(const DecodeArgs &da, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<BITS, G>), grid, dim3(kThreads), 0, st, da);
+  hipLaunchKernelGGL((decode_kernel<BITS, G>), grid, dim3(kDecodeThreads), 0, st, da);
   return (int)hipGetLastError();
 }
 

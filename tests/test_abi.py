@@ -51,11 +51,11 @@ def test_validate_dims_codes():
 
 @pytest.mark.parametrize("dims,splits", [
     ((1, 1, 128, 2, 32, 32, 256), 1),         # one workgroup does it all
-    ((8, 32, 128, 2, 32, 128, 4096), 4),      # 4 per (sequence, head): 1024 resident workgroups
-    ((16, 40, 128, 2, 32, 128, 2048), 2),
+    ((8, 32, 128, 2, 32, 128, 4096), 1),      # one workgroup per (sequence, head) fills the chip
+    ((16, 40, 128, 2, 32, 128, 2048), 1),
     ((64, 32, 128, 2, 32, 128, 8320), 1),     # many sequences: one workgroup each
-    ((1, 32, 128, 2, 128, 128, 131072), 32),  # long context: 32 workgroups per head
-    ((1, 32, 128, 4, 128, 128, 131072), 32),
+    ((1, 32, 128, 2, 128, 128, 131072), 8),   # long context: 8 workgroups per head
+    ((1, 32, 128, 4, 128, 128, 131072), 8),
     ((1, 1, 128, 2, 32, 32, 0), 1),           # window only
     ((1, 1, 128, 2, 32, 4096, 1 << 24), 64),  # capped at 64
 ])
