@@ -39,7 +39,7 @@ int check_dims(const kivi_dims *d) {
 
 bool cache_ok(const kivi_cache *c) {
   return c && c->k_codes && c->k_scale && c->k_zero && c->v_codes && c->v_scale && c->v_zero &&
-         c->k_res && c->v_res && c->q_len && c->r_len && c->status;
+         c->k_res && c->v_res && c->q_len && c->r_len && c->status && c->tickets;
 }
 
 int hip_rc(int rc) { return rc == 0 ? KIVI_OK : KIVI_EHIP; }

@@ -40,8 +40,13 @@ constexpr int kDecodeWavesPerSimd = kDecodeWorkgroupsPerCU * kDecodeWaves / 4;
 constexpr int kDecodeDepth = KIVI_DECODE_DEPTH;
 
 using half_t = _Float16;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------ wave helpers
+
+__device__ __forceinline__ uint32_t u4_get(const uint4 &v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -112,6 +117,7 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 struct GroupParams {
   float mn;  // canonical minimum (zero-point)
   float s;   // stored step as fp32
+  float rs;  // approximate 1 / s (0 when s == 0)
   half_t zero16, scale16;
 };
 
@@ -122,13 +128,27 @@ __device__ __forceinline__ GroupParams group_params(float mn_raw, float mx_raw, 
   const float step = (mx - g.mn) / levels;
   g.scale16 = (half_t)step;  // round to nearest even
   g.s = (float)g.scale16;
+  g.rs = g.s != 0.0f ? __builtin_amdgcn_rcpf(g.s) : 0.0f;
   g.zero16 = (half_t)g.mn;   // exact: mn is an fp16 value
   return g;
 }
 
-__device__ __forceinline__ uint32_t encode_one(float x, float mn, float s, float top) {
+// clamp(rint((x - mn) / s), 0, top) with an IEEE division, computed as
+// rint((x - mn) * rs) except where that product lies within 2^-16 of a
+// half-integer.  Why that is the same value: the quotient q = (x - mn) / s
+// is below 32 (x - mn is at most the group's range and s is at least half
+// the range over the levels, B <= 4), and the product differs from q by at
+// most q * 2^-22 < 2^-17 (one rounding of the product, a reciprocal within
+// one ulp).  Away from the half-integers by more than that, the product, q
+// and q rounded to fp32 (which cannot cross an fp32-representable
+// half-integer) all round to the same integer.  Near them, the division is
+// done.
+__device__ __forceinline__ uint32_t encode_one(float x, float mn, float s, float rs, float top) {
   if (s == 0.0f) return 0u;
-  float c = rintf((x - mn) / s);
+  const float d = x - mn;
+  const float q = d * rs;
+  float c = rintf(q);
+  if (fabsf(fabsf(q - c) - 0.5f) < 0x1p-16f) c = rintf(d / s);
   c = fminf(fmaxf(c, 0.0f), top);
   return (uint32_t)c;
 }
@@ -143,7 +163,7 @@ struct EncodeArgs {
   half_t *k_res, *v_res;         // window [batch][heads][R][D] (prefill writes it)
   int32_t *q_len, *r_len;
   const int32_t *len, *res;      // prefill: prompt lengths, window sizes (res may be null)
-  uint32_t *status;
+  uint32_t *status, *tickets;
   int heads, R, cap, prefill;
 };
 
@@ -170,108 +190,243 @@ __device__ __forceinline__ void load_tile(half_t (*xs)[kD + 8], const half_t *sr
   }
 }
 
-// One workgroup quantizes one tile of G tokens of one (sequence, head):
-// keys per channel over the G tokens, values per token over G channels, and
-// packs both into the tiled code layout.
+// Prefill: one workgroup quantizes one tile of G tokens of one
+// (sequence, head): keys per channel over the G tokens, values per token
+// over G channels, and packs both into the tiled code layout.  Both tiles
+// are loaded up front; threads 0..127 then take the 128 key groups and
+// threads 128..255 the 128 value groups.
 template <int BITS, int G>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
-  constexpr int W = kD * BITS / 32, CPW = 32 / BITS, NVG = kD / G;
+  constexpr int W = kD * BITS / 32, CPW = 32 / BITS;
   constexpr float kTop = (float)((1 << BITS) - 1);
-  static_assert(G * NVG == kD, "one value group per thread");
+  static_assert(G * (kD / G) == kD && kD == 128, "128 key groups and 128 value groups per tile");
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
 
-  int ntiles, dst0;
-  if (a.prefill) {
-    int n, r;
-    const bool ok = prefill_split(a, b, G, &n, &r) && n - r <= a.cap;
-    ntiles = ok ? (n - r) / G : 0;
-    dst0 = 0;
-  } else {
-    const int ql = a.q_len[b], rl = a.r_len[b];
-    ntiles = flush_ok(ql, rl, G, a.R, a.cap) ? a.R / G : 0;
-    dst0 = ql;
-  }
+  int n, r;
+  const bool ok = prefill_split(a, b, G, &n, &r) && n - r <= a.cap;
+  const int ntiles = ok ? (n - r) / G : 0;
+  const int dst0 = 0;
   if (tile >= ntiles) return;
 
-  __shared__ half_t xs[G][kD + 8];
-  __shared__ float gmn[kD], gst[kD];
+  __shared__ half_t xk[G][kD + 8], xv[G][kD + 8];
+  __shared__ float kmn[kD], kst[kD], krs[kD], vmn[kD], vst[kD], vrs[kD];
 
   const size_t bh = (size_t)b * a.heads + h;
   const size_t src_off = (bh * a.src_tokens + (size_t)tile * G) * kD;
   const size_t ktile = bh * (size_t)(a.cap / G) + (size_t)(dst0 / G) + tile;
 
-  // ---- keys: one group per channel over the G tokens of the tile
-  load_tile<G>(xs, a.src_k + src_off);
+  {
+    constexpr int N = G * (kD / 8);  // uint4 per tile
+    const uint4 *sk = reinterpret_cast<const uint4 *>(a.src_k + src_off);
+    const uint4 *sv = reinterpret_cast<const uint4 *>(a.src_v + src_off);
+    uint4 rk[(N + kThreads - 1) / kThreads], rv[(N + kThreads - 1) / kThreads];
+#pragma unroll
+    for (int i = 0; i < (N + kThreads - 1) / kThreads; ++i) {
+      const int e = tid + i * kThreads;
+      if (e < N) {
+        rk[i] = sk[e];
+        rv[i] = sv[e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (N + kThreads - 1) / kThreads; ++i) {
+      const int e = tid + i * kThreads;
+      if (e < N) {
+        const int t = e / (kD / 8), c = e % (kD / 8);
+        *reinterpret_cast<uint4 *>(&xk[t][c * 8]) = rk[i];
+        *reinterpret_cast<uint4 *>(&xv[t][c * 8]) = rv[i];
+      }
+    }
+  }
   __syncthreads();
+
   if (tid < kD) {
+    // key group: channel tid over the G tokens
     float mn = INFINITY, mx = -INFINITY;
     for (int t = 0; t < G; ++t) {
-      const float x = (float)xs[t][tid];
+      const float x = (float)xk[t][tid];
       mn = fminf(mn, x);
       mx = fmaxf(mx, x);
     }
     const GroupParams g = group_params(mn, mx, kTop);
     a.k_zero[ktile * kD + tid] = g.zero16;
     a.k_scale[ktile * kD + tid] = g.scale16;
-    gmn[tid] = g.mn;
-    gst[tid] = g.s;
-  }
-  __syncthreads();
-  for (int wi = tid; wi < W * G; wi += kThreads) {
-    const int w = wi / G, t = wi % G;
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int c = w * CPW + i;
-      word |= encode_one((float)xs[t][c], gmn[c], gst[c], kTop) << (i * BITS);
-    }
-    a.k_codes[ktile * (W * G) + wi] = word;
-  }
-  __syncthreads();
-
-  // ---- values: one group per (token, G consecutive channels)
-  load_tile<G>(xs, a.src_v + src_off);
-  __syncthreads();
-  // value zero-points and steps are tiled like the codes: [tile][group][token]
-  if (tid < kD) {
-    const int j = tid / G, t = tid % G;
+    kmn[tid] = g.mn;
+    kst[tid] = g.s;
+    krs[tid] = g.rs;
+  } else {
+    // value group: token t, channels j*G .. j*G+G-1; stored tiled like the
+    // codes, [tile][group][token]
+    const int e = tid - kD, j = e / G, t = e % G;
     float mn = INFINITY, mx = -INFINITY;
     for (int c = 0; c < G; ++c) {
-      const float x = (float)xs[t][j * G + c];
+      const float x = (float)xv[t][j * G + c];
       mn = fminf(mn, x);
       mx = fmaxf(mx, x);
     }
     const GroupParams g = group_params(mn, mx, kTop);
-    a.v_zero[ktile * kD + tid] = g.zero16;
-    a.v_scale[ktile * kD + tid] = g.scale16;
-    gmn[tid] = g.mn;
-    gst[tid] = g.s;
+    a.v_zero[ktile * kD + e] = g.zero16;
+    a.v_scale[ktile * kD + e] = g.scale16;
+    vmn[e] = g.mn;
+    vst[e] = g.s;
+    vrs[e] = g.rs;
   }
   __syncthreads();
+
   for (int wi = tid; wi < W * G; wi += kThreads) {
     const int w = wi / G, t = wi % G;
+    uint32_t kw = 0, vw = 0;
     const int gi = ((w * CPW) / G) * G + t;
-    const float mn = gmn[gi], s = gst[gi];
-    uint32_t word = 0;
+    const float vm = vmn[gi], vs = vst[gi], vr = vrs[gi];
 #pragma unroll
-    for (int i = 0; i < CPW; ++i)
-      word |= encode_one((float)xs[t][w * CPW + i], mn, s, kTop) << (i * BITS);
-    a.v_codes[ktile * (W * G) + wi] = word;
+    for (int i = 0; i < CPW; ++i) {
+      const int c = w * CPW + i;
+      kw |= encode_one((float)xk[t][c], kmn[c], kst[c], krs[c], kTop) << (i * BITS);
+      vw |= encode_one((float)xv[t][c], vm, vs, vr, kTop) << (i * BITS);
+    }
+    a.k_codes[ktile * (W * G) + wi] = kw;
+    a.v_codes[ktile * (W * G) + wi] = vw;
   }
 }
 
-// Flush commit: runs after encode_kernel on the same stream, so no encode
-// workgroup can observe the updated lengths.
-__global__ void flush_commit_kernel(EncodeArgs a, int batch, int G) {
-  for (int b = threadIdx.x; b < batch; b += blockDim.x) {
-    const int ql = a.q_len[b], rl = a.r_len[b];
-    if (rl != a.R) continue;
-    if (flush_ok(ql, rl, G, a.R, a.cap)) {
-      a.q_len[b] = ql + a.R;
-      a.r_len[b] = 0;
-    } else {
+// Flush: one workgroup of 1024 threads per (sequence, head) quantizes its
+// full window in blocks of up to 128 tokens (all of a block's loads are
+// issued before the first is used).  Each workgroup takes one of sequence
+// b's tickets once it has read b's lengths; the workgroup that took the
+// last one (every head has read the lengths by then, and none reads them
+// again) sets q_len[b] += R, r_len[b] = 0 and clears the ticket when it is
+// done.
+constexpr int kFlushThreads = 1024;
+
+template <int BITS, int G>
+__global__ __launch_bounds__(kFlushThreads) void flush_kernel(EncodeArgs a) {
+  constexpr int W = kD * BITS / 32, CPW = 32 / BITS;
+  constexpr float kTop = (float)((1 << BITS) - 1);
+  constexpr int TB = 128;                   // tokens per block
+  constexpr int NT = TB / G;                // tiles per full block
+  constexpr int PT = TB * (kD / 8) / kFlushThreads;  // uint4 per thread and operand
+  static_assert(NT * (kD / 2) <= kFlushThreads / 2 && NT * kD <= kFlushThreads / 2,
+                "key-group and value-group threads fit in the two halves of the workgroup");
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+
+  const int ql = a.q_len[b], rl = a.r_len[b];
+  if (!flush_ok(ql, rl, G, a.R, a.cap)) {
+    if (rl == a.R && h == 0 && tid == 0)
       atomicOr(a.status, (ql < 0 || ql % G) ? KIVI_ST_BAD_LENGTH : KIVI_ST_CAPACITY);
+    return;
+  }
+  // The ticket is taken now (the lengths have been read: the branch above
+  // depends on them) and looked at only at the end, so its latency hides
+  // behind the window loads.
+  uint32_t ticket = 0;
+  if (tid == 0)
+    ticket = __hip_atomic_fetch_add(a.tickets + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  __shared__ half_t xk[TB][kD + 8], xv[TB][kD + 8];
+  __shared__ float4 kp[NT * kD], vp[NT * kD];  // {minimum, step, 1 / step, -}
+  const size_t bh = (size_t)b * a.heads + h;
+  const uint4 *sk = reinterpret_cast<const uint4 *>(a.k_res + bh * a.R * kD);
+  const uint4 *sv = reinterpret_cast<const uint4 *>(a.v_res + bh * a.R * kD);
+
+  for (int blk = 0; blk < a.R; blk += TB) {
+    const int nt = min(TB, a.R - blk) / G;  // tiles in this block
+    const int ne = nt * G * (kD / 8);
+    const size_t tile0 = bh * (size_t)(a.cap / G) + (size_t)((ql + blk) / G);
+    {
+      uint4 rk[PT], rv[PT];
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {  // clamped: a partial block's extra loads are unused
+        const int e = min(tid + i * kFlushThreads, ne - 1);
+        rk[i] = sk[(size_t)blk * (kD / 8) + e];
+        rv[i] = sv[(size_t)blk * (kD / 8) + e];
+      }
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int e = tid + i * kFlushThreads;
+        if (e < ne) {
+          const int t = e / (kD / 8), c = e % (kD / 8);
+          *reinterpret_cast<uint4 *>(&xk[t][c * 8]) = rk[i];
+          *reinterpret_cast<uint4 *>(&xv[t][c * 8]) = rv[i];
+        }
+      }
     }
+    __syncthreads();
+    if (tid < kFlushThreads / 2) {
+      // key groups: tile tid / 64, channels 2 * (tid % 64) and the next one,
+      // each over the tile's G tokens
+      if (tid < nt * (kD / 2)) {
+        const int tl = tid / (kD / 2), c = 2 * (tid % (kD / 2));
+        float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
+#pragma unroll 8
+        for (int t = 0; t < G; ++t) {
+          const half2_t x2 = *reinterpret_cast<const half2_t *>(&xk[tl * G + t][c]);
+          const float x0 = (float)x2.x, x1 = (float)x2.y;
+          mn0 = fminf(mn0, x0);
+          mx0 = fmaxf(mx0, x0);
+          mn1 = fminf(mn1, x1);
+          mx1 = fmaxf(mx1, x1);
+        }
+        const GroupParams g0 = group_params(mn0, mx0, kTop), g1 = group_params(mn1, mx1, kTop);
+        const size_t o = tile0 * kD + (size_t)tl * kD + c;
+        *reinterpret_cast<half2_t *>(a.k_zero + o) = half2_t{g0.zero16, g1.zero16};
+        *reinterpret_cast<half2_t *>(a.k_scale + o) = half2_t{g0.scale16, g1.scale16};
+        kp[tl * kD + c] = make_float4(g0.mn, g0.s, g0.rs, 0.0f);
+        kp[tl * kD + c + 1] = make_float4(g1.mn, g1.s, g1.rs, 0.0f);
+      }
+    } else {
+      // value groups: tile e / 128, group (e % 128) / G, token (e % 128) % G,
+      // in the tiled [tile][group][token] order of the value zero-points
+      const int e = tid - kFlushThreads / 2;
+      if (e < nt * kD) {
+        const int tl = e / kD, j = (e % kD) / G, t = tl * G + (e % kD) % G;
+        float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < G; c += 8) {
+          const uint4 u = *reinterpret_cast<const uint4 *>(&xv[t][j * G + c]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const half2_t x2 = __builtin_bit_cast(half2_t, u4_get(u, q));
+            mn = fminf(mn, fminf((float)x2.x, (float)x2.y));
+            mx = fmaxf(mx, fmaxf((float)x2.x, (float)x2.y));
+          }
+        }
+        const GroupParams g = group_params(mn, mx, kTop);
+        a.v_zero[tile0 * kD + e] = g.zero16;
+        a.v_scale[tile0 * kD + e] = g.scale16;
+        vp[e] = make_float4(g.mn, g.s, g.rs, 0.0f);
+      }
+    }
+    __syncthreads();
+    for (int wi = tid; wi < nt * W * G; wi += kFlushThreads) {
+      const int tl = wi / (W * G), w = (wi / G) % W, tt = wi % G, t = tl * G + tt;
+      const float4 v = vp[tl * kD + ((w * CPW) / G) * G + tt];
+      uint32_t kw = 0, vw = 0;
+#pragma unroll
+      for (int i = 0; i < CPW; i += 8) {
+        const uint4 uk = *reinterpret_cast<const uint4 *>(&xk[t][w * CPW + i]);
+        const uint4 uv = *reinterpret_cast<const uint4 *>(&xv[t][w * CPW + i]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int c = w * CPW + i + q;
+          const half2_t k2 = __builtin_bit_cast(half2_t, u4_get(uk, q / 2));
+          const half2_t v2 = __builtin_bit_cast(half2_t, u4_get(uv, q / 2));
+          const float xk1 = (q & 1) ? (float)k2.y : (float)k2.x;
+          const float xv1 = (q & 1) ? (float)v2.y : (float)v2.x;
+          const float4 kq = kp[tl * kD + c];
+          kw |= encode_one(xk1, kq.x, kq.y, kq.z, kTop) << ((i + q) * BITS);
+          vw |= encode_one(xv1, v.x, v.y, v.z, kTop) << ((i + q) * BITS);
+        }
+      }
+      a.k_codes[tile0 * (W * G) + wi] = kw;
+      a.v_codes[tile0 * (W * G) + wi] = vw;
+    }
+    __syncthreads();
+  }
+
+  if (tid == 0 && ticket == (uint32_t)a.heads - 1) {
+    a.q_len[b] = ql + a.R;
+    a.r_len[b] = 0;
+    a.tickets[b] = 0u;
   }
 }
 
@@ -306,31 +461,33 @@ __global__ void prefill_commit_kernel(EncodeArgs a, int batch, int G) {
 }
 
 // ----------------------------------------------------------------- append
-// One workgroup per sequence copies the new token of every head into window
-// slot r_len[b], then bumps r_len[b].  Every thread reads r_len[b] before the
-// barrier and only thread 0 writes it after, so no thread sees the new value.
-__global__ __launch_bounds__(kThreads) void append_kernel(const half_t *k_new, const half_t *v_new,
-                                                          half_t *k_res, half_t *v_res,
-                                                          int32_t *r_len, uint32_t *status,
-                                                          int heads, int R) {
-  const int b = blockIdx.x;
+// One workgroup of 1024 threads per sequence copies the new token of every
+// head into window slot r_len[b] (one 16-byte piece of a key or value row
+// per thread and pass), then bumps r_len[b].  Every thread reads r_len[b]
+// before the barrier and only thread 0 writes it after, so no thread sees
+// the new value.
+constexpr int kAppendThreads = 1024;
+
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(
+    const half_t *k_new, const half_t *v_new, half_t *k_res, half_t *v_res, int32_t *r_len,
+    uint32_t *status, int heads, int R) {
+  const int b = blockIdx.x, tid = threadIdx.x;
   const int r = r_len[b];
   __syncthreads();
   if (r < 0 || r >= R) {
-    if (threadIdx.x == 0) atomicOr(status, r < 0 ? KIVI_ST_BAD_LENGTH : KIVI_ST_RESIDUAL_FULL);
+    if (tid == 0) atomicOr(status, r < 0 ? KIVI_ST_BAD_LENGTH : KIVI_ST_RESIDUAL_FULL);
     return;
   }
   constexpr int V = kD / 8;  // uint4 per row
-  for (int i = threadIdx.x; i < heads * V; i += kThreads) {
-    const int h = i / V, c = i % V;
-    const size_t bh = (size_t)b * heads + h;
-    const size_t src = bh * V + c;
-    const size_t dst = (bh * R + r) * V + c;
-    reinterpret_cast<uint4 *>(k_res)[dst] = reinterpret_cast<const uint4 *>(k_new)[src];
-    reinterpret_cast<uint4 *>(v_res)[dst] = reinterpret_cast<const uint4 *>(v_new)[src];
+  const int n = heads * V;   // uint4 per operand and sequence
+  for (int i = tid; i < 2 * n; i += kAppendThreads) {
+    const int e = i < n ? i : i - n;
+    const size_t bh = (size_t)b * heads + e / V;
+    const uint4 x = reinterpret_cast<const uint4 *>(i < n ? k_new : v_new)[(size_t)b * n + e];
+    reinterpret_cast<uint4 *>(i < n ? k_res : v_res)[(bh * R + r) * V + e % V] = x;
   }
   __syncthreads();
-  if (threadIdx.x == 0) r_len[b] = r + 1;
+  if (tid == 0) r_len[b] = r + 1;
 }
 
 // ----------------------------------------------------------------- decode
@@ -379,7 +536,6 @@ struct DecodeArgs {
 constexpr int kMaxSplits = 128;
 constexpr int kPartHead = 4;   // m, l, 2 pad floats before the 128 values
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 template <int BITS, int G>
 struct DecCfg {
@@ -501,9 +657,6 @@ __device__ __forceinline__ void axpy_pairs(uint32_t u, uint32_t uh, float pp, fl
   }
 }
 
-__device__ __forceinline__ uint32_t u4_get(const uint4 &v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
 
 // Combine the per-lane states of one wave and publish them to sm.fin.
 // CPW: channels per lane; WPR: lanes per token slot; FOLD8: lanes l and l^8
@@ -1043,6 +1196,7 @@ EncodeArgs encode_args(const kivi_dims &d, const kivi_cache &c) {
   ea.q_len = c.q_len;
   ea.r_len = c.r_len;
   ea.status = c.status;
+  ea.tickets = c.tickets;
   ea.heads = d.heads;
   ea.R = d.residual;
   ea.cap = d.capacity;
@@ -1054,7 +1208,7 @@ EncodeArgs encode_args(const kivi_dims &d, const kivi_cache &c) {
 int launch_append(const kivi_dims &d, const kivi_cache &c, const void *k_new, const void *v_new,
                   void *stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(append_kernel, dim3(d.batch), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL(append_kernel, dim3(d.batch), dim3(kAppendThreads), 0, st,
                      static_cast<const half_t *>(k_new), static_cast<const half_t *>(v_new),
                      static_cast<half_t *>(c.k_res), static_cast<half_t *>(c.v_res), c.r_len,
                      c.status, d.heads, d.residual);
@@ -1068,9 +1222,15 @@ int launch_flush(const kivi_dims &d, const kivi_cache &c, void *stream) {
   ea.src_v = ea.v_res;
   ea.src_tokens = d.residual;
   ea.prefill = 0;
-  int rc = launch_encode(d.bits, d.group, ea, dim3(d.residual / d.group, d.heads, d.batch), st);
-  if (rc) return rc;
-  hipLaunchKernelGGL(flush_commit_kernel, dim3(1), dim3(kThreads), 0, st, ea, d.batch, d.group);
+  const dim3 grid(d.heads, d.batch);
+  const int G = d.group;
+  if (d.bits == 2 && G == 32) hipLaunchKernelGGL((flush_kernel<2, 32>), grid, dim3(kFlushThreads), 0, st, ea);
+  else if (d.bits == 2 && G == 64) hipLaunchKernelGGL((flush_kernel<2, 64>), grid, dim3(kFlushThreads), 0, st, ea);
+  else if (d.bits == 2 && G == 128) hipLaunchKernelGGL((flush_kernel<2, 128>), grid, dim3(kFlushThreads), 0, st, ea);
+  else if (d.bits == 4 && G == 32) hipLaunchKernelGGL((flush_kernel<4, 32>), grid, dim3(kFlushThreads), 0, st, ea);
+  else if (d.bits == 4 && G == 64) hipLaunchKernelGGL((flush_kernel<4, 64>), grid, dim3(kFlushThreads), 0, st, ea);
+  else if (d.bits == 4 && G == 128) hipLaunchKernelGGL((flush_kernel<4, 128>), grid, dim3(kFlushThreads), 0, st, ea);
+  else return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
 

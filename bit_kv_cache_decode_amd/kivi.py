@@ -34,7 +34,7 @@ class Dims(ctypes.Structure):
 class CacheStruct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res",
-                 "q_len", "r_len", "status")]
+                 "q_len", "r_len", "status", "tickets")]
 
 
 class KiviError(RuntimeError):
@@ -136,6 +136,7 @@ class KiviCache:
         self.q_len = torch.zeros((batch,), dtype=i32, device=dev)
         self.r_len = torch.zeros((batch,), dtype=i32, device=dev)
         self.status = torch.zeros((1,), dtype=i32, device=dev)
+        self.tickets = torch.zeros((batch,), dtype=i32, device=dev)
         self.workspace = None
         self._struct = None
 

@@ -86,6 +86,9 @@ typedef struct {
  *   q_len  int32 [batch]  quantized tokens held (multiple of G, <= capacity)
  *   r_len  int32 [batch]  window tokens held, 0 <= r_len <= R
  *   status uint32 [1]     sticky KIVI_ST_* bits (caller clears it).
+ *   tickets uint32 [batch] per-sequence counters of kivi_flush_residual;
+ *                          zero-filled before first use, left zero-filled
+ *                          by every call.
  * Sequence b's context is its q_len[b] quantized tokens followed by its
  * r_len[b] window tokens, oldest first.
  *
@@ -103,6 +106,7 @@ typedef struct {
   void *k_res, *v_res;
   int32_t *q_len, *r_len;
   uint32_t *status;
+  uint32_t *tickets;
 } kivi_cache;
 
 /* Host-only check of dims; KIVI_OK, KIVI_EINVAL or KIVI_EUNSUPPORTED. */
@@ -127,7 +131,8 @@ int kivi_append_kv(const kivi_dims *dims, const kivi_cache *cache,
  * quantized token slots [q_len[b], q_len[b] + R); then q_len[b] += R and
  * r_len[b] = 0.  Sequences with r_len[b] < R are untouched.  If
  * q_len[b] + R > capacity the sequence is untouched and KIVI_ST_CAPACITY is
- * set.  Implemented as two kernels (quantize, then commit) on the stream.
+ * set.  One kernel: the workgroup that finishes reading sequence b's
+ * lengths last updates them (through cache->tickets).
  */
 int kivi_flush_residual(const kivi_dims *dims, const kivi_cache *cache,
                         void *stream);

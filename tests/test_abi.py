@@ -73,7 +73,7 @@ def test_entry_points_reject_bad_arguments_without_a_device():
     L = kivi.lib()
     d = kivi.make_dims(2, 2, 128, 2, 32, 32, 256)
     fake = ctypes.c_void_p(0x1000)
-    cs = kivi.CacheStruct(*([0x1000] * 11))
+    cs = kivi.CacheStruct(*([0x1000] * len(kivi.CacheStruct._fields_)))
     null_cache = kivi.CacheStruct()
     bad = kivi.make_dims(2, 2, 128, 3, 32, 32, 256)
     assert L.kivi_append_kv(ctypes.byref(bad), ctypes.byref(cs), fake, fake, None) == kivi.KIVI_EINVAL

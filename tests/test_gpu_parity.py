@@ -96,6 +96,29 @@ def test_llama2_13b_flush_of_full_window():
             assert np.array_equal(vs[b, h, 60:64].view(np.uint16), enc["v_scale"].view(np.uint16))
             assert np.array_equal(vz[b, h, 60:64].view(np.uint16), enc["v_zero"].view(np.uint16))
     assert c.status_bits() == 0
+    assert not c.tickets.any()
+
+
+def test_flush_only_full_windows_and_twice_in_a_row():
+    """A batch where some windows are full: only those are flushed (lengths
+    and codes), a second flush changes nothing, the tickets end at zero."""
+    w = workload(3, batch=4)
+    ql = np.array([1920, 1920, 1888, 1920], np.int32)
+    rl = np.array([128, 5, 128, 0], np.int32)
+    c = gpu_cache(w, q_len=ql, r_len=rl)
+    before = c.k_codes.cpu().numpy().copy()
+    for _ in range(2):
+        kivi.flush_residual(c)
+        torch.cuda.synchronize()
+        assert c.q_len.cpu().tolist() == [2048, 1920, 2016, 1920]
+        assert c.r_len.cpu().tolist() == [0, 5, 0, 0]
+        assert not c.tickets.any() and c.status_bits() == 0
+    after = c.k_codes.cpu().numpy()
+    assert np.array_equal(after[1], before[1]) and np.array_equal(after[3], before[3])
+    for b, h in [(0, 0), (0, 39), (2, 7)]:
+        t0 = int(ql[b])
+        enc = ocache.encode_tokens(w.k[b, h, t0:t0 + 128], w.v[b, h, t0:t0 + 128], 32, 2)
+        assert np.array_equal(after[b, h, t0 // 32:t0 // 32 + 4].view(np.uint32), enc["k_codes"])
 
 
 def test_ragged_serving_sampled_heads():
@@ -138,7 +161,7 @@ def test_streaming_appends_and_flushes_match_prefill():
     kivi.prefill(b, kt, vt, torch.tensor([n], dtype=torch.int32, device="cuda"),
                  torch.tensor([n % 32], dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
-    assert s.q_len.item() == 192 and s.r_len.item() == 8
+    assert s.q_len.item() == 192 and s.r_len.item() == 8 and not s.tickets.any()
     for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
         g = getattr(s, name).cpu().numpy()
         assert np.array_equal(g, getattr(b, name).cpu().numpy()), name
