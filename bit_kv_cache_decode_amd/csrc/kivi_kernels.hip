@@ -492,18 +492,21 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
 
 // ----------------------------------------------------------------- decode
 //
-// Grid (splits, heads, batch), 256 threads = 4 waves.  The 4 * splits waves
-// of one (sequence, head) share its work evenly: quantized sub-chunks of 64
-// (B=2) or 32 (B=4) tokens are dealt round-robin to the waves, and each wave
-// also takes an equal slice of the fp16 window tokens.  Every wave works on
-// its own (no block barrier until the end), and every lane keeps its own
+// Grid (splits, heads, batch), kDecodeWaves (8) waves per workgroup, one
+// workgroup per compute unit, two waves per SIMD.  The 8 * splits waves of
+// one (sequence, head) share its work: quantized sub-chunks of 64 (B=2) or
+// 32 (B=4) tokens are dealt round-robin to the waves, and each wave also
+// takes an equal slice of the fp16 window tokens, computed last.  Every
+// wave works on its own (no block barrier until the end), keeps
+// kDecodeDepth sub-chunks of loads in flight, and raises its issue priority
+// while it is behind the other wave of its SIMD; every lane keeps its own
 // online-softmax state (running max, sum, value sums) for the tokens it
-// sees; window tokens use the same lane layout and state as codes.  At the
-// end the lanes and waves of the workgroup are combined in LDS into one
-// partial state (max m, sum l, unnormalised value sums) in log2 units,
-// published to the workspace; the workgroup that takes the last ticket of
-// its (sequence, head) merges all partials by log-sum-exp rescaling and
-// writes the output.
+// sees.  At the end the lanes and waves of the workgroup are combined in
+// LDS (max m, sum l, unnormalised value sums, in log2 units).  With one
+// workgroup per (sequence, head) that is the output; otherwise each
+// workgroup publishes its partial state to the workspace and the one that
+// takes the last ticket of its (sequence, head) merges all partials by
+// log-sum-exp rescaling and writes the output.
 //
 // Dequantization is folded into the dot products:
 //   score_t = sum_d q'_d * K_hat[t,d]

@@ -275,3 +275,64 @@ def test_byte_model_matches_buffers():
     k_codes = 224 * 128 * 2 // 8
     assert per_head == 2 * k_codes + 7 * 128 * 4 + 224 * 4 * 4 + 2 * 32 * 256 + 256 + 512
     assert c.nbytes() >= per_head - 768
+
+
+def _near_tie_values(bits, rng, pairs=200):
+    """(mn, mx, xs) triples of fp16 values for which (x - mn) / s (s the fp16
+    step of a group with minimum mn and maximum mx, fp32 arithmetic) is a
+    half-integer or within 2^-15 of one: exact ties, and quotients near the
+    rounding boundaries where a reciprocal-based shortcut could round the
+    other way.  Negative minima give x - mn many significant bits."""
+    levels = np.float32((1 << bits) - 1)
+    f16 = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
+    f16 = np.concatenate([-f16[1:], f16])
+    out = []
+    for _ in range(pairs):
+        mn = np.float16(-rng.uniform(0.5, 60.0))
+        mx = np.float16(rng.uniform(0.5, 60.0))
+        s = np.float32(np.float16((np.float32(mx) - np.float32(mn)) / levels))
+        xs = f16[(f16 >= mn) & (f16 <= mx)]
+        q = (xs.astype(np.float32) - np.float32(mn)) / s
+        frac = np.abs(np.abs(q - np.rint(q)) - np.float32(0.5))
+        near = xs[frac < 2.0 ** -15]
+        if len(near):
+            out.append((mn, mx, near))
+    return out
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantizer_near_ties_bit_exact_on_both_encoders(bits):
+    """Keys and values built from exact and near rounding ties: the prefill
+    encoder and the flush kernel both match the oracle bit for bit."""
+    rng = np.random.default_rng(77 + bits)
+    cases = _near_tie_values(bits, rng)
+    assert sum(len(c[2]) for c in cases) > 300
+    G, R, D, H = 32, 128, 128, 2
+    k = np.zeros((1, H, R, D), np.float16)
+    v = np.zeros((1, H, R, D), np.float16)
+    for h in range(H):
+        for g in range(R // G):
+            for c in range(D):           # key group: channel c over tokens g*G .. g*G+G-1
+                mn, mx, near = cases[rng.integers(len(cases))]
+                col = np.concatenate([[mn, mx], rng.choice(near, size=G - 2)]).astype(np.float16)
+                k[0, h, g * G:(g + 1) * G, c] = rng.permutation(col)
+        for t in range(R):
+            for j in range(D // G):      # value group: token t, channels j*G .. j*G+G-1
+                mn, mx, near = cases[rng.integers(len(cases))]
+                row = np.concatenate([[mn, mx], rng.choice(near, size=G - 2)]).astype(np.float16)
+                v[0, h, t, j * G:(j + 1) * G] = rng.permutation(row)
+    kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    lens = torch.tensor([R], dtype=torch.int32, device="cuda")
+    pre = kivi.KiviCache(1, H, D, bits, G, R, 256)
+    kivi.prefill(pre, kt, vt, lens, torch.tensor([0], dtype=torch.int32, device="cuda"))
+    fl = kivi.KiviCache(1, H, D, bits, G, R, 256)
+    kivi.prefill(fl, kt, vt, lens, torch.tensor([R], dtype=torch.int32, device="cuda"))
+    kivi.flush_residual(fl)
+    torch.cuda.synchronize()
+    assert pre.q_len.item() == R and fl.q_len.item() == R and fl.r_len.item() == 0
+    for h in range(H):
+        enc = ocache.encode_tokens(k[0, h], v[0, h], G, bits)
+        for c in (pre, fl):
+            for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+                got = getattr(c, name)[0, h, :R // G].cpu().numpy()
+                assert np.array_equal(got.view(np.uint8), enc[name].view(np.uint8)), name
