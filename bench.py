@@ -13,9 +13,9 @@ another step left in the 256 MB Infinity Cache.  The K timed steps are
 captured in one HIP graph and replayed once between two synchronisations
 (throughput); the same K steps are then launched eagerly from the same
 starting state, one phase at a time (all appends, all decodes, all
-flushes) with HIP events on the launch stream around each phase, which give
-the per-kernel average GPU durations (the decode kernel's feeds the
-roofline).  The CPU oracle is timed beside it on a
+flushes), each phase a HIP graph replayed between HIP events on the launch
+stream, which give the per-kernel average GPU durations (the decode
+kernel's feeds the roofline).  The CPU oracle is timed beside it on a
 bounded sample of (sequence, head) steps.
 
 Prints one JSON line on stdout; diagnostics go to stderr.
@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "decode-attn query-heads/sec over 2-bit KV; achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+COPY_BUDGET_BYTES = 48e9
 KERNEL_SRC = os.path.join(ROOT, "bit_kv_cache_decode_amd", "csrc", "kivi_kernels.hip")
 
 
@@ -76,6 +77,30 @@ def measured_traffic(workload_name):
     return t.get("bytes_per_launch")
 
 
+def step_tokens(w):
+    """Starting window sizes and the token every step appends.  Where every
+    sequence's window holds at least one token, the cache starts one token
+    short (r_len - 1 window tokens) and the step appends that last token, so
+    after the append the cache holds exactly the workload's tokens.  Otherwise
+    (empty windows in the ragged workload) the cache starts with the
+    workload's tokens and the step appends one more, drawn N(0, 1) from seed
+    2000 + workload number; then every window must have room for it."""
+    import numpy as np
+    cfg = w.config
+    if np.all(w.r_len >= 1):
+        last = w.lengths - 1
+        b = np.arange(cfg.batch)
+        return (w.r_len - 1).astype(np.int32), np.ascontiguousarray(w.k[b, :, last]), \
+            np.ascontiguousarray(w.v[b, :, last])
+    if np.any(w.r_len >= cfg.residual):
+        raise SystemExit("a full window cannot take the appended token")
+    rng = np.random.Generator(np.random.PCG64(2000 + cfg.number))
+    shape = (cfg.batch, cfg.heads, cfg.head_dim)
+    k_new = rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+    v_new = rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+    return w.r_len.astype(np.int32), k_new, v_new
+
+
 def cpu_baseline(w, budget_s):
     """Time the CPU oracle on whole steps (append, decode, flush) of single
     (sequence, head) pairs of the same workload, cycling over the pairs until
@@ -88,22 +113,23 @@ def cpu_baseline(w, budget_s):
 
     cfg = w.config
     G, B, R = cfg.group, w.bits, cfg.residual
+    r_start, k_new, v_new = step_tokens(w)
     pairs = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
     states = {}
     done, spent = 0, 0.0
     with threadpool_limits(limits=1):
         while spent < budget_s:
             b, h = pairs[done % len(pairs)]
-            ql, rl = int(w.q_len[b]), int(w.r_len[b])
+            ql, r0 = int(w.q_len[b]), int(r_start[b])
             if (b, h) not in states:
-                states[(b, h)] = ocache.head_state(w.k[b, h], w.v[b, h], ql, rl - 1, G, B,
+                states[(b, h)] = ocache.head_state(w.k[b, h], w.v[b, h], ql, r0, G, B,
                                                    cfg.capacity, R)
             st = {k: (v.copy() if isinstance(v, np.ndarray) else v)
                   for k, v in states[(b, h)].items()}
             t0 = time.perf_counter()
-            st["k_res"][rl - 1] = w.k[b, h, ql + rl - 1]          # append
-            st["v_res"][rl - 1] = w.v[b, h, ql + rl - 1]
-            st["r_len"] = rl
+            st["k_res"][r0] = k_new[b, h]                         # append
+            st["v_res"][r0] = v_new[b, h]
+            st["r_len"] = rl = r0 + 1
             ocache.decode_head(w.q[b, h], st, cfg.sm_scale, G, B)  # decode
             if rl == R:                                           # flush
                 enc = ocache.encode_tokens(st["k_res"], st["v_res"], G, B)
@@ -136,28 +162,33 @@ def main():
     torch.cuda.set_device(0)
     w = wl.generate(args.workload, bits=args.bits)
     cfg = w.config
-    if np.any(w.r_len < 1):
-        raise SystemExit("the step appends into the window: every sequence needs r_len >= 1")
     dims = w.dims()
     Bt, H, D = cfg.batch, cfg.heads, cfg.head_dim
     K, W = args.steps, args.warmup
+    r_start, k_new, v_new = step_tokens(w)
 
-    # ---- the starting state: q_len quantized + (r_len - 1) window tokens
+    # ---- the starting state: q_len quantized + r_start window tokens
     kt = torch.from_numpy(w.k).cuda()
     vt = torch.from_numpy(w.v).cuda()
     base = kivi.KiviCache(**dims)
     q0 = torch.from_numpy(w.q_len).cuda()
-    r0 = torch.from_numpy(w.r_len - 1).cuda()
+    r0 = torch.from_numpy(r_start).cuda()
     kivi.prefill(base, kt, vt, q0 + r0, r0)
-    last = torch.from_numpy(w.lengths - 1).cuda().long()
-    bidx = torch.arange(Bt, device="cuda")
-    k_new = kt[bidx, :, last].contiguous()   # [batch, heads, D]
-    v_new = vt[bidx, :, last].contiguous()
+    k_new = torch.from_numpy(k_new).cuda()   # [batch, heads, D]
+    v_new = torch.from_numpy(v_new).cuda()
     q = torch.from_numpy(w.q).cuda()
     del kt, vt
     torch.cuda.synchronize()
     assert base.status_bits() == 0
 
+    # every timed step runs on its own copy of the starting state; the number
+    # of copies (and so of timed steps) is capped by a memory budget
+    cache_bytes = base.nbytes()
+    max_copies = max(2, int(COPY_BUDGET_BYTES // cache_bytes))
+    if max(K, W) > max_copies:
+        log(f"{max(K, W)} steps need {max(K, W)} cache copies of {cache_bytes / 1e9:.2f} GB; "
+            f"timing {min(K, max_copies)} steps, warming up {min(W, max_copies)}")
+        K, W = min(K, max_copies), min(W, max_copies)
     n_copies = max(K, W)
     copies = [base]
     for _ in range(n_copies - 1):
@@ -167,7 +198,6 @@ def main():
         copies.append(c)
     outs = [torch.empty((Bt, H, D), dtype=torch.float32, device="cuda") for _ in range(n_copies)]
     ws = kivi.new_workspace(base.dims)
-    cache_bytes = base.nbytes()
     log(f"workload {cfg.name}: {n_copies} cache copies of {cache_bytes / 1e6:.1f} MB")
 
     def reset():
@@ -208,24 +238,38 @@ def main():
         reset()
         torch.cuda.synchronize()
 
-    # ---- timed region 2: the same K steps launched eagerly, one phase at a
-    # time (the K appends, then the K decodes, then the K flushes; every copy
-    # is independent, so the results are those of K whole steps), with HIP
-    # events on the launch stream around each phase: each kernel's average
-    # duration is its phase time over K, free of host-side launch latency.
+    # ---- timed region 2: the same K steps one phase at a time (the K
+    # appends, then the K decodes, then the K flushes; every copy is
+    # independent, so the results are those of K whole steps), each phase a
+    # HIP graph replayed once between HIP events on the launch stream: each
+    # kernel's average duration is its phase time over K, with no host-side
+    # launch cost in it (eager launches with --eager).
+    phases = [
+        lambda i: kivi.append_kv(copies[i], k_new, v_new),
+        lambda i: kivi.decode_attn(copies[i], q, cfg.sm_scale, out=outs[i], workspace=ws),
+        lambda i: kivi.flush_residual(copies[i]),
+    ]
+    pgraphs = []
+    if not args.eager:
+        for fn in phases:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(K):
+                    fn(i)
+            pgraphs.append(g)
+        torch.cuda.synchronize()
+        reset()
+        torch.cuda.synchronize()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     evs[0].record()
-    for i in range(K):
-        kivi.append_kv(copies[i], k_new, v_new)
-    evs[1].record()
-    for i in range(K):
-        kivi.decode_attn(copies[i], q, cfg.sm_scale, out=outs[i], workspace=ws)
-    evs[2].record()
-    for i in range(K):
-        kivi.flush_residual(copies[i])
-    evs[3].record()
+    for p_i, fn in enumerate(phases):
+        if pgraphs:
+            pgraphs[p_i].replay()
+        else:
+            for i in range(K):
+                fn(i)
+        evs[p_i + 1].record()
     torch.cuda.synchronize()
     eager_wall = time.perf_counter() - t0
     if graph is None:
@@ -244,7 +288,7 @@ def main():
 
     step_s = wall / K
     qheads = Bt * H
-    dec_bytes = wl.decode_bytes(w.q_len, w.r_len, H, D, w.bits, cfg.group)
+    dec_bytes = wl.decode_bytes(w.q_len, r_start + 1, H, D, w.bits, cfg.group)
     achieved = dec_bytes / (decode_us * 1e-6) / 1e9
     result = {
         "metric": METRIC,
@@ -263,14 +307,14 @@ def main():
             "workload": f"{cfg.name}: {cfg.description}",
             "batch": Bt, "heads": H, "head_dim": D, "bits": w.bits, "group": cfg.group,
             "residual": cfg.residual,
-            "context": int(w.lengths.max()), "quantized_tokens": int(w.q_len.max()),
-            "window_tokens": int(w.r_len.max()),
+            "context": int((w.q_len + r_start + 1).max()),
+            "quantized_tokens": int(w.q_len.max()), "window_tokens": int((r_start + 1).max()),
             "step": "append + decode + flush, one HIP graph of all timed steps"
                     if graph is not None else "append + decode + flush, eager launches",
         },
         "decode": {"us": decode_us, "query_heads_per_s": qheads / (decode_us * 1e-6),
                    "algorithmic_bytes": int(dec_bytes), "GBps": achieved},
-        "eager_ms_per_step": eager_wall / K * 1e3,
+        "phased_ms_per_step": eager_wall / K * 1e3,
         "append_us": append_us,
         "flush_us": flush_us,
         "graph_replay_matches_eager": replay_ok,
