@@ -3,7 +3,8 @@
 
 One step = the whole hot path for one batch: append the new token of every
 (sequence, head) to the fp16 window, decode attention over the full context,
-flush the now-full window into 2-bit codes.  Default workload: the
+flush the now-full window into 2-bit codes -- one kivi_decode_step call (a
+single kernel when one workgroup covers a whole (sequence, head)).  Default workload: the
 Llama-2-7B-shaped layer (batch 8, 32 heads, head_dim 128, 3968 quantized +
 128 window tokens at decode time, B=2, G=32, R=128), synthetic seeded data.
 
@@ -12,10 +13,11 @@ starting state (3968 quantized + 127 window tokens), so no step re-reads data
 another step left in the 256 MB Infinity Cache.  The K timed steps are
 captured in one HIP graph and replayed once between two synchronisations
 (throughput); the same K steps are then launched eagerly from the same
-starting state, one phase at a time (all appends, all decodes, all
-flushes), each phase a HIP graph replayed between HIP events on the launch
-stream, which give the per-kernel average GPU durations (the decode
-kernel's feeds the roofline).  The CPU oracle is timed beside it on a
+starting state as separate calls, one phase at a time (all appends, all
+decodes, all flushes), each phase a HIP graph replayed between HIP events on
+the launch stream, which give the per-kernel average GPU durations of the
+three separate kernels (the decode kernel's feeds the roofline); their
+outputs must equal the whole-step kernel's bit for bit.  The CPU oracle is timed beside it on a
 bounded sample of (sequence, head) steps.
 
 Prints one JSON line on stdout; diagnostics go to stderr.
@@ -206,10 +208,9 @@ def main():
             c.r_len.copy_(r0)
 
     def step(i):
-        c = copies[i]
-        kivi.append_kv(c, k_new, v_new)
-        kivi.decode_attn(c, q, cfg.sm_scale, out=outs[i], workspace=ws)
-        kivi.flush_residual(c)
+        # append + decode + flush: one kernel when one workgroup covers a
+        # whole (sequence, head), else the three kernels
+        kivi.decode_step(copies[i], k_new, v_new, q, cfg.sm_scale, out=outs[i], workspace=ws)
 
     # ---- warmup (eager), then back to the starting state
     for i in range(W):
@@ -309,8 +310,10 @@ def main():
             "residual": cfg.residual,
             "context": int((w.q_len + r_start + 1).max()),
             "quantized_tokens": int(w.q_len.max()), "window_tokens": int((r_start + 1).max()),
-            "step": "append + decode + flush, one HIP graph of all timed steps"
-                    if graph is not None else "append + decode + flush, eager launches",
+            "step": ("kivi_decode_step (append + decode + flush, "
+                     + ("one kernel" if kivi.decode_splits(base.dims) == 1 else "three kernels")
+                     + "), " + ("one HIP graph of all timed steps" if graph is not None
+                                else "eager launches")),
         },
         "decode": {"us": decode_us, "query_heads_per_s": qheads / (decode_us * 1e-6),
                    "algorithmic_bytes": int(dec_bytes), "GBps": achieved},

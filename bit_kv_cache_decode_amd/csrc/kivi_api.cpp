@@ -73,7 +73,7 @@ DecodePlan decode_plan(const kivi_dims &d) {
   p.part_floats = 4 + (size_t)d.head_dim;
   const size_t parts = (size_t)bh * p.splits * p.part_floats * sizeof(float);
   p.counters_off = round_up(parts, 256);
-  p.bytes = p.counters_off + round_up((size_t)bh * sizeof(uint32_t), 256);
+  p.bytes = p.counters_off + (size_t)bh * kTicketStride * sizeof(uint32_t);
   return p;
 }
 
@@ -138,6 +138,20 @@ int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache, const void 
   const kivi::DecodePlan p = kivi::decode_plan(*dims);
   if (workspace_bytes < p.bytes) return KIVI_ENOSPC;
   return kivi::hip_rc(kivi::launch_decode(*dims, *cache, p, q, out, sm_scale, workspace, stream));
+}
+
+int kivi_decode_step(const kivi_dims *dims, const kivi_cache *cache, const void *k_new,
+                     const void *v_new, const void *q, float *out, float sm_scale,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache) || !k_new || !v_new || !q || !out || !workspace) return KIVI_EINVAL;
+  if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
+    return KIVI_EINVAL;
+  const kivi::DecodePlan p = kivi::decode_plan(*dims);
+  if (workspace_bytes < p.bytes) return KIVI_ENOSPC;
+  return kivi::hip_rc(kivi::launch_decode_step(*dims, *cache, p, k_new, v_new, q, out, sm_scale,
+                                               workspace, stream));
 }
 
 const char *kivi_strerror(int code) {

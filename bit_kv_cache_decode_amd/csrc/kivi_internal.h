@@ -19,6 +19,10 @@ namespace kivi {
 #define KIVI_DECODE_WG_PER_CU 1
 #endif
 constexpr int kDecodeWavesPerWorkgroup = KIVI_DECODE_WAVES;
+// Ticket counters (workspace and cache) sit 256 bytes apart: device-scope
+// atomics on one cache line are serialized, so counters that many
+// workgroups hit at once must not share a line.
+constexpr int kTicketStride = 64;
 constexpr int kDecodeWorkgroupsPerCU = KIVI_DECODE_WG_PER_CU;
 
 // Decode work split.  Each (sequence, head) gets `splits` workgroups of
@@ -48,5 +52,8 @@ int launch_prefill(const kivi_dims &d, const kivi_cache &c, const void *k,
 int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
                   const void *q, float *out, float sm_scale, void *workspace,
                   void *stream);
+int launch_decode_step(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
+                       const void *k_new, const void *v_new, const void *q, float *out,
+                       float sm_scale, void *workspace, void *stream);
 
 }  // namespace kivi

@@ -66,6 +66,36 @@ __device__ __forceinline__ float lane_group_sum(float v) {
   return v;
 }
 
+// Packed fp16 maximum / minimum of two half2 words (v_pk_max_f16 / v_pk_min_f16).
+__device__ __forceinline__ uint32_t pk_max16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(half2_t, a),
+                                                                __builtin_bit_cast(half2_t, b)));
+}
+
+__device__ __forceinline__ uint32_t pk_min16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(half2_t, a),
+                                                                __builtin_bit_cast(half2_t, b)));
+}
+
+__device__ __forceinline__ uint32_t neg16x2(uint32_t v) { return v ^ 0x80008000u; }
+__device__ __forceinline__ uint32_t swap16(uint32_t v) { return (v >> 16) | (v << 16); }
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Packed fp16 maximum over aligned groups of N consecutive lanes (as
+// lane_group_sum).
+template <int N>
+__device__ __forceinline__ uint32_t lane_group_pkmax(uint32_t v) {
+  v = pk_max16(v, dppu<0xB1>(v));
+  if constexpr (N >= 4) v = pk_max16(v, dppu<0x4E>(v));
+  if constexpr (N >= 8) v = pk_max16(v, dppu<0x141>(v));
+  if constexpr (N >= 16) v = pk_max16(v, dppu<0x140>(v));
+  return v;
+}
+
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -133,24 +163,41 @@ __device__ __forceinline__ GroupParams group_params(float mn_raw, float mx_raw, 
   return g;
 }
 
-// clamp(rint((x - mn) / s), 0, top) with an IEEE division, computed as
-// rint((x - mn) * rs) except where that product lies within 2^-16 of a
-// half-integer.  Why that is the same value: the quotient q = (x - mn) / s
-// is below 32 (x - mn is at most the group's range and s is at least half
-// the range over the levels, B <= 4), and the product differs from q by at
-// most q * 2^-22 < 2^-17 (one rounding of the product, a reciprocal within
-// one ulp).  Away from the half-integers by more than that, the product, q
-// and q rounded to fp32 (which cannot cross an fp32-representable
-// half-integer) all round to the same integer.  Near them, the division is
-// done.
-__device__ __forceinline__ uint32_t encode_one(float x, float mn, float s, float rs, float top) {
-  if (s == 0.0f) return 0u;
-  const float d = x - mn;
-  const float q = d * rs;
-  float c = rintf(q);
-  if (fabsf(fabsf(q - c) - 0.5f) < 0x1p-16f) c = rintf(d / s);
-  c = fminf(fmaxf(c, 0.0f), top);
-  return (uint32_t)c;
+// Codes are clamp(rint((x - mn) / s), 0, top) with an IEEE division.  They
+// are computed as rint((x - mn) * rs) (rs = 1 / s within one ulp, 0 when
+// s == 0, which gives code 0 as required), except where that product lies
+// within 2^-16 of a half-integer: there the division decides.  Why that is
+// the same value: the quotient q = (x - mn) / s is below 32 (x - mn is at
+// most the group's range and s is at least half the range over the levels,
+// B <= 4), and the product differs from q by at most q * 2^-22 < 2^-17 (one
+// rounding of the product, a reciprocal within one ulp).  Away from the
+// half-integers by more than that, the product, q and q rounded to fp32
+// (which cannot cross an fp32-representable half-integer) all round to the
+// same integer.  code_fast keeps the largest |q - rint(q)| of a word in
+// dmax (exact: q >= 0, and q - rint(q) is exact by Sterbenz's lemma, so it
+// is at most 0.5); a word with dmax > kNearHalf had a product within 2^-16
+// of a half-integer, and its caller recomputes it with code_exact
+// (x - mn >= 0, so no clamp at 0 is needed).
+constexpr float kNearHalf = 0.5f - 0x1p-16f;
+
+__device__ __forceinline__ float code_fast(float x, float mn, float rs, float &dmax) {
+  const float q = (x - mn) * rs;
+  const float c = rintf(q);
+  dmax = fmaxf(dmax, fabsf(q - c));
+  return c;
+}
+
+__device__ __forceinline__ float code_exact(float x, float mn, float s) {
+  return s == 0.0f ? 0.0f : rintf((x - mn) / s);
+}
+
+// Pack CPW codes (as floats, each at most top after the clamp) into one word.
+template <int BITS, int CPW>
+__device__ __forceinline__ uint32_t pack_codes(const float (&c)[CPW], float top) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) w |= (uint32_t)fminf(c[i], top) << (i * BITS);
+  return w;
 }
 
 #pragma clang fp contract(on)
@@ -275,158 +322,201 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
 
   for (int wi = tid; wi < W * G; wi += kThreads) {
     const int w = wi / G, t = wi % G;
-    uint32_t kw = 0, vw = 0;
     const int gi = ((w * CPW) / G) * G + t;
     const float vm = vmn[gi], vs = vst[gi], vr = vrs[gi];
+    float ck[CPW], cv[CPW];
+    float dmax = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int c = w * CPW + i;
-      kw |= encode_one((float)xk[t][c], kmn[c], kst[c], krs[c], kTop) << (i * BITS);
-      vw |= encode_one((float)xv[t][c], vm, vs, vr, kTop) << (i * BITS);
+      ck[i] = code_fast((float)xk[t][c], kmn[c], krs[c], dmax);
+      cv[i] = code_fast((float)xv[t][c], vm, vr, dmax);
     }
-    a.k_codes[ktile * (W * G) + wi] = kw;
-    a.v_codes[ktile * (W * G) + wi] = vw;
+    if (dmax > kNearHalf) {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const int c = w * CPW + i;
+        ck[i] = code_exact((float)xk[t][c], kmn[c], kst[c]);
+        cv[i] = code_exact((float)xv[t][c], vm, vs);
+      }
+    }
+    a.k_codes[ktile * (W * G) + wi] = pack_codes<BITS, CPW>(ck, kTop);
+    a.v_codes[ktile * (W * G) + wi] = pack_codes<BITS, CPW>(cv, kTop);
   }
 }
 
-// Flush: one workgroup of 1024 threads per (sequence, head) quantizes its
-// full window in blocks of up to 128 tokens (all of a block's loads are
-// issued before the first is used).  Each workgroup takes one of sequence
-// b's tickets once it has read b's lengths; the workgroup that took the
-// last one (every head has read the lengths by then, and none reads them
-// again) sets q_len[b] += R, r_len[b] = 0 and clears the ticket when it is
-// done.
-constexpr int kFlushThreads = 1024;
+// Quantize window tokens [blk0, blk1) of one (sequence, head) into
+// quantized slots from ql + blk0 on.  The loads of a block of TB tokens (a
+// multiple of G) are all issued up front, tile by tile; each tile of G
+// tokens is then staged in LDS as soon as its own loads have arrived, its
+// key groups (two channels per item) and value groups are computed, then its
+// code words, while the later tiles' loads are still in flight.  Token rnew
+// of the window is taken from knew / vnew (one fp16 row each) instead of the
+// cache when those are given: the token an append in the same kernel has
+// just written.  NTHREADS threads take part.
+template <int G, int TB>
+struct FlushSmem {
+  static constexpr int NB = TB / G >= 2 ? 2 : 1;  // tile buffers
+  half_t x[NB][2][G][kD + 8];                     // [buffer][key, value][token][channel]
+  float4 kp[NB][kD], vp[NB][kD];                  // {minimum, step, 1 / step, -}
+};
+
+template <int BITS, int G, int TB, int NTHREADS>
+__device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int ql, int tid,
+                                             FlushSmem<G, TB> &fs, int rnew, const uint4 *knew,
+                                             const uint4 *vnew, int blk0, int blk1) {
+  constexpr int W = kD * BITS / 32, CPW = 32 / BITS;
+  constexpr float kTop = (float)((1 << BITS) - 1);
+  constexpr int NTB = TB / G;                           // tiles per block
+  constexpr int TE = G * (kD / 8);                      // uint4 per tile and operand
+  constexpr int PE = 2 * TE / NTHREADS;                 // uint4 per thread and tile
+  constexpr int NB = FlushSmem<G, TB>::NB;
+  static_assert(TB % G == 0 && PE >= 1 && PE * NTHREADS == 2 * TE, "whole tiles per pass");
+  const uint4 *src[2] = {reinterpret_cast<const uint4 *>(a.k_res + bh * a.R * kD),
+                         reinterpret_cast<const uint4 *>(a.v_res + bh * a.R * kD)};
+  const uint4 *fresh_row[2] = {knew, vnew};
+
+  for (int blk = blk0; blk < blk1; blk += TB) {
+    const int nt = min(TB, blk1 - blk) / G;  // tiles in this block
+    uint4 r[NTB][PE];
+#pragma unroll
+    for (int tl = 0; tl < NTB; ++tl) {
+#pragma unroll
+      for (int i = 0; i < PE; ++i) {
+        const int e = tid + i * NTHREADS, op = e / TE, f = e % TE;
+        const int t = blk + min(tl, nt - 1) * G + f / (kD / 8);  // clamped: unused past nt
+        r[tl][i] = src[op][(size_t)t * (kD / 8) + f % (kD / 8)];
+      }
+    }
+#pragma unroll
+    for (int tl = 0; tl < NTB; ++tl) {
+      if (tl >= nt) break;
+      const int bf = tl % NB;
+      const size_t tile = bh * (size_t)(a.cap / G) + (size_t)((ql + blk) / G) + tl;
+#pragma unroll
+      for (int i = 0; i < PE; ++i) {
+        const int e = tid + i * NTHREADS, op = e / TE, f = e % TE;
+        const int t = f / (kD / 8), c = f % (kD / 8);
+        const bool fresh = knew != nullptr && blk + tl * G + t == rnew;
+        *reinterpret_cast<uint4 *>(&fs.x[bf][op][t][c * 8]) = fresh ? fresh_row[op][c] : r[tl][i];
+      }
+      __syncthreads();
+      for (int gi = tid; gi < kD / 2 + kD; gi += NTHREADS) {
+        if (gi < kD / 2) {
+          // key groups: channels 2 * gi and 2 * gi + 1 over the tile's G tokens
+          const int c = 2 * gi;
+          float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
+#pragma unroll 8
+          for (int t = 0; t < G; ++t) {
+            const half2_t x2 = *reinterpret_cast<const half2_t *>(&fs.x[bf][0][t][c]);
+            const float x0 = (float)x2.x, x1 = (float)x2.y;
+            mn0 = fminf(mn0, x0);
+            mx0 = fmaxf(mx0, x0);
+            mn1 = fminf(mn1, x1);
+            mx1 = fmaxf(mx1, x1);
+          }
+          const GroupParams g0 = group_params(mn0, mx0, kTop), g1 = group_params(mn1, mx1, kTop);
+          *reinterpret_cast<half2_t *>(a.k_zero + tile * kD + c) = half2_t{g0.zero16, g1.zero16};
+          *reinterpret_cast<half2_t *>(a.k_scale + tile * kD + c) = half2_t{g0.scale16, g1.scale16};
+          fs.kp[bf][c] = make_float4(g0.mn, g0.s, g0.rs, 0.0f);
+          fs.kp[bf][c + 1] = make_float4(g1.mn, g1.s, g1.rs, 0.0f);
+        } else {
+          // value groups: group e / G, token e % G, in the tiled
+          // [tile][group][token] order of the value zero-points
+          const int e = gi - kD / 2, j = e / G, t = e % G;
+          float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+          for (int c = 0; c < G; c += 8) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(&fs.x[bf][1][t][j * G + c]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const half2_t x2 = __builtin_bit_cast(half2_t, u4_get(u, q));
+              mn = fminf(mn, fminf((float)x2.x, (float)x2.y));
+              mx = fmaxf(mx, fmaxf((float)x2.x, (float)x2.y));
+            }
+          }
+          const GroupParams g = group_params(mn, mx, kTop);
+          a.v_zero[tile * kD + e] = g.zero16;
+          a.v_scale[tile * kD + e] = g.scale16;
+          fs.vp[bf][e] = make_float4(g.mn, g.s, g.rs, 0.0f);
+        }
+      }
+      __syncthreads();
+      for (int wi = tid; wi < 2 * W * G; wi += NTHREADS) {
+        // key words first, then value words; word (w, t) holds channels
+        // w * CPW .. w * CPW + CPW - 1 of token t
+        const int op = wi / (W * G), w = (wi / G) % W, t = wi % G;
+        float x[CPW], cd[CPW];
+#pragma unroll
+        for (int i = 0; i < CPW; i += 8) {
+          const uint4 u = *reinterpret_cast<const uint4 *>(&fs.x[bf][op][t][w * CPW + i]);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const half2_t x2 = __builtin_bit_cast(half2_t, u4_get(u, q / 2));
+            x[i + q] = (q & 1) ? (float)x2.y : (float)x2.x;
+          }
+        }
+        float dmax = 0.0f;
+        if (op == 0) {
+#pragma unroll
+          for (int i = 0; i < CPW; ++i) {
+            const float4 kq = fs.kp[bf][w * CPW + i];
+            cd[i] = code_fast(x[i], kq.x, kq.z, dmax);
+          }
+          if (dmax > kNearHalf) {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+              const float4 kq = fs.kp[bf][w * CPW + i];
+              cd[i] = code_exact(x[i], kq.x, kq.y);
+            }
+          }
+          a.k_codes[tile * (W * G) + (wi % (W * G))] = pack_codes<BITS, CPW>(cd, kTop);
+        } else {
+          const float4 v = fs.vp[bf][((w * CPW) / G) * G + t];
+#pragma unroll
+          for (int i = 0; i < CPW; ++i) cd[i] = code_fast(x[i], v.x, v.z, dmax);
+          if (dmax > kNearHalf) {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) cd[i] = code_exact(x[i], v.x, v.y);
+          }
+          a.v_codes[tile * (W * G) + (wi % (W * G))] = pack_codes<BITS, CPW>(cd, kTop);
+        }
+      }
+      if (NB == 1) __syncthreads();  // a single buffer is rewritten by the next tile
+    }
+    __syncthreads();
+  }
+}
+
+// Flush: grid (R / G, heads, batch); one workgroup of 256 threads quantizes
+// one tile of G window tokens of one (sequence, head).  Each workgroup takes
+// one of sequence b's tickets once it has read b's lengths (the atomic's
+// latency hides behind the window loads); the workgroup that took the last
+// one (every tile of every head has read the lengths by then, and none reads
+// them again) sets q_len[b] += R, r_len[b] = 0 and clears the ticket when it
+// is done.
+constexpr int kFlushThreads = 256;
 
 template <int BITS, int G>
 __global__ __launch_bounds__(kFlushThreads) void flush_kernel(EncodeArgs a) {
-  constexpr int W = kD * BITS / 32, CPW = 32 / BITS;
-  constexpr float kTop = (float)((1 << BITS) - 1);
-  constexpr int TB = 128;                   // tokens per block
-  constexpr int NT = TB / G;                // tiles per full block
-  constexpr int PT = TB * (kD / 8) / kFlushThreads;  // uint4 per thread and operand
-  static_assert(NT * (kD / 2) <= kFlushThreads / 2 && NT * kD <= kFlushThreads / 2,
-                "key-group and value-group threads fit in the two halves of the workgroup");
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int ql = a.q_len[b], rl = a.r_len[b];
   if (!flush_ok(ql, rl, G, a.R, a.cap)) {
-    if (rl == a.R && h == 0 && tid == 0)
+    if (rl == a.R && tile == 0 && h == 0 && tid == 0)
       atomicOr(a.status, (ql < 0 || ql % G) ? KIVI_ST_BAD_LENGTH : KIVI_ST_CAPACITY);
     return;
   }
-  // The ticket is taken now (the lengths have been read: the branch above
-  // depends on them) and looked at only at the end, so its latency hides
-  // behind the window loads.
   uint32_t ticket = 0;
   if (tid == 0)
-    ticket = __hip_atomic_fetch_add(a.tickets + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-  __shared__ half_t xk[TB][kD + 8], xv[TB][kD + 8];
-  __shared__ float4 kp[NT * kD], vp[NT * kD];  // {minimum, step, 1 / step, -}
-  const size_t bh = (size_t)b * a.heads + h;
-  const uint4 *sk = reinterpret_cast<const uint4 *>(a.k_res + bh * a.R * kD);
-  const uint4 *sv = reinterpret_cast<const uint4 *>(a.v_res + bh * a.R * kD);
-
-  for (int blk = 0; blk < a.R; blk += TB) {
-    const int nt = min(TB, a.R - blk) / G;  // tiles in this block
-    const int ne = nt * G * (kD / 8);
-    const size_t tile0 = bh * (size_t)(a.cap / G) + (size_t)((ql + blk) / G);
-    {
-      uint4 rk[PT], rv[PT];
-#pragma unroll
-      for (int i = 0; i < PT; ++i) {  // clamped: a partial block's extra loads are unused
-        const int e = min(tid + i * kFlushThreads, ne - 1);
-        rk[i] = sk[(size_t)blk * (kD / 8) + e];
-        rv[i] = sv[(size_t)blk * (kD / 8) + e];
-      }
-#pragma unroll
-      for (int i = 0; i < PT; ++i) {
-        const int e = tid + i * kFlushThreads;
-        if (e < ne) {
-          const int t = e / (kD / 8), c = e % (kD / 8);
-          *reinterpret_cast<uint4 *>(&xk[t][c * 8]) = rk[i];
-          *reinterpret_cast<uint4 *>(&xv[t][c * 8]) = rv[i];
-        }
-      }
-    }
-    __syncthreads();
-    if (tid < kFlushThreads / 2) {
-      // key groups: tile tid / 64, channels 2 * (tid % 64) and the next one,
-      // each over the tile's G tokens
-      if (tid < nt * (kD / 2)) {
-        const int tl = tid / (kD / 2), c = 2 * (tid % (kD / 2));
-        float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
-#pragma unroll 8
-        for (int t = 0; t < G; ++t) {
-          const half2_t x2 = *reinterpret_cast<const half2_t *>(&xk[tl * G + t][c]);
-          const float x0 = (float)x2.x, x1 = (float)x2.y;
-          mn0 = fminf(mn0, x0);
-          mx0 = fmaxf(mx0, x0);
-          mn1 = fminf(mn1, x1);
-          mx1 = fmaxf(mx1, x1);
-        }
-        const GroupParams g0 = group_params(mn0, mx0, kTop), g1 = group_params(mn1, mx1, kTop);
-        const size_t o = tile0 * kD + (size_t)tl * kD + c;
-        *reinterpret_cast<half2_t *>(a.k_zero + o) = half2_t{g0.zero16, g1.zero16};
-        *reinterpret_cast<half2_t *>(a.k_scale + o) = half2_t{g0.scale16, g1.scale16};
-        kp[tl * kD + c] = make_float4(g0.mn, g0.s, g0.rs, 0.0f);
-        kp[tl * kD + c + 1] = make_float4(g1.mn, g1.s, g1.rs, 0.0f);
-      }
-    } else {
-      // value groups: tile e / 128, group (e % 128) / G, token (e % 128) % G,
-      // in the tiled [tile][group][token] order of the value zero-points
-      const int e = tid - kFlushThreads / 2;
-      if (e < nt * kD) {
-        const int tl = e / kD, j = (e % kD) / G, t = tl * G + (e % kD) % G;
-        float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-        for (int c = 0; c < G; c += 8) {
-          const uint4 u = *reinterpret_cast<const uint4 *>(&xv[t][j * G + c]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const half2_t x2 = __builtin_bit_cast(half2_t, u4_get(u, q));
-            mn = fminf(mn, fminf((float)x2.x, (float)x2.y));
-            mx = fmaxf(mx, fmaxf((float)x2.x, (float)x2.y));
-          }
-        }
-        const GroupParams g = group_params(mn, mx, kTop);
-        a.v_zero[tile0 * kD + e] = g.zero16;
-        a.v_scale[tile0 * kD + e] = g.scale16;
-        vp[e] = make_float4(g.mn, g.s, g.rs, 0.0f);
-      }
-    }
-    __syncthreads();
-    for (int wi = tid; wi < nt * W * G; wi += kFlushThreads) {
-      const int tl = wi / (W * G), w = (wi / G) % W, tt = wi % G, t = tl * G + tt;
-      const float4 v = vp[tl * kD + ((w * CPW) / G) * G + tt];
-      uint32_t kw = 0, vw = 0;
-#pragma unroll
-      for (int i = 0; i < CPW; i += 8) {
-        const uint4 uk = *reinterpret_cast<const uint4 *>(&xk[t][w * CPW + i]);
-        const uint4 uv = *reinterpret_cast<const uint4 *>(&xv[t][w * CPW + i]);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int c = w * CPW + i + q;
-          const half2_t k2 = __builtin_bit_cast(half2_t, u4_get(uk, q / 2));
-          const half2_t v2 = __builtin_bit_cast(half2_t, u4_get(uv, q / 2));
-          const float xk1 = (q & 1) ? (float)k2.y : (float)k2.x;
-          const float xv1 = (q & 1) ? (float)v2.y : (float)v2.x;
-          const float4 kq = kp[tl * kD + c];
-          kw |= encode_one(xk1, kq.x, kq.y, kq.z, kTop) << ((i + q) * BITS);
-          vw |= encode_one(xv1, v.x, v.y, v.z, kTop) << ((i + q) * BITS);
-        }
-      }
-      a.k_codes[tile0 * (W * G) + wi] = kw;
-      a.v_codes[tile0 * (W * G) + wi] = vw;
-    }
-    __syncthreads();
-  }
-
-  if (tid == 0 && ticket == (uint32_t)a.heads - 1) {
+    ticket = __hip_atomic_fetch_add(a.tickets + (size_t)b * kTicketStride, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+  __shared__ FlushSmem<G, G> fs;
+  flush_window<BITS, G, G, kFlushThreads>(a, (size_t)b * a.heads + h, ql, tid, fs, -1, nullptr,
+                                          nullptr, tile * G, tile * G + G);
+  if (tid == 0 && ticket == (uint32_t)(a.heads * (a.R / G)) - 1) {
     a.q_len[b] = ql + a.R;
     a.r_len[b] = 0;
-    a.tickets[b] = 0u;
+    a.tickets[(size_t)b * kTicketStride] = 0u;
   }
 }
 
@@ -530,6 +620,7 @@ struct DecodeArgs {
   const int32_t *q_len, *r_len;
   uint32_t *status;
   const half_t *q;
+  const half_t *k_new, *v_new;  // whole-step kernel only
   float *out, *part;
   uint32_t *tickets;
   float qscale;  // sm_scale * log2(e)
@@ -963,8 +1054,177 @@ __device__ __forceinline__ void window_step(const WinStep<BITS, G> &x, bool vali
   }
 }
 
+// ------------------------------------------ whole step: flush from registers
+// When the step's append fills the window and every wave holds all of its
+// window tokens in its prefetched registers (at most 16 per wave, R <= 128),
+// the flush quantizes them from those registers instead of reading the
+// window again.  Lane (slot, w) holds channels w * CPW .. w * CPW + CPW - 1
+// of one token per step: exactly one key code word and one value code word.
+//   values: a value group (one token, G channels) is G / CPW consecutive
+//   lanes, whose minimum and maximum meet by DPP.
+//   keys: a key group (one channel over the G tokens of a tile) is spread
+//   over the slots and steps of G / wpw waves.  Each lane reduces its own
+//   steps and stores (-minimum, maximum) of its channel pairs in LDS; after
+//   a barrier, one thread per (tile, channel) reduces those over the tile's
+//   waves and slots and computes the group's parameters, which every lane
+//   reads back for its CPW channels after a second barrier.
+// Minima travel negated, so that one packed fp16 maximum reduces both.
+constexpr int kMaxRegFlushTiles = 4;  // R <= 128, G >= 32
+
 template <int BITS, int G>
-__global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_kernel(DecodeArgs a) {
+struct RegFlushSmem {
+  uint32_t part[kDecodeWaves][DecCfg<BITS, G>::TQS][kD / 2][2];  // [wave][slot][pair]{-min, max}
+  float2 prm[kMaxRegFlushTiles][kD];                              // [tile][channel]{min, 1/step}
+  float step[kMaxRegFlushTiles][kD];
+};
+
+// LDS of the whole-step flush: the register path's, or the window-reading
+// path's for longer windows (never both in one launch).
+template <int BITS, int G>
+union FusedFlushSmem {
+  RegFlushSmem<BITS, G> reg;
+  FlushSmem<G, G> lds;
+};
+
+template <int BITS, int G>
+__device__ __forceinline__ FusedFlushSmem<BITS, G> &fused_flush_smem() {
+  __shared__ FusedFlushSmem<BITS, G> u;
+  return u;
+}
+
+// One code word from a lane's CPW fp16 channels; fast(i) gives channel i's
+// {minimum, 1 / step}, step(i) its step (only read for a word near a tie).
+template <int BITS, int NV, typename Fast, typename Step>
+__device__ __forceinline__ uint32_t encode_lane_word(const uint4 (&x)[NV], Fast fast, Step step) {
+  constexpr int CPW = 8 * NV;
+  constexpr float kTop = (float)((1 << BITS) - 1);
+  float xf[CPW], cd[CPW];
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const half2_t h = __builtin_bit_cast(half2_t, u4_get(x[v], e));
+      xf[8 * v + 2 * e] = (float)h.x;
+      xf[8 * v + 2 * e + 1] = (float)h.y;
+    }
+  float dmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const float2 p = fast(i);
+    cd[i] = code_fast(xf[i], p.x, p.y, dmax);
+  }
+  if (dmax > kNearHalf) {
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) cd[i] = code_exact(xf[i], fast(i).x, step(i));
+  }
+  return pack_codes<BITS, CPW>(cd, kTop);
+}
+
+// Before the barrier: the lane's key partials to LDS, and its value groups
+// and value code words (one per step).  tile0 is the window's first tile in
+// the cache; the wave's tokens [begin, begin + wsteps * STEP) lie in one tile.
+template <int BITS, int G>
+__device__ __forceinline__ void flush_regs_values(const EncodeArgs &ea, RegFlushSmem<BITS, G> &rf,
+                                                  const WinStep<BITS, G> (&x)[WinCfg<BITS, G>::PF],
+                                                  int wsteps, size_t tile0, int begin, int wv,
+                                                  int w, int slot) {
+  using C = DecCfg<BITS, G>;
+  using WC = WinCfg<BITS, G>;
+  constexpr int NV = WC::NV, HW = 4 * NV;  // half2 words per lane and operand
+  constexpr int LG = G / C::CPW;           // lanes per value group
+  constexpr float kTop = (float)((1 << BITS) - 1);
+  uint32_t kmn[HW], kmx[HW];
+#pragma unroll
+  for (int h = 0; h < HW; ++h) kmn[h] = kmx[h] = u4_get(x[0].k[h / 4], h % 4);
+#pragma unroll
+  for (int i = 1; i < WC::PF; ++i)
+    if (i < wsteps) {
+#pragma unroll
+      for (int h = 0; h < HW; ++h) {
+        kmn[h] = pk_min16(kmn[h], u4_get(x[i].k[h / 4], h % 4));
+        kmx[h] = pk_max16(kmx[h], u4_get(x[i].k[h / 4], h % 4));
+      }
+    }
+  uint4 *dst = reinterpret_cast<uint4 *>(&rf.part[wv][slot][w * HW][0]);
+#pragma unroll
+  for (int j = 0; j < HW / 2; ++j)
+    dst[j] = make_uint4(neg16x2(kmn[2 * j]), kmx[2 * j], neg16x2(kmn[2 * j + 1]), kmx[2 * j + 1]);
+
+#pragma unroll
+  for (int i = 0; i < WC::PF; ++i)
+    if (i < wsteps) {
+      const int t = begin + i * WC::STEP + slot;  // window token
+      uint32_t mn = u4_get(x[i].v[0], 0), mx = mn;
+#pragma unroll
+      for (int h = 1; h < HW; ++h) {
+        mn = pk_min16(mn, u4_get(x[i].v[h / 4], h % 4));
+        mx = pk_max16(mx, u4_get(x[i].v[h / 4], h % 4));
+      }
+      const uint32_t nm = pk_max16(neg16x2(mn), swap16(neg16x2(mn)));
+      const uint32_t xm = pk_max16(mx, swap16(mx));
+      const half2_t r =
+          __builtin_bit_cast(half2_t, lane_group_pkmax<LG>((nm & 0xFFFFu) | (xm & 0xFFFF0000u)));
+      const GroupParams g = group_params(-(float)r.x, (float)r.y, kTop);
+      const size_t tile = tile0 + (size_t)(t / G);
+      const int e = ((w * C::CPW) / G) * G + t % G;  // [group][token] inside the tile
+      if (w % LG == 0) {
+        ea.v_zero[tile * kD + e] = g.zero16;
+        ea.v_scale[tile * kD + e] = g.scale16;
+      }
+      ea.v_codes[tile * (C::W * G) + w * G + t % G] = encode_lane_word<BITS, NV>(
+          x[i].v, [&](int) { return make_float2(g.mn, g.rs); }, [&](int) { return g.s; });
+    }
+}
+
+// After the barrier: thread tid takes channel 2 * cp + mm of tile T
+// (tid = 128 T + 2 cp + mm); the pair's two threads swap their halves by DPP.
+template <int BITS, int G>
+__device__ __forceinline__ void flush_regs_params(const EncodeArgs &ea, RegFlushSmem<BITS, G> &rf,
+                                                  size_t tile0, int R, int wpw, int tid) {
+  using C = DecCfg<BITS, G>;
+  constexpr float kTop = (float)((1 << BITS) - 1);
+  const int T = tid >> 7, cp = (tid >> 1) & 63, mm = tid & 1;
+  if (T >= R / G) return;  // uniform over each pair of waves
+  const int nwt = G / wpw, u0 = T * nwt;
+  uint32_t v = rf.part[u0][0][cp][mm];
+  for (int u = u0; u < u0 + nwt; ++u)
+#pragma unroll
+    for (int sl = 0; sl < C::TQS; ++sl) v = pk_max16(v, rf.part[u][sl][cp][mm]);
+  const half2_t hv = __builtin_bit_cast(half2_t, v), hp = __builtin_bit_cast(half2_t, dppu<0xB1>(v));
+  const float mn = mm ? -(float)hp.y : -(float)hv.x;
+  const float mx = mm ? (float)hv.y : (float)hp.x;
+  const GroupParams g = group_params(mn, mx, kTop);
+  const int c = 2 * cp + mm;
+  ea.k_zero[(tile0 + T) * kD + c] = g.zero16;
+  ea.k_scale[(tile0 + T) * kD + c] = g.scale16;
+  rf.prm[T][c] = make_float2(g.mn, g.rs);
+  rf.step[T][c] = g.s;
+}
+
+// After the second barrier: the lane's key code words (one per step).
+template <int BITS, int G>
+__device__ __forceinline__ void flush_regs_keys(const EncodeArgs &ea, const RegFlushSmem<BITS, G> &rf,
+                                                const WinStep<BITS, G> (&x)[WinCfg<BITS, G>::PF],
+                                                int wsteps, size_t tile0, int begin, int w,
+                                                int slot) {
+  using C = DecCfg<BITS, G>;
+  using WC = WinCfg<BITS, G>;
+  const int T = begin / G;
+  float2 pr[C::CPW];
+#pragma unroll
+  for (int i = 0; i < C::CPW; ++i) pr[i] = rf.prm[T][w * C::CPW + i];
+#pragma unroll
+  for (int i = 0; i < WC::PF; ++i)
+    if (i < wsteps) {
+      const int t = begin + i * WC::STEP + slot;
+      ea.k_codes[(tile0 + T) * (C::W * G) + w * G + t % G] = encode_lane_word<BITS, WC::NV>(
+          x[i].k, [&](int c) { return pr[c]; }, [&](int c) { return rf.step[T][w * C::CPW + c]; });
+    }
+}
+
+template <int BITS, int G, bool FUSED>
+__global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_kernel(DecodeArgs a,
+                                                                                  EncodeArgs ea) {
   using C = DecCfg<BITS, G>;
   using WC = WinCfg<BITS, G>;
   __shared__ DecSmem<BITS, G> sm;
@@ -974,6 +1234,44 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
   const int S = a.splits;
 
   int ql = a.q_len[b], rl = a.r_len[b];
+  // Whole step (FUSED, one workgroup per (sequence, head)): append the new
+  // token at window slot rnew, decode over the window including it, and
+  // flush the window if that filled it; the same results as the three
+  // separate calls.  The new token's row is written to the cache, and used
+  // from registers wherever this kernel needs it.
+  const int ql0 = ql;
+  int rl1 = rl;  // window length after the append (FUSED)
+  int rnew = -1;
+  bool flush = false, commit = false;
+  uint32_t ticket = 0;
+  const uint4 *knew = nullptr, *vnew = nullptr;
+  if constexpr (FUSED) {
+    knew = reinterpret_cast<const uint4 *>(a.k_new + bh * kD);
+    vnew = reinterpret_cast<const uint4 *>(a.v_new + bh * kD);
+    if (rl >= 0 && rl < a.R) {
+      rnew = rl;
+      rl += 1;
+      commit = true;
+      if (tid < 2 * (kD / 8)) {  // 16 bytes of the key or value row per thread
+        const int c = tid % (kD / 8);
+        const uint4 x = tid < kD / 8 ? knew[c] : vnew[c];
+        half_t *dst = (tid < kD / 8 ? ea.k_res : ea.v_res) + (bh * a.R + rnew) * kD;
+        reinterpret_cast<uint4 *>(dst)[c] = x;
+      }
+    } else if (h == 0 && tid == 0) {
+      atomicOr(a.status, rl < 0 ? KIVI_ST_BAD_LENGTH : KIVI_ST_RESIDUAL_FULL);
+    }
+    flush = flush_ok(ql, rl, G, a.R, a.cap);
+    if (!flush && rl == a.R && h == 0 && tid == 0)
+      atomicOr(a.status, (ql < 0 || ql % G) ? KIVI_ST_BAD_LENGTH : KIVI_ST_CAPACITY);
+    commit = commit || flush;
+    rl1 = rl;
+    // every workgroup of the sequence takes a ticket once it has read the
+    // lengths; the one with the last ticket writes the new lengths at the end
+    if (commit && tid == 0)
+      ticket = __hip_atomic_fetch_add(ea.tickets + (size_t)b * kTicketStride, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (!(ql >= 0 && ql <= a.cap && (ql % G) == 0 && rl >= 0 && rl <= a.R)) {
     if (split == 0 && h == 0 && tid == 0) atomicOr(a.status, KIVI_ST_BAD_LENGTH);
     ql = 0;
@@ -1077,14 +1375,40 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
     float qv[C::CPW];
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) qv[i] = stg.qs[w * C::CPW + i];
+    // the appended token (FUSED) comes from registers, not from the cache
+    auto fresh = [&](WinStep<BITS, G> &x, int i) {
+      if constexpr (FUSED) {
+        if (ws.begin + i * WC::STEP + slot == rnew) {
+#pragma unroll
+          for (int v = 0; v < WC::NV; ++v) {
+            x.k[v] = knew[(w * C::CPW) / 8 + v];
+            x.v[v] = vnew[(w * C::CPW) / 8 + v];
+          }
+        }
+      }
+    };
 #pragma unroll
     for (int i = 0; i < WC::PF; ++i)
-      if (i < wsteps) window_step<BITS, G>(wpf[i], ws.begin + i * WC::STEP + slot < ws.end, qv, st);
+      if (i < wsteps) {
+        fresh(wpf[i], i);
+        window_step<BITS, G>(wpf[i], ws.begin + i * WC::STEP + slot < ws.end, qv, st);
+      }
     for (int i = WC::PF; i < wsteps; ++i) {  // windows longer than the prefetched steps
       WinStep<BITS, G> x;
       ws.issue(x, i);
+      fresh(x, i);
       window_step<BITS, G>(x, ws.begin + i * WC::STEP + slot < ws.end, qv, st);
     }
+  }
+  // Whole step whose append filled the window (R <= 128): the flush's value
+  // words and key partials, from the window registers.
+  [[maybe_unused]] bool regflush = false;
+  [[maybe_unused]] const size_t tile0 = bh * tps + (size_t)(ql0 / G);
+  if constexpr (FUSED) {
+    regflush = flush && a.win_per_wave <= 16;
+    if (regflush && wsteps > 0)
+      flush_regs_values<BITS, G>(ea, fused_flush_smem<BITS, G>().reg, wpf, wsteps, tile0, ws.begin, wv,
+                                 w, slot);
   }
   wave_publish<C::CPW, C::W, C::W == 8>(sm.fin.acc[wv], sm.fin.bias[wv], sm.fin.m[wv],
                                          sm.fin.l[wv], st.m, st.l, st.acc, st.bias);
@@ -1114,6 +1438,25 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
   }
   if (S == 1) {  // the workgroup saw every token: finish here
     if (tid < kD) a.out[bh * kD + tid] = L > 0.0f ? acc_out / L : 0.0f;
+    if constexpr (FUSED) {
+      if (regflush) {
+        flush_regs_params<BITS, G>(ea, fused_flush_smem<BITS, G>().reg, tile0, a.R, a.win_per_wave, tid);
+        __syncthreads();
+        if (wsteps > 0)
+          flush_regs_keys<BITS, G>(ea, fused_flush_smem<BITS, G>().reg, wpf, wsteps, tile0, ws.begin, w,
+                                   slot);
+      } else if (flush) {
+        // longer windows: read again (mostly L2 hits, this workgroup has
+        // just read them) and quantized through LDS
+        flush_window<BITS, G, G, kDecodeThreads>(ea, bh, ql0, tid, fused_flush_smem<BITS, G>().lds,
+                                                 rnew, knew, vnew, 0, a.R);
+      }
+      if (commit && tid == 0 && ticket == (uint32_t)a.heads - 1) {
+        ea.q_len[b] = flush ? ql0 + a.R : ql0;
+        ea.r_len[b] = flush ? 0 : rl1;
+        ea.tickets[(size_t)b * kTicketStride] = 0u;
+      }
+    }
     return;
   }
 
@@ -1135,7 +1478,7 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
   if (tid == 0)
-    sm.ticket = (int)__hip_atomic_fetch_add(a.tickets + bh, 1u, __ATOMIC_RELAXED,
+    sm.ticket = (int)__hip_atomic_fetch_add(a.tickets + bh * kTicketStride, 1u, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (sm.ticket != S - 1) return;
@@ -1161,7 +1504,8 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
     }
     a.out[bh * kD + tid] = lsum > 0.0f ? macc / lsum : 0.0f;
   }
-  if (tid == 0) __hip_atomic_store(a.tickets + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0)
+    __hip_atomic_store(a.tickets + bh * kTicketStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int BITS, int G>
@@ -1181,8 +1525,12 @@ int launch_encode(int bits, int G, const EncodeArgs &ea, dim3 grid, hipStream_t 
 }
 
 template <int BITS, int G>
-int launch_decode_t(const DecodeArgs &da, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<BITS, G>), grid, dim3(kDecodeThreads), 0, st, da);
+int launch_decode_t(const DecodeArgs &da, const EncodeArgs &ea, bool fused, dim3 grid,
+                    hipStream_t st) {
+  if (fused)
+    hipLaunchKernelGGL((decode_kernel<BITS, G, true>), grid, dim3(kDecodeThreads), 0, st, da, ea);
+  else
+    hipLaunchKernelGGL((decode_kernel<BITS, G, false>), grid, dim3(kDecodeThreads), 0, st, da, ea);
   return (int)hipGetLastError();
 }
 
@@ -1225,7 +1573,7 @@ int launch_flush(const kivi_dims &d, const kivi_cache &c, void *stream) {
   ea.src_v = ea.v_res;
   ea.src_tokens = d.residual;
   ea.prefill = 0;
-  const dim3 grid(d.heads, d.batch);
+  const dim3 grid(d.residual / d.group, d.heads, d.batch);
   const int G = d.group;
   if (d.bits == 2 && G == 32) hipLaunchKernelGGL((flush_kernel<2, 32>), grid, dim3(kFlushThreads), 0, st, ea);
   else if (d.bits == 2 && G == 64) hipLaunchKernelGGL((flush_kernel<2, 64>), grid, dim3(kFlushThreads), 0, st, ea);
@@ -1260,9 +1608,10 @@ int launch_prefill(const kivi_dims &d, const kivi_cache &c, const void *k, const
   return (int)hipGetLastError();
 }
 
-int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, const void *q,
-                  float *out, float sm_scale, void *workspace, void *stream) {
-  hipStream_t st = static_cast<hipStream_t>(stream);
+namespace {
+
+DecodeArgs decode_args(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, const void *q,
+                       float *out, float sm_scale, void *workspace) {
   DecodeArgs da{};
   da.k_codes = static_cast<const uint32_t *>(c.k_codes);
   da.v_codes = static_cast<const uint32_t *>(c.v_codes);
@@ -1286,15 +1635,44 @@ int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, 
   da.splits = p.splits;
   da.win_per_wave = p.win_per_wave;
   da.part_stride = (int)p.part_floats;
-  const dim3 grid(p.splits, d.heads, d.batch);
+  return da;
+}
+
+int launch_decode_any(const kivi_dims &d, const DecodeArgs &da, const EncodeArgs &ea, bool fused,
+                      hipStream_t st) {
+  const dim3 grid(da.splits, d.heads, d.batch);
   const int G = d.group;
-  if (d.bits == 2 && G == 32) return launch_decode_t<2, 32>(da, grid, st);
-  if (d.bits == 2 && G == 64) return launch_decode_t<2, 64>(da, grid, st);
-  if (d.bits == 2 && G == 128) return launch_decode_t<2, 128>(da, grid, st);
-  if (d.bits == 4 && G == 32) return launch_decode_t<4, 32>(da, grid, st);
-  if (d.bits == 4 && G == 64) return launch_decode_t<4, 64>(da, grid, st);
-  if (d.bits == 4 && G == 128) return launch_decode_t<4, 128>(da, grid, st);
+  if (d.bits == 2 && G == 32) return launch_decode_t<2, 32>(da, ea, fused, grid, st);
+  if (d.bits == 2 && G == 64) return launch_decode_t<2, 64>(da, ea, fused, grid, st);
+  if (d.bits == 2 && G == 128) return launch_decode_t<2, 128>(da, ea, fused, grid, st);
+  if (d.bits == 4 && G == 32) return launch_decode_t<4, 32>(da, ea, fused, grid, st);
+  if (d.bits == 4 && G == 64) return launch_decode_t<4, 64>(da, ea, fused, grid, st);
+  if (d.bits == 4 && G == 128) return launch_decode_t<4, 128>(da, ea, fused, grid, st);
   return (int)hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, const void *q,
+                  float *out, float sm_scale, void *workspace, void *stream) {
+  const DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, workspace);
+  return launch_decode_any(d, da, encode_args(d, c), false, static_cast<hipStream_t>(stream));
+}
+
+int launch_decode_step(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
+                       const void *k_new, const void *v_new, const void *q, float *out,
+                       float sm_scale, void *workspace, void *stream) {
+  if (p.splits != 1) {  // the window is spread over several workgroups: three kernels
+    int rc = launch_append(d, c, k_new, v_new, stream);
+    if (rc) return rc;
+    rc = launch_decode(d, c, p, q, out, sm_scale, workspace, stream);
+    if (rc) return rc;
+    return launch_flush(d, c, stream);
+  }
+  DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, workspace);
+  da.k_new = static_cast<const half_t *>(k_new);
+  da.v_new = static_cast<const half_t *>(v_new);
+  return launch_decode_any(d, da, encode_args(d, c), true, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace kivi

@@ -23,7 +23,7 @@ ST_RESIDUAL_FULL, ST_CAPACITY, ST_BAD_LENGTH = 0x1, 0x2, 0x4
 # Every symbol the public header declares.
 EXPORTS = ("kivi_validate_dims", "kivi_append_kv", "kivi_flush_residual", "kivi_prefill",
            "kivi_decode_workspace_bytes", "kivi_decode_splits", "kivi_decode_attn",
-           "kivi_strerror")
+           "kivi_decode_step", "kivi_strerror")
 
 
 class Dims(ctypes.Structure):
@@ -63,6 +63,8 @@ def lib():
         L.kivi_decode_workspace_bytes.restype = ctypes.c_size_t
         L.kivi_decode_splits.argtypes = [P(Dims)]
         L.kivi_decode_attn.argtypes = [P(Dims), P(CacheStruct), V, V, ctypes.c_float, V,
+                                       ctypes.c_size_t, V]
+        L.kivi_decode_step.argtypes = [P(Dims), P(CacheStruct), V, V, V, V, ctypes.c_float, V,
                                        ctypes.c_size_t, V]
         L.kivi_strerror.argtypes = [ctypes.c_int]
         L.kivi_strerror.restype = ctypes.c_char_p
@@ -136,7 +138,7 @@ class KiviCache:
         self.q_len = torch.zeros((batch,), dtype=i32, device=dev)
         self.r_len = torch.zeros((batch,), dtype=i32, device=dev)
         self.status = torch.zeros((1,), dtype=i32, device=dev)
-        self.tickets = torch.zeros((batch,), dtype=i32, device=dev)
+        self.tickets = torch.zeros((batch, 64), dtype=i32, device=dev)
         self.workspace = None
         self._struct = None
 
@@ -203,8 +205,7 @@ def new_workspace(dims, device="cuda"):
     return torch.zeros((n,), dtype=torch.uint8, device=device)
 
 
-def decode_attn(cache, q, sm_scale, out=None, workspace=None):
-    """out[b, h] = softmax(sm_scale * q[b, h] . K^T) V over the cache; fp32."""
+def _decode_buffers(cache, q, out, workspace):
     d = cache.dims
     _need(q, torch.float16, (d.batch, d.heads, d.head_dim), "q")
     if out is None:
@@ -216,8 +217,28 @@ def decode_attn(cache, q, sm_scale, out=None, workspace=None):
         workspace = cache.workspace
     if workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
-    nbytes = workspace.numel() * workspace.element_size()
+    return out, workspace, workspace.numel() * workspace.element_size()
+
+
+def decode_attn(cache, q, sm_scale, out=None, workspace=None):
+    """out[b, h] = softmax(sm_scale * q[b, h] . K^T) V over the cache; fp32."""
+    d = cache.dims
+    out, workspace, nbytes = _decode_buffers(cache, q, out, workspace)
     _check(lib().kivi_decode_attn(ctypes.byref(d), ctypes.byref(cache.struct()), q.data_ptr(),
                                   out.data_ptr(), ctypes.c_float(sm_scale), workspace.data_ptr(),
                                   ctypes.c_size_t(nbytes), _stream()), "kivi_decode_attn")
+    return out
+
+
+def decode_step(cache, k_new, v_new, q, sm_scale, out=None, workspace=None):
+    """append_kv, decode_attn, flush_residual in one call (one kernel when a
+    workgroup covers a whole (sequence, head)); returns the fp32 output."""
+    d = cache.dims
+    _need(k_new, torch.float16, (d.batch, d.heads, d.head_dim), "k_new")
+    _need(v_new, torch.float16, (d.batch, d.heads, d.head_dim), "v_new")
+    out, workspace, nbytes = _decode_buffers(cache, q, out, workspace)
+    _check(lib().kivi_decode_step(ctypes.byref(d), ctypes.byref(cache.struct()), k_new.data_ptr(),
+                                  v_new.data_ptr(), q.data_ptr(), out.data_ptr(),
+                                  ctypes.c_float(sm_scale), workspace.data_ptr(),
+                                  ctypes.c_size_t(nbytes), _stream()), "kivi_decode_step")
     return out

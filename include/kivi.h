@@ -86,9 +86,11 @@ typedef struct {
  *   q_len  int32 [batch]  quantized tokens held (multiple of G, <= capacity)
  *   r_len  int32 [batch]  window tokens held, 0 <= r_len <= R
  *   status uint32 [1]     sticky KIVI_ST_* bits (caller clears it).
- *   tickets uint32 [batch] per-sequence counters of kivi_flush_residual;
- *                          zero-filled before first use, left zero-filled
- *                          by every call.
+ *   tickets uint32 [batch][64]  per-sequence counters of kivi_flush_residual
+ *                          and kivi_decode_step (element [b][0]; the rest
+ *                          of each row keeps counters on separate cache
+ *                          lines); zero-filled before first use, left
+ *                          zero-filled by every call.
  * Sequence b's context is its q_len[b] quantized tokens followed by its
  * r_len[b] window tokens, oldest first.
  *
@@ -183,6 +185,22 @@ int kivi_decode_splits(const kivi_dims *dims);
 int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache,
                      const void *q, float *out, float sm_scale,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One whole generation step: kivi_append_kv, then kivi_decode_attn, then
+ * kivi_flush_residual, with the same results (outputs, cache contents,
+ * lengths, status bits) as those three calls in that order, arguments as
+ * there.  When one workgroup covers a whole (sequence, head) (see
+ * kivi_decode_splits: 1) it is a single kernel: each workgroup appends its
+ * (sequence, head)'s token, uses it from registers in the attention, and if
+ * the window is then full quantizes it (re-reading it from the cache while
+ * it is still in L2) and the last workgroup of the sequence commits the
+ * lengths through cache->tickets.  Otherwise it launches the three kernels.
+ */
+int kivi_decode_step(const kivi_dims *dims, const kivi_cache *cache,
+                     const void *k_new, const void *v_new, const void *q,
+                     float *out, float sm_scale, void *workspace,
+                     size_t workspace_bytes, void *stream);
 
 /* Static description of a return code. */
 const char *kivi_strerror(int code);

@@ -64,8 +64,9 @@ def test_decode_plan(dims, splits):
     assert kivi.decode_splits(d) == splits
     bh = dims[0] * dims[1]
     ws = kivi.workspace_bytes(d)
-    # partial states (4 + head_dim floats per split) plus one ticket per (sequence, head)
-    assert ws >= bh * splits * (4 + 128) * 4 + bh * 4
+    # partial states (4 + head_dim floats per split) plus one ticket per
+    # (sequence, head), each on its own 256-byte line
+    assert ws >= bh * splits * (4 + 128) * 4 + bh * 256
     assert ws % 256 == 0
 
 

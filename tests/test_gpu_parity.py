@@ -216,7 +216,7 @@ def test_decode_is_deterministic_and_leaves_workspace_clean():
     d = c.dims
     ws = c.workspace.cpu().numpy()
     bh = d.batch * d.heads
-    tickets = ws[len(ws) - ((bh * 4 + 255) // 256 * 256):][: bh * 4]
+    tickets = ws[len(ws) - bh * 256:]
     assert np.all(tickets == 0)
 
 
@@ -336,3 +336,133 @@ def test_quantizer_near_ties_bit_exact_on_both_encoders(bits):
             for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
                 got = getattr(c, name)[0, h, :R // G].cpu().numpy()
                 assert np.array_equal(got.view(np.uint8), enc[name].view(np.uint8)), name
+
+
+def _state(c):
+    return {n: t.cpu().numpy().copy() for n, t in c.buffers().items()}
+
+
+def _step_both(make, k_new, v_new, q, scale):
+    """Run append + decode + flush on one cache and decode_step on an
+    identical one; return both outputs and both final states."""
+    a, b = make(), make()
+    kivi.append_kv(a, k_new, v_new)
+    out_a = kivi.decode_attn(a, q, scale).clone()
+    kivi.flush_residual(a)
+    out_b = kivi.decode_step(b, k_new, v_new, q, scale).clone()
+    torch.cuda.synchronize()
+    return out_a, out_b, _state(a), _state(b)
+
+
+def _assert_same_step(out_a, out_b, sa, sb):
+    assert torch.equal(out_a, out_b)
+    for name in sa:
+        assert np.array_equal(sa[name].view(np.uint8), sb[name].view(np.uint8)), name
+    assert not sb["tickets"].any()
+
+
+@pytest.mark.parametrize("q_len,r_len,capacity,bad_q", [
+    (192, 31, 256, None),   # the append fills the window: flushed in the same kernel
+    (192, 5, 256, None),    # append only
+    (0, 0, 256, None),      # empty cache
+    (192, 32, 256, None),   # full window: the append is refused, the flush happens
+    (192, 31, 224, None),   # the flush would pass capacity
+    (192, 31, 256, 33),     # q_len not a multiple of G
+])
+def test_decode_step_matches_three_calls_tiny(q_len, r_len, capacity, bad_q):
+    w = workload(1)
+    kn = torch.from_numpy(w.k[:, :, 255]).cuda().contiguous()
+    vn = torch.from_numpy(w.v[:, :, 255]).cuda().contiguous()
+    q = torch.from_numpy(w.q).cuda()
+
+    def make():
+        c = gpu_cache(w, capacity=capacity, q_len=[q_len], r_len=[r_len])
+        if bad_q is not None:
+            c.q_len.fill_(bad_q)
+        return c
+    out_a, out_b, sa, sb = _step_both(make, kn, vn, q, w.config.sm_scale)
+    _assert_same_step(out_a, out_b, sa, sb)
+
+
+@pytest.mark.parametrize("bits,G,R", [
+    (2, 32, 128), (4, 32, 128), (2, 64, 128), (4, 128, 128),
+    (2, 32, 64), (4, 64, 64),        # 8 window tokens per wave
+    (2, 32, 256), (4, 128, 256),     # longer windows: read again and quantized through LDS
+])
+def test_decode_step_flush_in_kernel_matches_oracle(bits, G, R):
+    """The append fills the window and the same kernel flushes it: the new
+    tiles equal the oracle's encoding of the window (new token included) bit
+    for bit, and the whole state equals that of the three separate calls."""
+    rng = np.random.default_rng(1000 + 7 * bits + G + R)
+    B, H, D = 2, 3, 128
+    ql, n = G, G + R - 1
+    cap = ql + R
+    k = rng.standard_normal((B, H, n, D), np.float32)
+    k[..., ::9] *= 8.0                                  # a few outlier key channels
+    k = k.astype(np.float16)
+    v = rng.standard_normal((B, H, n, D), np.float32).astype(np.float16)
+    k_new = rng.standard_normal((B, H, D), np.float32).astype(np.float16)
+    v_new = rng.standard_normal((B, H, D), np.float32).astype(np.float16)
+    q = rng.standard_normal((B, H, D), np.float32).astype(np.float16)
+    kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    lens = torch.full((B,), n, dtype=torch.int32, device="cuda")
+    res = torch.full((B,), R - 1, dtype=torch.int32, device="cuda")
+
+    def make():
+        c = kivi.KiviCache(B, H, D, bits, G, R, cap)
+        kivi.prefill(c, kt, vt, lens, res)
+        return c
+    dims = kivi.make_dims(batch=B, heads=H, head_dim=D, bits=bits, group=G, residual=R,
+                          capacity=cap)
+    assert kivi.decode_splits(dims) == 1
+    out_a, out_b, sa, sb = _step_both(make, torch.from_numpy(k_new).cuda(),
+                                      torch.from_numpy(v_new).cuda(), torch.from_numpy(q).cuda(),
+                                      0.125)
+    _assert_same_step(out_a, out_b, sa, sb)
+    assert (sb["q_len"] == ql + R).all() and (sb["r_len"] == 0).all()
+    assert not sb["status"].any()
+    t0, t1 = ql // G, (ql + R) // G
+    for b in range(B):
+        for h in range(H):
+            enc = ocache.encode_tokens(np.concatenate([k[b, h, ql:], k_new[b, h][None]]),
+                                       np.concatenate([v[b, h, ql:], v_new[b, h][None]]), G, bits)
+            for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+                got = sb[name][b, h, t0:t1]
+                assert np.array_equal(got.view(np.uint8), enc[name].view(np.uint8)), (name, b, h)
+
+
+@pytest.mark.parametrize("number", [2, 4])
+def test_decode_step_matches_three_calls_full_workloads(number):
+    """The Llama-2-7B-shaped layer (every window fills and is flushed in the
+    step) and a ragged batch (a mix of flushed and not): one kernel per step
+    (one workgroup per (sequence, head)), identical to the three calls."""
+    w = workload(number, batch=16 if number == 4 else None)
+    cfg = w.config
+    rl = np.minimum(w.r_len, cfg.residual - 1) if number == 4 else w.r_len - 1
+    rng = np.random.default_rng(5)
+    kn = torch.from_numpy(rng.standard_normal((len(rl), cfg.heads, 128), np.float32)
+                          .astype(np.float16)).cuda()
+    vn = torch.from_numpy(rng.standard_normal((len(rl), cfg.heads, 128), np.float32)
+                          .astype(np.float16)).cuda()
+    q = torch.from_numpy(w.q).cuda()
+    d = w.dims()
+    assert kivi.decode_splits(kivi.make_dims(**d)) == 1
+    out_a, out_b, sa, sb = _step_both(lambda: gpu_cache(w, r_len=rl), kn, vn, q, cfg.sm_scale)
+    _assert_same_step(out_a, out_b, sa, sb)
+    if number == 2:
+        assert (sb["r_len"] == 0).all() and (sb["q_len"] == w.q_len + 128).all()
+
+
+def test_decode_step_with_split_heads_uses_three_kernels():
+    """Batch 1 x 32 heads over a long context splits each (sequence, head)
+    over several workgroups; decode_step then runs the three kernels."""
+    w = workload(5, bits=2)
+    d = w.dims()
+    assert kivi.decode_splits(kivi.make_dims(**d)) > 1
+    ql, rl = np.array([4096], np.int32), np.array([127], np.int32)
+    rng = np.random.default_rng(6)
+    kn = torch.from_numpy(rng.standard_normal((1, 32, 128), np.float32).astype(np.float16)).cuda()
+    vn = torch.from_numpy(rng.standard_normal((1, 32, 128), np.float32).astype(np.float16)).cuda()
+    q = torch.from_numpy(w.q).cuda()
+    out_a, out_b, sa, sb = _step_both(lambda: gpu_cache(w, q_len=ql, r_len=rl), kn, vn, q, 1.0)
+    _assert_same_step(out_a, out_b, sa, sb)
