@@ -16,8 +16,9 @@ captured in one HIP graph and replayed once between two synchronisations
 starting state as separate calls, one phase at a time (all appends, all
 decodes, all flushes), each phase a HIP graph replayed between HIP events on
 the launch stream, which give the per-kernel average GPU durations of the
-three separate kernels (the decode kernel's feeds the roofline); their
-outputs must equal the whole-step kernel's bit for bit.  The CPU oracle is timed beside it on a
+three separate kernels (the decode kernel's feeds the roofline); they must
+leave the cache exactly as the whole-step kernel does, and give its output up
+to rounding.  The CPU oracle is timed beside it on a
 bounded sample of (sequence, head) steps.
 
 Prints one JSON line on stdout; diagnostics go to stderr.
@@ -236,6 +237,7 @@ def main():
         wall = time.perf_counter() - t0
         replay_ok = bool(torch.equal(outs[0], eager_out0))
         states_ok = bool(all(c.status_bits() == 0 for c in copies[:K]))
+        step_state = {n: t.clone() for n, t in copies[0].buffers().items()}
         reset()
         torch.cuda.synchronize()
 
@@ -275,10 +277,16 @@ def main():
     eager_wall = time.perf_counter() - t0
     if graph is None:
         wall = eager_wall
-    eager_ok = bool(torch.equal(outs[0], eager_out0))
+    # The three kernels must leave the cache bit for bit as the whole-step
+    # kernel does; their output may differ from it by rounding only (the
+    # whole-step kernel may take the window tokens first).
+    eager_ok = bool(torch.allclose(outs[0], eager_out0, rtol=1e-5, atol=1e-6))
     if graph is None:
         replay_ok = eager_ok
         states_ok = bool(all(c.status_bits() == 0 for c in copies[:K]))
+    else:
+        eager_ok = eager_ok and all(torch.equal(t, step_state[n])
+                                    for n, t in copies[0].buffers().items())
 
     append_us = 1e3 * evs[0].elapsed_time(evs[1]) / K
     decode_us = 1e3 * evs[1].elapsed_time(evs[2]) / K
@@ -321,7 +329,7 @@ def main():
         "append_us": append_us,
         "flush_us": flush_us,
         "graph_replay_matches_eager": replay_ok,
-        "phased_matches_eager": eager_ok,
+        "phased_matches_step": eager_ok,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(cfg.name)},
     }

@@ -48,6 +48,12 @@ __device__ __forceinline__ uint32_t u4_get(const uint4 &v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// c ? a : b on values (a conditional on two uint4 lvalues can become a
+// select of their addresses, forcing them into scratch memory)
+__device__ __forceinline__ uint4 sel4(bool c, uint4 a, uint4 b) {
+  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(
@@ -101,42 +107,26 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
+// Whole-wave sum / maximum, the same value in every lane: DPP within each
+// row of 16 lanes (as lane_group_sum), then the four rows' lanes 0, 16, 32
+// and 48 read as scalars.
+__device__ __forceinline__ float row_sum16(float v) { return lane_group_sum<16>(v); }
+
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v = row_sum16(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-// Block-wide sums of N values; `red` is shared scratch of 4 * N floats.
-template <int N>
-__device__ __forceinline__ void block_sum(float (&v)[N], float *red) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int k = 0; k < N; ++k) v[k] = wave_sum(v[k]);
-  if (lane == 0) {
-#pragma unroll
-    for (int k = 0; k < N; ++k) red[wv * N + k] = v[k];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < N; ++k) v[k] = red[k] + red[N + k] + red[2 * N + k] + red[3 * N + k];
-  __syncthreads();
-}
-
-__device__ __forceinline__ float block_max(float v, float *red) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  v = wave_max(v);
-  if (lane == 0) red[wv] = v;
-  __syncthreads();
-  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return v;
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // ---------------------------------------------------------------- encoder
@@ -147,7 +137,8 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 struct GroupParams {
   float mn;  // canonical minimum (zero-point)
   float s;   // stored step as fp32
-  float rs;  // approximate 1 / s (0 when s == 0)
+  float rs;  // fast-path multiplier: 1 / s within one ulp, 0 when s == 0,
+             // NaN when s is an fp16 subnormal (see FastWord)
   half_t zero16, scale16;
 };
 
@@ -158,40 +149,71 @@ __device__ __forceinline__ GroupParams group_params(float mn_raw, float mx_raw, 
   const float step = (mx - g.mn) / levels;
   g.scale16 = (half_t)step;  // round to nearest even
   g.s = (float)g.scale16;
-  g.rs = g.s != 0.0f ? __builtin_amdgcn_rcpf(g.s) : 0.0f;
+  g.rs = g.s == 0.0f ? 0.0f : g.s < 0x1p-14f ? __builtin_nanf("") : __builtin_amdgcn_rcpf(g.s);
   g.zero16 = (half_t)g.mn;   // exact: mn is an fp16 value
   return g;
 }
 
-// Codes are clamp(rint((x - mn) / s), 0, top) with an IEEE division.  They
-// are computed as rint((x - mn) * rs) (rs = 1 / s within one ulp, 0 when
-// s == 0, which gives code 0 as required), except where that product lies
-// within 2^-16 of a half-integer: there the division decides.  Why that is
-// the same value: the quotient q = (x - mn) / s is below 32 (x - mn is at
-// most the group's range and s is at least half the range over the levels,
-// B <= 4), and the product differs from q by at most q * 2^-22 < 2^-17 (one
-// rounding of the product, a reciprocal within one ulp).  Away from the
-// half-integers by more than that, the product, q and q rounded to fp32
-// (which cannot cross an fp32-representable half-integer) all round to the
-// same integer.  code_fast keeps the largest |q - rint(q)| of a word in
-// dmax (exact: q >= 0, and q - rint(q) is exact by Sterbenz's lemma, so it
-// is at most 0.5); a word with dmax > kNearHalf had a product within 2^-16
-// of a half-integer, and its caller recomputes it with code_exact
-// (x - mn >= 0, so no clamp at 0 is needed).
+// Codes are clamp(rint((x - mn) / s), 0, top) with an IEEE division.  The
+// fast path computes rint((x - mn) * rs) (rs = 1 / s within one ulp, 0 when
+// s == 0, which gives code 0 as required) and falls back to the division
+// for a word where it may differ:
+//  * near ties: the quotient q = (x - mn) / s is below 32 (x - mn is at most
+//    the group's range and s is at least half the range over the levels,
+//    B <= 4), and the product differs from q by at most q * 2^-22 < 2^-17
+//    (one rounding of the product, a reciprocal within one ulp).  Away from
+//    the half-integers by more than that, the product, q and q rounded to
+//    fp32 (which cannot cross an fp32-representable half-integer) all round
+//    to the same integer.  dmax keeps the word's largest |q - rint(q)|
+//    (exact: q >= 0, and q - rint(q) is exact by Sterbenz's lemma, so it is
+//    at most 0.5); dmax > kNearHalf means a product within 2^-16 of a
+//    half-integer.
+//  * the clamp: with a normal fp16 step (s >= 2^-14, the fp32 step rounded
+//    to fp16 with a relative error of at most 2^-11) the product is at most
+//    top * (1 + 2^-10) < top + 1/2, so rint never passes top and the fast
+//    path needs no clamp.  A subnormal step has rs = NaN, which makes the
+//    word's sums NaN.
+// The fast codes enter the word as two fp32 sums, one per half word, of
+// c * 2^(B * i): integers below 2^16, so the sums are exact.  The exact path
+// needs no clamp at 0 (x - mn >= 0).
 constexpr float kNearHalf = 0.5f - 0x1p-16f;
 
-__device__ __forceinline__ float code_fast(float x, float mn, float rs, float &dmax) {
-  const float q = (x - mn) * rs;
-  const float c = rintf(q);
-  dmax = fmaxf(dmax, fabsf(q - c));
-  return c;
+// 1.0f the compiler cannot see through: fma(x, one, -mn) then stays an fma,
+// which takes an fp16 x directly (v_fma_mix_f32), and equals x - mn.
+__device__ __forceinline__ float opaque_one() {
+  float one = 1.0f;
+  asm volatile("" : "+v"(one));
+  return one;
 }
+
+template <int BITS, int CPW>
+struct FastWord {
+  float lo = 0.0f, hi = 0.0f, dmax = 0.0f, one = opaque_one();
+  // code i of the word: channel value x of a group {mn, rs}
+  __device__ __forceinline__ void add(int i, float x, float mn, float rs) {
+    const float q = fmaf(x, one, -mn) * rs;  // x - mn, rounded once
+    const float c = rintf(q);
+    dmax = fmaxf(dmax, fabsf(q - c));
+    const float f = (float)(1u << (BITS * (i % (CPW / 2))));
+    if (i < CPW / 2)
+      lo = fmaf(c, f, lo);
+    else
+      hi = fmaf(c, f, hi);
+  }
+  __device__ __forceinline__ bool exact_needed() const {
+    const float t = lo + hi;
+    return dmax > kNearHalf || t != t;
+  }
+  __device__ __forceinline__ uint32_t word() const {
+    return (uint32_t)lo | ((uint32_t)hi << (BITS * (CPW / 2)));
+  }
+};
 
 __device__ __forceinline__ float code_exact(float x, float mn, float s) {
   return s == 0.0f ? 0.0f : rintf((x - mn) / s);
 }
 
-// Pack CPW codes (as floats, each at most top after the clamp) into one word.
+// Pack CPW exact codes (as floats; clamped to top here) into one word.
 template <int BITS, int CPW>
 __device__ __forceinline__ uint32_t pack_codes(const float (&c)[CPW], float top) {
   uint32_t w = 0;
@@ -264,25 +286,20 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
 
   {
     constexpr int N = G * (kD / 8);  // uint4 per tile
+    static_assert(N % kThreads == 0, "whole passes");
     const uint4 *sk = reinterpret_cast<const uint4 *>(a.src_k + src_off);
     const uint4 *sv = reinterpret_cast<const uint4 *>(a.src_v + src_off);
-    uint4 rk[(N + kThreads - 1) / kThreads], rv[(N + kThreads - 1) / kThreads];
+    uint4 rk[N / kThreads], rv[N / kThreads];
 #pragma unroll
-    for (int i = 0; i < (N + kThreads - 1) / kThreads; ++i) {
-      const int e = tid + i * kThreads;
-      if (e < N) {
-        rk[i] = sk[e];
-        rv[i] = sv[e];
-      }
+    for (int i = 0; i < N / kThreads; ++i) {
+      rk[i] = sk[tid + i * kThreads];
+      rv[i] = sv[tid + i * kThreads];
     }
 #pragma unroll
-    for (int i = 0; i < (N + kThreads - 1) / kThreads; ++i) {
-      const int e = tid + i * kThreads;
-      if (e < N) {
-        const int t = e / (kD / 8), c = e % (kD / 8);
-        *reinterpret_cast<uint4 *>(&xk[t][c * 8]) = rk[i];
-        *reinterpret_cast<uint4 *>(&xv[t][c * 8]) = rv[i];
-      }
+    for (int i = 0; i < N / kThreads; ++i) {
+      const int e = tid + i * kThreads, t = e / (kD / 8), c = e % (kD / 8);
+      *reinterpret_cast<uint4 *>(&xk[t][c * 8]) = rk[i];
+      *reinterpret_cast<uint4 *>(&xv[t][c * 8]) = rv[i];
     }
   }
   __syncthreads();
@@ -324,24 +341,28 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     const int w = wi / G, t = wi % G;
     const int gi = ((w * CPW) / G) * G + t;
     const float vm = vmn[gi], vs = vst[gi], vr = vrs[gi];
-    float ck[CPW], cv[CPW];
-    float dmax = 0.0f;
+    FastWord<BITS, CPW> fk, fv;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int c = w * CPW + i;
-      ck[i] = code_fast((float)xk[t][c], kmn[c], krs[c], dmax);
-      cv[i] = code_fast((float)xv[t][c], vm, vr, dmax);
+      fk.add(i, (float)xk[t][c], kmn[c], krs[c]);
+      fv.add(i, (float)xv[t][c], vm, vr);
     }
-    if (dmax > kNearHalf) {
+    uint32_t wk = fk.word(), wv = fv.word();
+    if (fk.exact_needed()) {
+      float cd[CPW];
 #pragma unroll
-      for (int i = 0; i < CPW; ++i) {
-        const int c = w * CPW + i;
-        ck[i] = code_exact((float)xk[t][c], kmn[c], kst[c]);
-        cv[i] = code_exact((float)xv[t][c], vm, vs);
-      }
+      for (int i = 0; i < CPW; ++i) cd[i] = code_exact((float)xk[t][w * CPW + i], kmn[w * CPW + i], kst[w * CPW + i]);
+      wk = pack_codes<BITS, CPW>(cd, kTop);
     }
-    a.k_codes[ktile * (W * G) + wi] = pack_codes<BITS, CPW>(ck, kTop);
-    a.v_codes[ktile * (W * G) + wi] = pack_codes<BITS, CPW>(cv, kTop);
+    if (fv.exact_needed()) {
+      float cd[CPW];
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) cd[i] = code_exact((float)xv[t][w * CPW + i], vm, vs);
+      wv = pack_codes<BITS, CPW>(cd, kTop);
+    }
+    a.k_codes[ktile * (W * G) + wi] = wk;
+    a.v_codes[ktile * (W * G) + wi] = wv;
   }
 }
 
@@ -397,8 +418,9 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
       for (int i = 0; i < PE; ++i) {
         const int e = tid + i * NTHREADS, op = e / TE, f = e % TE;
         const int t = f / (kD / 8), c = f % (kD / 8);
-        const bool fresh = knew != nullptr && blk + tl * G + t == rnew;
-        *reinterpret_cast<uint4 *>(&fs.x[bf][op][t][c * 8]) = fresh ? fresh_row[op][c] : r[tl][i];
+        uint4 val = r[tl][i];
+        if (knew != nullptr && blk + tl * G + t == rnew) val = fresh_row[op][c];
+        *reinterpret_cast<uint4 *>(&fs.x[bf][op][t][c * 8]) = val;
       }
       __syncthreads();
       for (int gi = tid; gi < kD / 2 + kD; gi += NTHREADS) {
@@ -456,30 +478,34 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
             x[i + q] = (q & 1) ? (float)x2.y : (float)x2.x;
           }
         }
-        float dmax = 0.0f;
+        FastWord<BITS, CPW> fw;
         if (op == 0) {
 #pragma unroll
           for (int i = 0; i < CPW; ++i) {
             const float4 kq = fs.kp[bf][w * CPW + i];
-            cd[i] = code_fast(x[i], kq.x, kq.z, dmax);
+            fw.add(i, x[i], kq.x, kq.z);
           }
-          if (dmax > kNearHalf) {
+          uint32_t word = fw.word();
+          if (fw.exact_needed()) {
 #pragma unroll
             for (int i = 0; i < CPW; ++i) {
               const float4 kq = fs.kp[bf][w * CPW + i];
               cd[i] = code_exact(x[i], kq.x, kq.y);
             }
+            word = pack_codes<BITS, CPW>(cd, kTop);
           }
-          a.k_codes[tile * (W * G) + (wi % (W * G))] = pack_codes<BITS, CPW>(cd, kTop);
+          a.k_codes[tile * (W * G) + (wi % (W * G))] = word;
         } else {
           const float4 v = fs.vp[bf][((w * CPW) / G) * G + t];
 #pragma unroll
-          for (int i = 0; i < CPW; ++i) cd[i] = code_fast(x[i], v.x, v.z, dmax);
-          if (dmax > kNearHalf) {
+          for (int i = 0; i < CPW; ++i) fw.add(i, x[i], v.x, v.z);
+          uint32_t word = fw.word();
+          if (fw.exact_needed()) {
 #pragma unroll
             for (int i = 0; i < CPW; ++i) cd[i] = code_exact(x[i], v.x, v.y);
+            word = pack_codes<BITS, CPW>(cd, kTop);
           }
-          a.v_codes[tile * (W * G) + (wi % (W * G))] = pack_codes<BITS, CPW>(cd, kTop);
+          a.v_codes[tile * (W * G) + (wi % (W * G))] = word;
         }
       }
       if (NB == 1) __syncthreads();  // a single buffer is rewritten by the next tile
@@ -1107,16 +1133,15 @@ __device__ __forceinline__ uint32_t encode_lane_word(const uint4 (&x)[NV], Fast 
       xf[8 * v + 2 * e] = (float)h.x;
       xf[8 * v + 2 * e + 1] = (float)h.y;
     }
-  float dmax = 0.0f;
+  FastWord<BITS, CPW> fw;
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const float2 p = fast(i);
-    cd[i] = code_fast(xf[i], p.x, p.y, dmax);
+    fw.add(i, xf[i], p.x, p.y);
   }
-  if (dmax > kNearHalf) {
+  if (!fw.exact_needed()) return fw.word();
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) cd[i] = code_exact(xf[i], fast(i).x, step(i));
-  }
+  for (int i = 0; i < CPW; ++i) cd[i] = code_exact(xf[i], fast(i).x, step(i));
   return pack_codes<BITS, CPW>(cd, kTop);
 }
 
@@ -1319,7 +1344,33 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
   // (Issuing everything up front would not help: the memory system serves
   // all waves' requests interleaved, so the first data a wave needs would
   // arrive no sooner than the rest.)
+  // Except in a whole step whose append fills a window of at most 128
+  // tokens ("early"): there the window comes first -- its loads before the
+  // quantized ones, then its attention and the whole flush (quantized from
+  // the window registers) while the first quantized sub-chunks are in
+  // flight; after the last quantized byte, the flush's arithmetic would run
+  // with HBM idle.
+  [[maybe_unused]] const size_t tile0 = bh * tps + (size_t)(ql0 / G);
+  bool early = false;
+  if constexpr (FUSED) early = flush && a.win_per_wave <= 16;
+
   const uint32_t qraw = bload1(make_rsrc(a.q + bh * kD, kD * 2), (uint32_t)lane * 4, 0);
+  // FUSED: this lane's channels of the appended token, loaded unconditionally
+  // (a load under a branch would make the compiler wait for every load in
+  // flight after it)
+  [[maybe_unused]] WinStep<BITS, G> xnew;
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int v = 0; v < WC::NV; ++v) {
+      xnew.k[v] = knew[(w * C::CPW) / 8 + v];
+      xnew.v[v] = vnew[(w * C::CPW) / 8 + v];
+    }
+  }
+  WinStep<BITS, G> wpf[WC::PF];
+  if (early) {
+#pragma unroll
+    for (int i = 0; i < WC::PF; ++i) ws.issue(wpf[i], i);
+  }
   SubLoads<BITS, G> ring[kDecodeDepth];
 #pragma unroll
   for (int k = 0; k < kDecodeDepth; ++k) qs.issue(ring[k], k);
@@ -1329,7 +1380,7 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
   const float qs0 = (float)hq.x * a.qscale, qs1 = (float)hq.y * a.qscale;
   const float qf0 = qs0 * code_factor<BITS>((2 * lane) % C::CPW);
   const float qf1 = qs1 * code_factor<BITS>((2 * lane + 1) % C::CPW);
-  stg.qs[2 * lane] = qs0;  // for the window tokens, read back at the end
+  stg.qs[2 * lane] = qs0;  // for the window tokens
   stg.qs[2 * lane + 1] = qs1;
 
   LaneState<C::CPW> st;
@@ -1338,6 +1389,50 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
   st.bias = 0.0f;
 #pragma unroll
   for (int i = 0; i < C::CPW; ++i) st.acc[i] = 0.0f;
+
+  // the wave's window tokens; the appended token (FUSED) comes from
+  // registers, not from the cache
+  auto window = [&]() {
+    if (wsteps <= 0) return;
+    __builtin_amdgcn_wave_barrier();
+    float qv[C::CPW];
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) qv[i] = stg.qs[w * C::CPW + i];
+    auto fresh = [&](WinStep<BITS, G> &x, int i) {
+      if constexpr (FUSED) {
+        const bool hit = ws.begin + i * WC::STEP + slot == rnew;
+#pragma unroll
+        for (int v = 0; v < WC::NV; ++v) {
+          x.k[v] = sel4(hit, xnew.k[v], x.k[v]);
+          x.v[v] = sel4(hit, xnew.v[v], x.v[v]);
+        }
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < WC::PF; ++i)
+      if (i < wsteps) {
+        fresh(wpf[i], i);
+        window_step<BITS, G>(wpf[i], ws.begin + i * WC::STEP + slot < ws.end, qv, st);
+      }
+    for (int i = WC::PF; i < wsteps; ++i) {  // windows longer than the prefetched steps
+      WinStep<BITS, G> x;
+      ws.issue(x, i);
+      fresh(x, i);
+      window_step<BITS, G>(x, ws.begin + i * WC::STEP + slot < ws.end, qv, st);
+    }
+  };
+
+  if constexpr (FUSED) {
+    if (early) {
+      window();
+      auto &rf = fused_flush_smem<BITS, G>().reg;
+      if (wsteps > 0) flush_regs_values<BITS, G>(ea, rf, wpf, wsteps, tile0, ws.begin, wv, w, slot);
+      __syncthreads();
+      flush_regs_params<BITS, G>(ea, rf, tile0, a.R, a.win_per_wave, tid);
+      __syncthreads();
+      if (wsteps > 0) flush_regs_keys<BITS, G>(ea, rf, wpf, wsteps, tile0, ws.begin, w, slot);
+    }
+  }
 
   // Whole rounds of kDecodeDepth sub-chunks (no branch inside a round, so
   // the wait before each sub-chunk only covers its own loads), then the
@@ -1354,9 +1449,10 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
       qs.issue(ring[k], c0 + k + kDecodeDepth);
     }
   }
-  WinStep<BITS, G> wpf[WC::PF];
+  if (!early) {
 #pragma unroll
-  for (int i = 0; i < WC::PF; ++i) ws.issue(wpf[i], i);
+    for (int i = 0; i < WC::PF; ++i) ws.issue(wpf[i], i);
+  }
 #pragma unroll
   for (int k = 0; k < kDecodeDepth - 1; ++k)
     if (c0 + k < qs.n) {
@@ -1369,47 +1465,7 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
 #if KIVI_DECODE_PRIORITY
   __builtin_amdgcn_s_setprio(0);
 #endif
-
-  if (wsteps > 0) {
-    __builtin_amdgcn_wave_barrier();
-    float qv[C::CPW];
-#pragma unroll
-    for (int i = 0; i < C::CPW; ++i) qv[i] = stg.qs[w * C::CPW + i];
-    // the appended token (FUSED) comes from registers, not from the cache
-    auto fresh = [&](WinStep<BITS, G> &x, int i) {
-      if constexpr (FUSED) {
-        if (ws.begin + i * WC::STEP + slot == rnew) {
-#pragma unroll
-          for (int v = 0; v < WC::NV; ++v) {
-            x.k[v] = knew[(w * C::CPW) / 8 + v];
-            x.v[v] = vnew[(w * C::CPW) / 8 + v];
-          }
-        }
-      }
-    };
-#pragma unroll
-    for (int i = 0; i < WC::PF; ++i)
-      if (i < wsteps) {
-        fresh(wpf[i], i);
-        window_step<BITS, G>(wpf[i], ws.begin + i * WC::STEP + slot < ws.end, qv, st);
-      }
-    for (int i = WC::PF; i < wsteps; ++i) {  // windows longer than the prefetched steps
-      WinStep<BITS, G> x;
-      ws.issue(x, i);
-      fresh(x, i);
-      window_step<BITS, G>(x, ws.begin + i * WC::STEP + slot < ws.end, qv, st);
-    }
-  }
-  // Whole step whose append filled the window (R <= 128): the flush's value
-  // words and key partials, from the window registers.
-  [[maybe_unused]] bool regflush = false;
-  [[maybe_unused]] const size_t tile0 = bh * tps + (size_t)(ql0 / G);
-  if constexpr (FUSED) {
-    regflush = flush && a.win_per_wave <= 16;
-    if (regflush && wsteps > 0)
-      flush_regs_values<BITS, G>(ea, fused_flush_smem<BITS, G>().reg, wpf, wsteps, tile0, ws.begin, wv,
-                                 w, slot);
-  }
+  if (!early) window();
   wave_publish<C::CPW, C::W, C::W == 8>(sm.fin.acc[wv], sm.fin.bias[wv], sm.fin.m[wv],
                                          sm.fin.l[wv], st.m, st.l, st.acc, st.bias);
   __syncthreads();
@@ -1439,13 +1495,7 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
   if (S == 1) {  // the workgroup saw every token: finish here
     if (tid < kD) a.out[bh * kD + tid] = L > 0.0f ? acc_out / L : 0.0f;
     if constexpr (FUSED) {
-      if (regflush) {
-        flush_regs_params<BITS, G>(ea, fused_flush_smem<BITS, G>().reg, tile0, a.R, a.win_per_wave, tid);
-        __syncthreads();
-        if (wsteps > 0)
-          flush_regs_keys<BITS, G>(ea, fused_flush_smem<BITS, G>().reg, wpf, wsteps, tile0, ws.begin, w,
-                                   slot);
-      } else if (flush) {
+      if (flush && !early) {
         // longer windows: read again (mostly L2 hits, this workgroup has
         // just read them) and quantized through LDS
         flush_window<BITS, G, G, kDecodeThreads>(ea, bh, ql0, tid, fused_flush_smem<BITS, G>().lds,

@@ -355,7 +355,9 @@ def _step_both(make, k_new, v_new, q, scale):
 
 
 def _assert_same_step(out_a, out_b, sa, sb):
-    assert torch.equal(out_a, out_b)
+    # the cache bit for bit; the output up to rounding (the whole-step kernel
+    # may take the window tokens first, a different summation order)
+    torch.testing.assert_close(out_b, out_a, rtol=1e-5, atol=1e-6)
     for name in sa:
         assert np.array_equal(sa[name].view(np.uint8), sb[name].view(np.uint8)), name
     assert not sb["tickets"].any()
