@@ -67,9 +67,10 @@ def kernel_hash():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload_name):
-    """Per-launch HBM bytes of the decode kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
+def measured_traffic(workload_name, key="bytes_per_launch"):
+    """Per-launch HBM bytes of the decode kernel (or, with key
+    "step_bytes_per_launch", of the whole-step kernel) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -77,7 +78,7 @@ def measured_traffic(workload_name):
         return None
     if t.get("kernel_source_sha256") != kernel_hash() or t.get("workload") != workload_name:
         return None
-    return t.get("bytes_per_launch")
+    return t.get(key)
 
 
 def step_tokens(w):
@@ -231,10 +232,15 @@ def main():
         torch.cuda.synchronize()
         reset()
         torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        g0.record()
         graph.replay()
+        g1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        step_event_us = 1e3 * g0.elapsed_time(g1) / K
         replay_ok = bool(torch.equal(outs[0], eager_out0))
         states_ok = bool(all(c.status_bits() == 0 for c in copies[:K]))
         step_state = {n: t.clone() for n, t in copies[0].buffers().items()}
@@ -296,6 +302,7 @@ def main():
             f"status clean: {states_ok}")
 
     step_s = wall / K
+    one_kernel = kivi.decode_splits(base.dims) == 1
     qheads = Bt * H
     dec_bytes = wl.decode_bytes(w.q_len, r_start + 1, H, D, w.bits, cfg.group)
     achieved = dec_bytes / (decode_us * 1e-6) / 1e9
@@ -333,6 +340,16 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(cfg.name)},
     }
+    if one_kernel and graph is not None:
+        # the whole-step kernel itself: the step's algorithmic bytes over its
+        # per-step time inside the graph (HIP events around the replay)
+        sb = wl.step_bytes(w.q_len, r_start, H, D, w.bits, cfg.group, cfg.residual)
+        result["step_kernel"] = {
+            "kernel": "decode_kernel whole-step variant (kivi_decode_step)",
+            "us": step_event_us, "algorithmic_bytes": sb,
+            "GBps": sb / (step_event_us * 1e-6) / 1e9,
+            "frac": sb / (step_event_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+            "traffic": measured_traffic(cfg.name, "step_bytes_per_launch")}
     if args.copy_mb:
         # an elementwise kernel (not a DMA-engine memcpy, which no counter sees)
         src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device="cuda")

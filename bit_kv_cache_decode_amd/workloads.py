@@ -175,6 +175,27 @@ def flush_bytes_per_head(residual, head_dim, bits, group):
     return read + write
 
 
+def flush_write_bytes_per_head(residual, head_dim, bits, group):
+    """The write part of ``flush_bytes_per_head``: codes and zero/scale arrays."""
+    D = head_dim
+    return 2 * residual * D * bits // 8 + (residual // group) * D * 4 + residual * (D // group) * 4
+
+
+def step_bytes(q_len, r_start, heads, head_dim, bits, group, residual):
+    """Algorithmic bytes of one whole step done in one kernel, over a batch:
+    the decode's bytes over the window with the appended token in it (that
+    token is read from the new-token input instead of the window), writing
+    the new K and V rows into the window, and, for every sequence whose
+    window the append fills, the flush's writes (the window it quantizes is
+    the one the decode reads)."""
+    total = decode_bytes(q_len, np.asarray(r_start) + 1, heads, head_dim, bits, group)
+    for r in np.asarray(r_start):
+        total += heads * 2 * head_dim * 2
+        if int(r) + 1 == residual:
+            total += heads * flush_write_bytes_per_head(residual, head_dim, bits, group)
+    return int(total)
+
+
 def append_bytes_per_head(head_dim):
     """Algorithmic bytes of appending one token to one (sequence, head):
     read and write one fp16 K row and one fp16 V row."""

@@ -372,6 +372,18 @@ def test_decode_byte_model_per_head():
     assert wl.decode_bytes_per_head(0, 0, 128, 2, 32) == 768
 
 
+def test_step_byte_model():
+    # the Llama-2-7B-shaped layer, every window filled by the step's append:
+    # decode bytes + new K/V rows (2*128*2 per head) + flush writes per head
+    # (codes 2*128*128*2/8, K meta 4*128*4, V meta 128*4*4)
+    ql = np.full(8, 3968)
+    assert wl.step_bytes(ql, np.full(8, 127), 32, 128, 2, 32, 128) == \
+        256 * (447232 + 512 + 8192 + 2048 + 2048)
+    # a window the append does not fill: no flush bytes
+    assert wl.step_bytes(ql[:1], np.array([5]), 1, 128, 2, 32, 128) == \
+        wl.decode_bytes_per_head(3968, 6, 128, 2, 32) + 512
+
+
 # ----------------------------------------------------------------- direction
 
 def test_per_channel_keys_beat_per_token_keys_on_outlier_channels():
