@@ -26,13 +26,14 @@ constexpr int kD = 128;        // head_dim covered by the compiled kernels
 constexpr int kThreads = 256;  // 4 waves of 64
 // Decode shape and pipelining: waves per workgroup and workgroups per
 // compute unit (shared with the host-side work split), hence waves per SIMD;
-// sub-chunks whose loads are kept in flight per wave; whether waves raise
-// their issue priority while they are behind.
+// sub-chunks whose loads are kept in flight per wave; how waves set their
+// issue priority (0 never, 1 from their own progress fraction, 2 from their
+// lead over the slowest wave of the workgroup).
 #ifndef KIVI_DECODE_DEPTH
 #define KIVI_DECODE_DEPTH 2
 #endif
 #ifndef KIVI_DECODE_PRIORITY
-#define KIVI_DECODE_PRIORITY 1
+#define KIVI_DECODE_PRIORITY 2
 #endif
 constexpr int kDecodeWaves = kDecodeWavesPerWorkgroup;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
@@ -692,6 +693,7 @@ struct DecSmem {
     } mg;
   } u;
   int ticket;
+  int prog[kDecodeWaves];  // sub-chunks each wave has started (issue priority)
 };
 
 __device__ __forceinline__ void store_agent(float *p, float v) {
@@ -889,6 +891,27 @@ __device__ __forceinline__ void set_progress_priority(int done, int total) {
   if (lvl >= 3) __builtin_amdgcn_s_setprio(3);
   else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
   else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+// Issue priority from the wave's lead over the slowest wave of its
+// workgroup: each wave posts the number of sub-chunks it has started in
+// prog[wave]; the slowest gets 3, one less per sub-chunk of lead.  With the
+// fraction-based levels above the waves of a SIMD still drift a quarter of
+// their work apart (on 32 sub-chunks per wave, the younger four waves ended
+// 6 µs after the older four in a 50 µs compute-only run).  Priority only
+// orders issue, never results; an unwritten slot at the start (left over in
+// LDS) can only mis-set a priority until every wave has posted once.
+__device__ __forceinline__ void set_lead_priority(int *prog, int wv, int lane, int done) {
+  if (lane == 0) prog[wv] = done;
+  int v = lane < kDecodeWaves ? prog[lane] : 0x7fffffff;
+  v = min(v, (int)dppu<0xB1>((uint32_t)v));
+  v = min(v, (int)dppu<0x4E>((uint32_t)v));
+  v = min(v, (int)dppu<0x141>((uint32_t)v));
+  const int lead = done - __builtin_amdgcn_readlane(v, 0);
+  if (lead <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (lead == 1) __builtin_amdgcn_s_setprio(2);
+  else if (lead == 2) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
 }
 
@@ -1376,6 +1399,9 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
   for (int k = 0; k < kDecodeDepth; ++k) qs.issue(ring[k], k);
 
   auto &stg = sm.u.wave[wv];
+#if KIVI_DECODE_PRIORITY == 2
+  if (lane == 0) sm.prog[wv] = 0;
+#endif
   const half2_t hq = __builtin_bit_cast(half2_t, qraw);
   const float qs0 = (float)hq.x * a.qscale, qs1 = (float)hq.y * a.qscale;
   const float qf0 = qs0 * code_factor<BITS>((2 * lane) % C::CPW);
@@ -1441,7 +1467,9 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
   for (; c0 + kDecodeDepth <= qs.n; c0 += kDecodeDepth) {
 #pragma unroll
     for (int k = 0; k < kDecodeDepth; ++k) {
-#if KIVI_DECODE_PRIORITY
+#if KIVI_DECODE_PRIORITY == 2
+      set_lead_priority(sm.prog, wv, lane, c0 + k);
+#elif KIVI_DECODE_PRIORITY
       set_progress_priority(c0 + k, qs.n);
 #endif
       process_sub<BITS, G>(ring[k], qs.t0(c0 + k), ql, lane, qs0, qs1, qf0, qf1, stg.qp, stg.cz,
@@ -1456,7 +1484,9 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
 #pragma unroll
   for (int k = 0; k < kDecodeDepth - 1; ++k)
     if (c0 + k < qs.n) {
-#if KIVI_DECODE_PRIORITY
+#if KIVI_DECODE_PRIORITY == 2
+      set_lead_priority(sm.prog, wv, lane, c0 + k);
+#elif KIVI_DECODE_PRIORITY
       set_progress_priority(c0 + k, qs.n);
 #endif
       process_sub<BITS, G>(ring[k], qs.t0(c0 + k), ql, lane, qs0, qs1, qf0, qf1, stg.qp, stg.cz,
@@ -1477,18 +1507,24 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_ke
     if (sm.fin.l[x] > 0.0f) M = fmaxf(M, sm.fin.m[x]);
   float L = 0.0f, acc_out = 0.0f;
   if (M != -INFINITY) {
+    float ex[kDecodeWaves];
 #pragma unroll
     for (int x = 0; x < kDecodeWaves; ++x) {
-      const float e = sm.fin.l[x] > 0.0f ? exp2_fast(sm.fin.m[x] - M) : 0.0f;
-      L += e * sm.fin.l[x];
-      if (tid < kD && e != 0.0f) {
+      ex[x] = sm.fin.l[x] > 0.0f ? exp2_fast(sm.fin.m[x] - M) : 0.0f;
+      L += ex[x] * sm.fin.l[x];
+    }
+    // every wave published finite sums (zeros without tokens), so all are
+    // read at once instead of one wave's behind another's test
+    if (tid < kD) {
+#pragma unroll
+      for (int x = 0; x < kDecodeWaves; ++x) {
         float sa = 0.0f, sb = 0.0f;
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
           sa += sm.fin.acc[x][y][tid];
           sb += sm.fin.bias[x][y][tid / C::CPW];
         }
-        acc_out += e * fmaf(sa, code_factor<BITS>(tid % C::CPW), sb);
+        acc_out += ex[x] * fmaf(sa, code_factor<BITS>(tid % C::CPW), sb);
       }
     }
   }
