@@ -302,7 +302,7 @@ def main():
             f"status clean: {states_ok}")
 
     step_s = wall / K
-    one_kernel = kivi.decode_splits(base.dims) == 1
+    one_kernel = kivi.decode_step_kernels(base.dims) == 1
     qheads = Bt * H
     dec_bytes = wl.decode_bytes(w.q_len, r_start + 1, H, D, w.bits, cfg.group)
     achieved = dec_bytes / (decode_us * 1e-6) / 1e9
@@ -326,7 +326,7 @@ def main():
             "context": int((w.q_len + r_start + 1).max()),
             "quantized_tokens": int(w.q_len.max()), "window_tokens": int((r_start + 1).max()),
             "step": ("kivi_decode_step (append + decode + flush, "
-                     + ("one kernel" if kivi.decode_splits(base.dims) == 1 else "three kernels")
+                     + ("one kernel" if one_kernel else "three kernels")
                      + "), " + ("one HIP graph of all timed steps" if graph is not None
                                 else "eager launches")),
         },

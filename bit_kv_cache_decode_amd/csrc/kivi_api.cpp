@@ -68,6 +68,7 @@ DecodePlan decode_plan(const kivi_dims &d) {
     }
   }
   p.splits = best;
+  p.depth = bh * p.splits > kWorkgroupSlots ? 1 : 2;
   const long waves = (long)kDecodeWavesPerWorkgroup * p.splits;
   p.win_per_wave = (int)(((d.residual + waves - 1) / waves + 7) / 8 * 8);
   p.part_floats = 4 + (size_t)d.head_dim;
@@ -126,6 +127,12 @@ int kivi_decode_splits(const kivi_dims *dims) {
   const int rc = kivi::check_dims(dims);
   if (rc != KIVI_OK) return rc;
   return kivi::decode_plan(*dims).splits;
+}
+
+int kivi_decode_step_kernels(const kivi_dims *dims) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  return kivi::step_in_one_kernel(kivi::decode_plan(*dims)) ? 1 : 3;
 }
 
 int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache, const void *q, float *out,

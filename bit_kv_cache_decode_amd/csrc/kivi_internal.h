@@ -35,12 +35,20 @@ struct DecodePlan {
   int sub;           // quantized tokens per sub-chunk
   int splits;        // workgroups per (sequence, head)
   int win_per_wave;  // window tokens per wave (multiple of 8)
+  int depth;         // sub-chunks in flight per wave: 2 when the grid is at most one workgroup
+                     // per compute unit, else 1 (several workgroups then share a compute unit)
   size_t part_floats;     // floats of partial state per split (4 + D)
   size_t counters_off;    // byte offset of the per-(sequence, head) tickets
   size_t bytes;           // total workspace bytes
 };
 
 DecodePlan decode_plan(const kivi_dims &d);
+
+// Whether kivi_decode_step runs as the single whole-step kernel: it needs one
+// workgroup per (sequence, head), and holds many more registers than the
+// decode alone, so it only pays while the grid is one workgroup per compute
+// unit (depth 2).  Otherwise the step is the three kernels.
+inline bool step_in_one_kernel(const DecodePlan &p) { return p.splits == 1 && p.depth == 2; }
 
 // Kernel launchers (return a hipError_t value as int, 0 on success).
 int launch_append(const kivi_dims &d, const kivi_cache &c, const void *k_new,

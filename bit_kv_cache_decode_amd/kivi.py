@@ -22,7 +22,7 @@ ST_RESIDUAL_FULL, ST_CAPACITY, ST_BAD_LENGTH = 0x1, 0x2, 0x4
 
 # Every symbol the public header declares.
 EXPORTS = ("kivi_validate_dims", "kivi_append_kv", "kivi_flush_residual", "kivi_prefill",
-           "kivi_decode_workspace_bytes", "kivi_decode_splits", "kivi_decode_attn",
+           "kivi_decode_workspace_bytes", "kivi_decode_splits", "kivi_decode_step_kernels", "kivi_decode_attn",
            "kivi_decode_step", "kivi_strerror")
 
 
@@ -62,6 +62,7 @@ def lib():
         L.kivi_decode_workspace_bytes.argtypes = [P(Dims)]
         L.kivi_decode_workspace_bytes.restype = ctypes.c_size_t
         L.kivi_decode_splits.argtypes = [P(Dims)]
+        L.kivi_decode_step_kernels.argtypes = [P(Dims)]
         L.kivi_decode_attn.argtypes = [P(Dims), P(CacheStruct), V, V, ctypes.c_float, V,
                                        ctypes.c_size_t, V]
         L.kivi_decode_step.argtypes = [P(Dims), P(CacheStruct), V, V, V, V, ctypes.c_float, V,
@@ -94,6 +95,10 @@ def workspace_bytes(dims):
 
 def decode_splits(dims):
     return lib().kivi_decode_splits(ctypes.byref(dims))
+
+
+def decode_step_kernels(dims):
+    return lib().kivi_decode_step_kernels(ctypes.byref(dims))
 
 
 def _stream():

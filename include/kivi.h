@@ -166,6 +166,13 @@ size_t kivi_decode_workspace_bytes(const kivi_dims *dims);
 int kivi_decode_splits(const kivi_dims *dims);
 
 /*
+ * Number of kernels kivi_decode_step launches for these dims: 1 (the
+ * whole-step kernel) or 3 (append, decode, flush).  Negative error code for
+ * invalid or unsupported dims.
+ */
+int kivi_decode_step_kernels(const kivi_dims *dims);
+
+/*
  * Decode attention for one new query token per (sequence, head):
  *   out[b,h,:] = softmax(sm_scale * q[b,h,:] . Khat^T) . Vhat
  * over the q_len[b] dequantized tokens followed by the r_len[b] fp16 window
@@ -188,14 +195,19 @@ int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache,
 
 /*
  * One whole generation step: kivi_append_kv, then kivi_decode_attn, then
- * kivi_flush_residual, with the same results (outputs, cache contents,
- * lengths, status bits) as those three calls in that order, arguments as
- * there.  When one workgroup covers a whole (sequence, head) (see
- * kivi_decode_splits: 1) it is a single kernel: each workgroup appends its
- * (sequence, head)'s token, uses it from registers in the attention, and if
- * the window is then full quantizes it (re-reading it from the cache while
- * it is still in L2) and the last workgroup of the sequence commits the
- * lengths through cache->tickets.  Otherwise it launches the three kernels.
+ * kivi_flush_residual ([P1] section 3.1: append to the fp16 window, attend
+ * over quantized and window tokens, quantize the window once it holds R
+ * tokens), arguments as there.  The cache contents, lengths and status bits
+ * are exactly those of the three calls in that order; the output is theirs
+ * up to rounding (the summation order may differ).  When one workgroup
+ * covers a whole (sequence, head) (kivi_decode_splits: 1) and the grid is
+ * at most one workgroup per compute unit (batch * heads <= 256), it is a
+ * single kernel: each workgroup appends its (sequence, head)'s token, uses it
+ * from registers in the attention, and if the window is then full quantizes
+ * it (from the registers that hold it for the attention when R <= 128, else
+ * re-reading it), and the last workgroup of the sequence commits the lengths
+ * through cache->tickets.  Otherwise it launches the three kernels.
+ * Errors as for the three calls; KIVI_ENOSPC if workspace_bytes is too small.
  */
 int kivi_decode_step(const kivi_dims *dims, const kivi_cache *cache,
                      const void *k_new, const void *v_new, const void *q,

@@ -49,19 +49,20 @@ def test_validate_dims_codes():
     assert kivi.workspace_bytes(kivi.make_dims(8, 32, 64, 2, 32, 128, 4096)) == 0
 
 
-@pytest.mark.parametrize("dims,splits", [
-    ((1, 1, 128, 2, 32, 32, 256), 1),         # one workgroup does it all
-    ((8, 32, 128, 2, 32, 128, 4096), 1),      # one workgroup per (sequence, head) fills the chip
-    ((16, 40, 128, 2, 32, 128, 2048), 1),
-    ((64, 32, 128, 2, 32, 128, 8320), 1),     # many sequences: one workgroup each
-    ((1, 32, 128, 2, 128, 128, 131072), 8),   # long context: 8 workgroups per head
-    ((1, 32, 128, 4, 128, 128, 131072), 8),
-    ((1, 1, 128, 2, 32, 32, 0), 1),           # window only
-    ((1, 1, 128, 2, 32, 4096, 1 << 24), 64),  # capped at 64
+@pytest.mark.parametrize("dims,splits,step_kernels", [
+    ((1, 1, 128, 2, 32, 32, 256), 1, 1),         # one workgroup does it all
+    ((8, 32, 128, 2, 32, 128, 4096), 1, 1),      # one workgroup per (sequence, head) fills the chip
+    ((16, 40, 128, 2, 32, 128, 2048), 1, 3),     # more pairs than compute units
+    ((64, 32, 128, 2, 32, 128, 8320), 1, 3),     # many sequences: one workgroup each
+    ((1, 32, 128, 2, 128, 128, 131072), 8, 3),   # long context: 8 workgroups per head
+    ((1, 32, 128, 4, 128, 128, 131072), 8, 3),
+    ((1, 1, 128, 2, 32, 32, 0), 1, 1),           # window only
+    ((1, 1, 128, 2, 32, 4096, 1 << 24), 64, 3),  # capped at 64
 ])
-def test_decode_plan(dims, splits):
+def test_decode_plan(dims, splits, step_kernels):
     d = kivi.make_dims(*dims)
     assert kivi.decode_splits(d) == splits
+    assert kivi.decode_step_kernels(d) == step_kernels
     bh = dims[0] * dims[1]
     ws = kivi.workspace_bytes(d)
     # partial states (4 + head_dim floats per split) plus one ticket per

@@ -436,9 +436,10 @@ def test_decode_step_flush_in_kernel_matches_oracle(bits, G, R):
 @pytest.mark.parametrize("number", [2, 4])
 def test_decode_step_matches_three_calls_full_workloads(number):
     """The Llama-2-7B-shaped layer (every window fills and is flushed in the
-    step) and a ragged batch (a mix of flushed and not): one kernel per step
-    (one workgroup per (sequence, head)), identical to the three calls."""
-    w = workload(number, batch=16 if number == 4 else None)
+    step) and a ragged batch of 8 (a mix of flushed and not): one kernel per
+    step (one workgroup per (sequence, head), 256 workgroups), identical to
+    the three calls."""
+    w = workload(number, batch=8 if number == 4 else None)
     cfg = w.config
     rl = np.minimum(w.r_len, cfg.residual - 1) if number == 4 else w.r_len - 1
     rng = np.random.default_rng(5)
@@ -453,6 +454,25 @@ def test_decode_step_matches_three_calls_full_workloads(number):
     _assert_same_step(out_a, out_b, sa, sb)
     if number == 2:
         assert (sb["r_len"] == 0).all() and (sb["q_len"] == w.q_len + 128).all()
+
+
+def test_decode_step_on_a_large_grid_matches_three_calls():
+    """More (sequence, head) pairs than compute units (the 13B layer, 640):
+    the decode runs with one sub-chunk in flight per wave so that several
+    workgroups share a compute unit, and decode_step launches the three
+    kernels; the result is that of the three calls and the window flushes."""
+    w = workload(3)
+    cfg = w.config
+    rl = w.r_len - 1
+    rng = np.random.default_rng(8)
+    kn = torch.from_numpy(rng.standard_normal((len(rl), cfg.heads, 128), np.float32)
+                          .astype(np.float16)).cuda()
+    vn = torch.from_numpy(rng.standard_normal((len(rl), cfg.heads, 128), np.float32)
+                          .astype(np.float16)).cuda()
+    q = torch.from_numpy(w.q).cuda()
+    out_a, out_b, sa, sb = _step_both(lambda: gpu_cache(w, r_len=rl), kn, vn, q, cfg.sm_scale)
+    _assert_same_step(out_a, out_b, sa, sb)
+    assert (sb["r_len"] == 0).all() and (sb["q_len"] == w.q_len + 128).all()
 
 
 def test_decode_step_with_split_heads_uses_three_kernels():
