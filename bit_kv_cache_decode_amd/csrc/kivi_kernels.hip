@@ -1452,13 +1452,13 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 2 * kDecodeWavesPerSim
 
   if constexpr (FUSED) {
     if (early) {
+      // the window's attention and the flush's value words and key
+      // partials, which need no other wave; the key groups (across waves)
+      // are finished after the workgroup's combine barrier
       window();
-      auto &rf = fused_flush_smem<BITS, G>().reg;
-      if (wsteps > 0) flush_regs_values<BITS, G>(ea, rf, wpf, wsteps, tile0, ws.begin, wv, w, slot);
-      __syncthreads();
-      flush_regs_params<BITS, G>(ea, rf, tile0, a.R, a.win_per_wave, tid);
-      __syncthreads();
-      if (wsteps > 0) flush_regs_keys<BITS, G>(ea, rf, wpf, wsteps, tile0, ws.begin, w, slot);
+      if (wsteps > 0)
+        flush_regs_values<BITS, G>(ea, fused_flush_smem<BITS, G>().reg, wpf, wsteps, tile0,
+                                   ws.begin, wv, w, slot);
     }
   }
 
@@ -1533,7 +1533,12 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 2 * kDecodeWavesPerSim
   if (S == 1) {  // the workgroup saw every token: finish here
     if (tid < kD) a.out[bh * kD + tid] = L > 0.0f ? acc_out / L : 0.0f;
     if constexpr (FUSED) {
-      if (flush && !early) {
+      if (early) {
+        auto &rf = fused_flush_smem<BITS, G>().reg;
+        flush_regs_params<BITS, G>(ea, rf, tile0, a.R, a.win_per_wave, tid);
+        __syncthreads();
+        if (wsteps > 0) flush_regs_keys<BITS, G>(ea, rf, wpf, wsteps, tile0, ws.begin, w, slot);
+      } else if (flush) {
         // longer windows: read again (mostly L2 hits, this workgroup has
         // just read them) and quantized through LDS
         flush_window<BITS, G, G, kDecodeThreads>(ea, bh, ql0, tid, fused_flush_smem<BITS, G>().lds,
