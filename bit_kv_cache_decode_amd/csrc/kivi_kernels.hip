@@ -247,15 +247,6 @@ __device__ __forceinline__ bool flush_ok(int ql, int rl, int G, int R, int cap) 
   return rl == R && ql >= 0 && (ql % G) == 0 && ql + R <= cap;
 }
 
-template <int G>
-__device__ __forceinline__ void load_tile(half_t (*xs)[kD + 8], const half_t *src) {
-  for (int i = threadIdx.x; i < G * (kD / 8); i += kThreads) {
-    const int t = i / (kD / 8), c = i % (kD / 8);
-    *reinterpret_cast<uint4 *>(&xs[t][c * 8]) =
-        *reinterpret_cast<const uint4 *>(src + (size_t)t * kD + c * 8);
-  }
-}
-
 // Prefill: one workgroup quantizes one tile of G tokens of one
 // (sequence, head): keys per channel over the G tokens, values per token
 // over G channels, and packs both into the tiled code layout.  Both tiles

@@ -74,6 +74,17 @@ def test_llama2_13b_layer_all_heads():
         assert_head_bit_exact(head_buffers(c, b, h), oracle_head(w, b, h), 32)
 
 
+def test_llama2_13b_layer_at_4_bits_sampled_heads():
+    """640 (sequence, head) pairs at B=4: the decode with one sub-chunk in
+    flight per wave (several workgroups per compute unit) at 4 bits."""
+    w = workload(3, bits=4)
+    c = gpu_cache(w)
+    rng = np.random.default_rng(413)
+    heads = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, 16, 24),
+                                                     rng.integers(0, 40, 24))} | {(15, 39)})
+    _check_heads(c, w, heads)
+
+
 def test_llama2_13b_flush_of_full_window():
     """Flush of a full 128-token window per head: bit-exact against the
     oracle's bulk quantization of the same 2048 tokens, every head."""
@@ -473,6 +484,48 @@ def test_decode_step_on_a_large_grid_matches_three_calls():
     out_a, out_b, sa, sb = _step_both(lambda: gpu_cache(w, r_len=rl), kn, vn, q, cfg.sm_scale)
     _assert_same_step(out_a, out_b, sa, sb)
     assert (sb["r_len"] == 0).all() and (sb["q_len"] == w.q_len + 128).all()
+
+
+def test_decode_step_streaming_matches_oracle():
+    """Consecutive whole steps in one kernel each, over two sequences whose
+    windows fill at different steps (one flush per sequence along the way):
+    every step's output against the oracle's append, decode, flush, and the
+    final buffers bit for bit; the tickets are left at zero after each."""
+    rng = np.random.default_rng(4242)
+    B, H, D, G, R, bits = 2, 3, 128, 32, 64, 2
+    cap = 4 * G + R
+    n0 = np.array([G + R - 3, 2 * G + R - 7])       # windows 3 and 7 short of full
+    res = np.array([R - 3, R - 7])
+    T = int(n0.max())
+    k = rng.standard_normal((B, H, T, D), np.float32)
+    k[..., 5] *= 40.0                                # an outlier key channel
+    k = k.astype(np.float16)
+    v = rng.standard_normal((B, H, T, D), np.float32).astype(np.float16)
+    c = kivi.KiviCache(B, H, D, bits, G, R, cap)
+    kivi.prefill(c, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                 torch.from_numpy(n0.astype(np.int32)).cuda(),
+                 torch.from_numpy(res.astype(np.int32)).cuda())
+    assert kivi.decode_step_kernels(c.dims) == 1
+    ref = ocache.Cache(B, H, D, bits, G, R, cap)
+    ref.prefill(k, v, n0, res)
+    ws = kivi.new_workspace(c.dims)
+    for step in range(10):
+        kn = rng.standard_normal((B, H, D), np.float32).astype(np.float16)
+        vn = rng.standard_normal((B, H, D), np.float32).astype(np.float16)
+        q = (rng.standard_normal((B, H, D), np.float32) / np.sqrt(D)).astype(np.float16)
+        out = kivi.decode_step(c, torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(),
+                               torch.from_numpy(q).cuda(), 1.0, workspace=ws)
+        ref.append(kn, vn)
+        expect = ref.decode(q, 1.0)
+        ref.flush()
+        torch.cuda.synchronize()
+        assert_within_tolerance(out.cpu().numpy(), expect, f"step {step}")
+        assert not c.tickets.any() and c.status_bits() == 0
+    assert np.array_equal(c.q_len.cpu().numpy(), ref.q_len)
+    assert np.array_equal(c.r_len.cpu().numpy(), ref.r_len)
+    for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+        assert np.array_equal(getattr(c, name).cpu().numpy().view(np.uint8),
+                              getattr(ref, name).view(np.uint8)), name
 
 
 def test_decode_step_with_split_heads_uses_three_kernels():
