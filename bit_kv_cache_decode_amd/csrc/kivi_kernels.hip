@@ -596,14 +596,17 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
 
 // ----------------------------------------------------------------- decode
 //
-// Grid (splits, heads, batch), kDecodeWaves (8) waves per workgroup, one
-// workgroup per compute unit, two waves per SIMD.  The 8 * splits waves of
-// one (sequence, head) share its work: quantized sub-chunks of 64 (B=2) or
-// 32 (B=4) tokens are dealt round-robin to the waves, and each wave also
-// takes an equal slice of the fp16 window tokens, computed last.  Every
-// wave works on its own (no block barrier until the end), keeps
-// kDecodeDepth sub-chunks of loads in flight, and raises its issue priority
-// while it is behind the other wave of its SIMD; every lane keeps its own
+// Grid (splits, heads, batch), kDecodeWaves (8) waves per workgroup: one
+// workgroup per compute unit (two waves per SIMD) with two sub-chunks of
+// loads in flight per wave, or, on grids larger than the chip, one sub-chunk
+// in flight and a register footprint small enough for two or three
+// workgroups per compute unit.  The 8 * splits waves of one (sequence,
+// head) share its work: quantized sub-chunks of 64 (B=2) or 32 (B=4) tokens
+// are dealt round-robin to the waves, and each wave also takes an equal
+// slice of the fp16 window tokens, computed last.  Every wave works on its
+// own (no block barrier until the end) and sets its issue priority from
+// its lead over the slowest wave of its workgroup (the slowest issues
+// first); every lane keeps its own
 // online-softmax state (running max, sum, value sums) for the tokens it
 // sees.  At the end the lanes and waves of the workgroup are combined in
 // LDS (max m, sum l, unnormalised value sums, in log2 units).  With one
