@@ -17,6 +17,8 @@ path computes, written from the pages' definitions:
   split (partial) form and its log-sum-exp merge.
 * ``cache``      -- the streaming cache (prefill, append, flush, decode) in the
   library's documented buffer layouts, one (sequence, head) at a time.
+* ``axis_ablation`` -- the four choices of grouping axis for keys and values
+  and the key, score and output errors each gives (analysis, not parity).
 
 Precision: the quantizer runs the fixed fp32 operation sequence stated in
 ``quantizer``; attention runs in fp64 on the exactly dequantized values.
@@ -26,4 +28,4 @@ fix (hand-worked cases, brute force, closed forms, invariants); none is
 "parity unpinned".
 """
 
-from . import attention, cache, packing, quantizer  # noqa: F401
+from . import attention, axis_ablation, cache, packing, quantizer  # noqa: F401
