@@ -54,8 +54,8 @@ def test_validate_dims_codes():
     ((8, 32, 128, 2, 32, 128, 4096), 1, 1),      # one workgroup per (sequence, head) fills the chip
     ((16, 40, 128, 2, 32, 128, 2048), 1, 3),     # more pairs than compute units
     ((64, 32, 128, 2, 32, 128, 8320), 1, 3),     # many sequences: one workgroup each
-    ((1, 32, 128, 2, 128, 128, 131072), 8, 3),   # long context: 8 workgroups per head
-    ((1, 32, 128, 4, 128, 128, 131072), 8, 3),
+    ((1, 32, 128, 2, 128, 128, 131072), 16, 3),  # long context: 16 workgroups per head, two per CU
+    ((1, 32, 128, 4, 128, 128, 131072), 16, 3),
     ((1, 1, 128, 2, 32, 32, 0), 1, 1),           # window only
     ((1, 1, 128, 2, 32, 4096, 1 << 24), 64, 3),  # capped at 64
 ])
