@@ -56,6 +56,8 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch steps eagerly instead of a graph")
+    p.add_argument("--no-stream", action="store_true",
+                   help="skip the stream-read ceiling (kivi_stream_read) measurement")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="after the run, copy a buffer of this many MiB once (a known-size "
                         "reference dispatch for scaling hardware byte counters)")
@@ -147,6 +149,46 @@ def cpu_baseline(w, budget_s):
                       f"over the {len(pairs)} pairs of the same workload, numpy with 1 BLAS "
                       f"thread, {spent:.1f} s of timed work",
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def stream_ceiling(nbytes, steps):
+    """The HBM read rate this device sustains for the decode's byte count:
+    kivi_stream_read over buffers of nbytes (rounded up to 16), rotated among
+    enough copies that none is re-read from the 256 MB Infinity Cache, timed
+    like the decode (a HIP graph of `steps` launches between HIP events) at
+    several grid sizes; the fastest grid gives the ceiling."""
+    import torch
+    from bit_kv_cache_decode_amd import kivi
+
+    n16 = (int(nbytes) + 15) // 16
+    n_rot = max(2, -(-int(1.2e9) // (n16 * 16)))
+    bufs = [torch.full((n16 * 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(n_rot)]
+    by_wg = {}
+    for wg in (256, 512, 1024, 2048):
+        sink = torch.empty((wg * 8,), dtype=torch.int32, device="cuda")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                kivi.stream_read(bufs[i % n_rot], wg, sink)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        by_wg[wg] = 1e3 * e0.elapsed_time(e1) / steps
+        del g, sink
+    best = min(by_wg, key=by_wg.get)
+    us = by_wg[best]
+    del bufs
+    torch.cuda.empty_cache()
+    return {"kernel": "stream_read_kernel (kivi_stream_read)", "bytes": n16 * 16,
+            "workgroups": best, "us": us, "GBps": n16 * 16 / (us * 1e-6) / 1e9,
+            "frac_of_peak": n16 * 16 / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+            "us_by_workgroups": {str(k): round(v, 3) for k, v in by_wg.items()},
+            "rotated_buffers": n_rot}
 
 
 def main():
@@ -301,6 +343,25 @@ def main():
         log(f"WARNING: outputs match the warmup's: graph {replay_ok}, phased {eager_ok}; "
             f"status clean: {states_ok}")
 
+    # ---- per-call decode durations: HIP events around each of `calls`
+    # separate launches, every copy back in the decode phase's state (its
+    # starting lengths plus the appended token, which the window still holds)
+    for c in copies:
+        c.q_len.copy_(q0)
+        c.r_len.copy_(r0 + 1)
+    torch.cuda.synchronize()
+    calls = max(200, K)
+    pc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for i, (e0, e1) in enumerate(pc):
+        e0.record()
+        kivi.decode_attn(copies[i % n_copies], q, cfg.sm_scale, out=outs[i % n_copies], workspace=ws)
+        e1.record()
+    torch.cuda.synchronize()
+    per_call = np.array([1e3 * e0.elapsed_time(e1) for e0, e1 in pc])
+    reset()
+    torch.cuda.synchronize()
+
     step_s = wall / K
     one_kernel = kivi.decode_step_kernels(base.dims) == 1
     qheads = Bt * H
@@ -332,6 +393,9 @@ def main():
         },
         "decode": {"us": decode_us, "query_heads_per_s": qheads / (decode_us * 1e-6),
                    "algorithmic_bytes": int(dec_bytes), "GBps": achieved},
+        "decode_per_call_us": {"median": float(np.median(per_call)),
+                               "p10": float(np.percentile(per_call, 10)),
+                               "p90": float(np.percentile(per_call, 90)), "calls": calls},
         "phased_ms_per_step": eager_wall / K * 1e3,
         "append_us": append_us,
         "flush_us": flush_us,
@@ -350,6 +414,10 @@ def main():
             "GBps": sb / (step_event_us * 1e-6) / 1e9,
             "frac": sb / (step_event_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
             "traffic": measured_traffic(cfg.name, "step_bytes_per_launch")}
+    if not args.no_stream:
+        sr = stream_ceiling(dec_bytes, K)
+        result["stream_read"] = sr
+        result["decode_frac_of_stream_read"] = achieved / sr["GBps"]
     if args.copy_mb:
         # an elementwise kernel (not a DMA-engine memcpy, which no counter sees)
         src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device="cuda")

@@ -18,10 +18,8 @@ constexpr long kWorkgroupSlots = 256L * kDecodeWorkgroupsPerCU;
 // units of one sub-chunk per wave, for choosing the split count.
 constexpr double kWorkgroupOverhead = 2.0;
 constexpr int kMaxSplits = 64;
-// Sub-chunks per wave, after doubling the split count, from which a
-// one-workgroup-per-compute-unit grid is split twice as finely (below).
-constexpr long kLongStreamSubChunks = 16;
 constexpr int kMaxResidual = 4096;
+constexpr int32_t kMaxStreamWorkgroups = 1 << 20;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -70,18 +68,6 @@ DecodePlan decode_plan(const kivi_dims &d) {
       best_cost = cost;
     }
   }
-  // A grid of at most one workgroup per compute unit whose waves each stream
-  // many sub-chunks runs faster split twice as finely at depth 1: two
-  // workgroups then share a compute unit (four waves per SIMD instead of
-  // two), which hides more of the memory latency behind the dequant
-  // arithmetic.  Measured on batch 1 x 32 heads x 131072 tokens: 84 -> 79 us
-  // at B=2, 121 -> 112 us at B=4 (32 and 64 sub-chunks per wave before the
-  // doubling).  Short streams lose to the extra merge (Llama-2-7B layer at 2
-  // splits: 28.1 against 26.8 us, 8 sub-chunks per wave), as do three or
-  // more workgroups per compute unit.
-  if (bh * best <= kWorkgroupSlots && 2 * best <= kMaxSplits &&
-      nsub >= (long)kDecodeWavesPerWorkgroup * 2 * best * kLongStreamSubChunks)
-    best *= 2;
   p.splits = best;
   p.depth = bh * p.splits > kWorkgroupSlots ? 1 : 2;
   const long waves = (long)kDecodeWavesPerWorkgroup * p.splits;
@@ -174,6 +160,13 @@ int kivi_decode_step(const kivi_dims *dims, const kivi_cache *cache, const void 
   if (workspace_bytes < p.bytes) return KIVI_ENOSPC;
   return kivi::hip_rc(kivi::launch_decode_step(*dims, *cache, p, k_new, v_new, q, out, sm_scale,
                                                workspace, stream));
+}
+
+int kivi_stream_read(const void *src, size_t bytes, int32_t workgroups, uint32_t *sink,
+                     void *stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 || ((uintptr_t)src) % 16) return KIVI_EINVAL;
+  if (workgroups < 1 || workgroups > kivi::kMaxStreamWorkgroups) return KIVI_EINVAL;
+  return kivi::hip_rc(kivi::launch_stream_read(src, bytes, workgroups, sink, stream));
 }
 
 const char *kivi_strerror(int code) {

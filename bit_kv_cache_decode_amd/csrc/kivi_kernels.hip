@@ -1595,6 +1595,41 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 2 * kDecodeWavesPerSim
     __hip_atomic_store(a.tickets + bh * kTicketStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------ measurement: stream read
+// Reads a buffer once with 16-byte loads and folds it into one word per wave:
+// the HBM read rate this chip sustains for a given size and grid, the
+// ceiling the decode's rate is compared with.  Workgroup i streams its own
+// contiguous slice (as a decode workgroup streams its (sequence, head)),
+// kStreamUnroll loads in flight per lane, the lanes of a wave on consecutive
+// 16-byte pieces.
+constexpr int kStreamThreads = 512;
+constexpr int kStreamUnroll = 8;
+
+__global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4 *src, size_t n16,
+                                                                     size_t per_wg,
+                                                                     uint32_t *sink) {
+  const size_t begin = (size_t)blockIdx.x * per_wg;
+  const size_t end = begin < n16 ? min(n16, begin + per_wg) : begin;
+  uint32_t x = 0;
+  size_t i = begin + threadIdx.x;
+  // every index of a round is below end: the largest is i + (U - 1) * T
+  for (; i + (size_t)(kStreamUnroll - 1) * kStreamThreads < end;
+       i += (size_t)kStreamUnroll * kStreamThreads) {
+    uint4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = src[i + (size_t)u * kStreamThreads];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < end; i += kStreamThreads) {
+    const uint4 v = src[i];
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off);
+  if ((threadIdx.x & 63) == 0) sink[(size_t)blockIdx.x * (kStreamThreads / 64) + threadIdx.x / 64] = x;
+}
+
 template <int BITS, int G>
 int launch_encode_t(const EncodeArgs &ea, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((encode_kernel<BITS, G>), grid, dim3(kThreads), 0, st, ea);
@@ -1742,6 +1777,16 @@ int launch_decode_any(const kivi_dims &d, const DecodeArgs &da, const EncodeArgs
 }
 
 }  // namespace
+
+int launch_stream_read(const void *src, size_t bytes, int workgroups, uint32_t *sink,
+                       void *stream) {
+  const size_t n16 = bytes / 16;
+  const size_t per_wg = (n16 + (size_t)workgroups - 1) / (size_t)workgroups;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(kStreamThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4 *>(src), n16,
+                     per_wg, sink);
+  return (int)hipGetLastError();
+}
 
 int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, const void *q,
                   float *out, float sm_scale, void *workspace, void *stream) {

@@ -23,7 +23,7 @@ ST_RESIDUAL_FULL, ST_CAPACITY, ST_BAD_LENGTH = 0x1, 0x2, 0x4
 # Every symbol the public header declares.
 EXPORTS = ("kivi_validate_dims", "kivi_append_kv", "kivi_flush_residual", "kivi_prefill",
            "kivi_decode_workspace_bytes", "kivi_decode_splits", "kivi_decode_step_kernels", "kivi_decode_attn",
-           "kivi_decode_step", "kivi_strerror")
+           "kivi_decode_step", "kivi_stream_read", "kivi_strerror")
 
 
 class Dims(ctypes.Structure):
@@ -67,6 +67,7 @@ def lib():
                                        ctypes.c_size_t, V]
         L.kivi_decode_step.argtypes = [P(Dims), P(CacheStruct), V, V, V, V, ctypes.c_float, V,
                                        ctypes.c_size_t, V]
+        L.kivi_stream_read.argtypes = [V, ctypes.c_size_t, I32, V, V]
         L.kivi_strerror.argtypes = [ctypes.c_int]
         L.kivi_strerror.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -247,3 +248,16 @@ def decode_step(cache, k_new, v_new, q, sm_scale, out=None, workspace=None):
                                   ctypes.c_float(sm_scale), workspace.data_ptr(),
                                   ctypes.c_size_t(nbytes), _stream()), "kivi_decode_step")
     return out
+
+
+def stream_read(src, workgroups, sink=None):
+    """Read the contiguous GPU tensor `src` once (kivi_stream_read, a
+    measurement aid); returns the sink tensor (int32 [workgroups * 8])."""
+    if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    if sink is None:
+        sink = torch.empty((workgroups * 8,), dtype=torch.int32, device=src.device)
+    _need(sink, torch.int32, (workgroups * 8,), "sink")
+    _check(lib().kivi_stream_read(src.data_ptr(), ctypes.c_size_t(src.numel() * src.element_size()),
+                                  int(workgroups), sink.data_ptr(), _stream()), "kivi_stream_read")
+    return sink

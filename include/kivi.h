@@ -214,6 +214,21 @@ int kivi_decode_step(const kivi_dims *dims, const kivi_cache *cache,
                      float *out, float sm_scale, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/*
+ * Measurement aid, not a step of the method: reads `bytes` bytes of device
+ * memory at `src` once with 16-byte loads and writes one XOR fold per wave
+ * to `sink`, so that its duration gives the HBM read rate the device
+ * sustains for that size, the ceiling against which the decode's achieved
+ * bandwidth is also reported.  `workgroups` 512-thread workgroups each
+ * stream one contiguous slice of about bytes / workgroups.
+ *   src   device, 16-byte aligned; bytes a non-zero multiple of 16
+ *   sink  device uint32 [workgroups * 8] (written; the values mean nothing)
+ * Returns KIVI_EINVAL for a null pointer, a misaligned or empty buffer, or
+ * workgroups outside [1, 2^20].  Asynchronous on `stream`; allocates nothing.
+ */
+int kivi_stream_read(const void *src, size_t bytes, int32_t workgroups,
+                     uint32_t *sink, void *stream);
+
 /* Static description of a return code. */
 const char *kivi_strerror(int code);
 

@@ -54,8 +54,8 @@ def test_validate_dims_codes():
     ((8, 32, 128, 2, 32, 128, 4096), 1, 1),      # one workgroup per (sequence, head) fills the chip
     ((16, 40, 128, 2, 32, 128, 2048), 1, 3),     # more pairs than compute units
     ((64, 32, 128, 2, 32, 128, 8320), 1, 3),     # many sequences: one workgroup each
-    ((1, 32, 128, 2, 128, 128, 131072), 16, 3),  # long context: 16 workgroups per head, two per CU
-    ((1, 32, 128, 4, 128, 128, 131072), 16, 3),
+    ((1, 32, 128, 2, 128, 128, 131072), 8, 3),   # long context: 8 workgroups per head
+    ((1, 32, 128, 4, 128, 128, 131072), 8, 3),
     ((1, 1, 128, 2, 32, 32, 0), 1, 1),           # window only
     ((1, 1, 128, 2, 32, 4096, 1 << 24), 64, 3),  # capped at 64
 ])
@@ -91,5 +91,15 @@ def test_entry_points_reject_bad_arguments_without_a_device():
                               fake, ctypes.c_size_t(need), None) == kivi.KIVI_EINVAL
     assert L.kivi_decode_attn(ctypes.byref(d), ctypes.byref(cs), None, fake, ctypes.c_float(1.0),
                               fake, ctypes.c_size_t(need), None) == kivi.KIVI_EINVAL
+    # the stream-read measurement aid: null, empty, unaligned or oddly sized
+    # buffers and workgroup counts outside [1, 2^20]
+    sz = ctypes.c_size_t
+    assert L.kivi_stream_read(None, sz(1024), 4, fake, None) == kivi.KIVI_EINVAL
+    assert L.kivi_stream_read(fake, sz(1024), 4, None, None) == kivi.KIVI_EINVAL
+    assert L.kivi_stream_read(fake, sz(0), 4, fake, None) == kivi.KIVI_EINVAL
+    assert L.kivi_stream_read(fake, sz(1000), 4, fake, None) == kivi.KIVI_EINVAL
+    assert L.kivi_stream_read(ctypes.c_void_p(0x1008), sz(1024), 4, fake, None) == kivi.KIVI_EINVAL
+    assert L.kivi_stream_read(fake, sz(1024), 0, fake, None) == kivi.KIVI_EINVAL
+    assert L.kivi_stream_read(fake, sz(1024), (1 << 20) + 1, fake, None) == kivi.KIVI_EINVAL
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(L.kivi_strerror(code), bytes)
