@@ -68,10 +68,10 @@ def _exact_nearest(x, mn, s, bits):
     return best[0], tie_gap
 
 
-@pytest.mark.parametrize("bits", [2, 4])
-def test_quantizer_matches_exact_brute_force(bits):
+@pytest.mark.parametrize("bits,n_groups", [(2, 400), (4, 400), (8, 60)])
+def test_quantizer_matches_exact_brute_force(bits, n_groups):
     rng = np.random.default_rng(7 + bits)
-    n_groups, n = 400, 16
+    n = 16
     scale = rng.choice([1e-3, 1.0, 30.0, 300.0], size=(n_groups, 1))
     x = (rng.standard_normal((n_groups, n)) * scale).astype(np.float16)
     x[::7, 3] *= np.float16(40.0)                       # outliers inside groups
@@ -87,7 +87,7 @@ def test_quantizer_matches_exact_brute_force(bits):
     assert near_ties < n_groups * n // 100
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_error_at_most_half_step(bits):
     rng = np.random.default_rng(11)
     x = (rng.standard_normal((2000, 32)) * rng.choice([0.01, 1, 50], (2000, 1))).astype(np.float16)
@@ -100,7 +100,7 @@ def test_error_at_most_half_step(bits):
     assert normal.mean() > 0.99
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_min_maps_to_zero_and_max_to_top_code(bits):
     rng = np.random.default_rng(5)
     x = rng.standard_normal((500, 32)).astype(np.float16)
@@ -114,7 +114,7 @@ def test_min_maps_to_zero_and_max_to_top_code(bits):
 
 def test_constant_groups_reconstruct_exactly():
     x = np.repeat(np.array([[-3.5], [0.0], [7.25], [65504.0]], np.float16), 32, axis=1)
-    for bits in (2, 4):
+    for bits in (2, 4, 8):
         codes, zero, step = oq.quantize_groups(x, bits)
         assert np.all(codes == 0) and np.all(step == 0)
         xhat = oq.dequantize_values(codes, zero[:, None], step[:, None], 32)
@@ -124,7 +124,7 @@ def test_constant_groups_reconstruct_exactly():
 def test_step_formula_is_range_over_levels():
     rng = np.random.default_rng(3)
     x = rng.standard_normal((300, 32)).astype(np.float16)
-    for bits in (2, 4):
+    for bits in (2, 4, 8):
         _, _, step = oq.quantize_groups(x, bits)
         rngv = x.max(1).astype(np.float64) - x.min(1).astype(np.float64)
         # fp16 step within half an fp16 ulp (plus fp32 rounding) of range / (2^B - 1)
@@ -153,7 +153,7 @@ def test_key_and_value_axes_are_transposes():
     """A key tile [G, D] quantized per channel equals the transposed tile
     [D, G] quantized per token with group G (one group per row)."""
     rng = np.random.default_rng(21)
-    for G, bits in [(32, 2), (128, 2), (32, 4), (64, 4)]:
+    for G, bits in [(32, 2), (128, 2), (32, 4), (64, 4), (32, 8), (128, 8)]:
         tile = rng.standard_normal((G, 128)).astype(np.float16)
         tile[:, 5] *= np.float16(60)
         ck, zk, sk = oq.quantize_keys(tile, G, bits)
@@ -191,7 +191,7 @@ def test_packing_hand_cases(golden_dir):
         assert np.array_equal(opack.unpack_tiles(packed, bits), codes)
 
 
-@pytest.mark.parametrize("bits,G", [(2, 32), (2, 128), (4, 32), (4, 128)])
+@pytest.mark.parametrize("bits,G", [(2, 32), (2, 128), (4, 32), (4, 128), (8, 32), (8, 128)])
 def test_pack_unpack_round_trip(bits, G):
     rng = np.random.default_rng(bits * G)
     codes = rng.integers(0, 2 ** bits, size=(2 * G, 128), dtype=np.uint8)
@@ -209,7 +209,7 @@ def _small_kv(rng, n, D=128, outlier=True):
     return k.astype(np.float16), rng.standard_normal((n, D)).astype(np.float16)
 
 
-@pytest.mark.parametrize("bits,G,R", [(2, 32, 128), (2, 32, 32), (4, 128, 128), (2, 64, 128)])
+@pytest.mark.parametrize("bits,G,R", [(2, 32, 128), (2, 32, 32), (4, 128, 128), (2, 64, 128), (8, 32, 64)])
 def test_streaming_equals_bulk(bits, G, R):
     """Token-by-token appends with flushes at R give the same buffers as one
     bulk prefill of the same tokens (tutorial section 3.1 streaming rule)."""
@@ -282,7 +282,7 @@ def test_attention_closed_form():
     assert abs(out[0] - 4.0) < 1e-15
 
 
-@pytest.mark.parametrize("bits,G", [(2, 4), (4, 8), (2, 8)])
+@pytest.mark.parametrize("bits,G", [(2, 4), (4, 8), (2, 8), (8, 4)])
 def test_attention_matches_textbook_loops(bits, G):
     rng = np.random.default_rng(40 + bits + G)
     D, L = 16, 48
