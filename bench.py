@@ -381,7 +381,8 @@ def main():
         "dtype": "fp32",
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}: {cfg.description}",
+            "workload": f"{cfg.name}: {cfg.description}"
+                        + (f", run at B={w.bits}" if w.bits != cfg.bits else ""),
             "batch": Bt, "heads": H, "head_dim": D, "bits": w.bits, "group": cfg.group,
             "residual": cfg.residual,
             "context": int((w.q_len + r_start + 1).max()),

@@ -88,7 +88,7 @@ int kivi_validate_dims(const kivi_dims *d) {
   if (d->batch <= 0 || d->heads <= 0 || d->head_dim <= 0 || d->group <= 0 || d->residual <= 0 ||
       d->capacity < 0)
     return KIVI_EINVAL;
-  if (d->bits != 2 && d->bits != 4) return KIVI_EINVAL;
+  if (d->bits != 2 && d->bits != 4 && d->bits != 8) return KIVI_EINVAL;
   if (d->head_dim % d->group || d->residual % d->group || d->capacity % d->group)
     return KIVI_EINVAL;
   if ((d->head_dim * d->bits) % 32) return KIVI_EINVAL;
@@ -133,7 +133,7 @@ int kivi_decode_splits(const kivi_dims *dims) {
 int kivi_decode_step_kernels(const kivi_dims *dims) {
   const int rc = kivi::check_dims(dims);
   if (rc != KIVI_OK) return rc;
-  return kivi::step_in_one_kernel(kivi::decode_plan(*dims)) ? 1 : 3;
+  return kivi::step_in_one_kernel(*dims, kivi::decode_plan(*dims)) ? 1 : 3;
 }
 
 int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache, const void *q, float *out,

@@ -47,8 +47,11 @@ DecodePlan decode_plan(const kivi_dims &d);
 // Whether kivi_decode_step runs as the single whole-step kernel: it needs one
 // workgroup per (sequence, head), and holds many more registers than the
 // decode alone, so it only pays while the grid is one workgroup per compute
-// unit (depth 2).  Otherwise the step is the three kernels.
-inline bool step_in_one_kernel(const DecodePlan &p) { return p.splits == 1 && p.depth == 2; }
+// unit (depth 2), and is not compiled for B = 8 (four channels per lane).
+// Otherwise the step is the three kernels.
+inline bool step_in_one_kernel(const kivi_dims &d, const DecodePlan &p) {
+  return p.splits == 1 && p.depth == 2 && d.bits != 8;
+}
 
 // Kernel launchers (return a hipError_t value as int, 0 on success).
 int launch_append(const kivi_dims &d, const kivi_cache &c, const void *k_new,

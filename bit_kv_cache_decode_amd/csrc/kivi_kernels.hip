@@ -17,6 +17,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kivi_internal.h"
 
 namespace kivi {
@@ -57,15 +59,18 @@ __device__ __forceinline__ float dpp(float v) {
       float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over aligned groups of N consecutive lanes (N in 2, 4, 8, 16); every
-// lane of a group receives the group sum.  DPP: quad_perm xor1 / xor2, then
-// half-row mirror (lane i <-> 7 - i) and row mirror (lane i <-> 15 - i).
+// Sum over aligned groups of N consecutive lanes (N in 2, 4, 8, 16, 32);
+// every lane of a group receives the group sum.  DPP: quad_perm xor1 / xor2,
+// then half-row mirror (lane i <-> 7 - i) and row mirror (lane i <-> 15 - i);
+// for 32, a swizzle swaps the two rows of each half wave (lane i <-> i ^ 16).
 template <int N>
 __device__ __forceinline__ float lane_group_sum(float v) {
   v += dpp<0xB1>(v);
   if constexpr (N >= 4) v += dpp<0x4E>(v);
   if constexpr (N >= 8) v += dpp<0x141>(v);
   if constexpr (N >= 16) v += dpp<0x140>(v);
+  if constexpr (N >= 32)  // bitmask mode: and 0x1F, or 0, xor 0x10
+    v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
   return v;
 }
 
@@ -155,16 +160,17 @@ __device__ __forceinline__ GroupParams group_params(float mn_raw, float mx_raw, 
 // fast path computes rint((x - mn) * rs) (rs = 1 / s within one ulp, 0 when
 // s == 0, which gives code 0 as required) and falls back to the division
 // for a word where it may differ:
-//  * near ties: the quotient q = (x - mn) / s is below 32 (x - mn is at most
-//    the group's range and s is at least half the range over the levels,
-//    B <= 4), and the product differs from q by at most q * 2^-22 < 2^-17
-//    (one rounding of the product, a reciprocal within one ulp).  Away from
-//    the half-integers by more than that, the product, q and q rounded to
-//    fp32 (which cannot cross an fp32-representable half-integer) all round
-//    to the same integer.  dmax keeps the word's largest |q - rint(q)|
-//    (exact: q >= 0, and q - rint(q) is exact by Sterbenz's lemma, so it is
-//    at most 0.5); dmax > kNearHalf means a product within 2^-16 of a
-//    half-integer.
+//  * near ties: the quotient q = (x - mn) / s is below 2^B (x - mn is at
+//    most the group's range and s is the range over the levels, rounded to
+//    fp16 with a relative error of at most 2^-11), and the product differs
+//    from q by at most q * 2^-22 (one rounding of the product, a reciprocal
+//    within one ulp): below 2^-18 for B <= 4, below 2^-14 for B = 8.  Away
+//    from the half-integers by more than that, the product, q and q rounded
+//    to fp32 (at most 2^-17 away for q < 256) all round to the same
+//    integer.  dmax keeps the word's largest |q - rint(q)| (exact: q >= 0,
+//    and q - rint(q) is exact by Sterbenz's lemma, so it is at most 0.5);
+//    dmax > near_half(B) means a product within 2^-16 (B <= 4) or 2^-13
+//    (B = 8) of a half-integer.
 //  * the clamp: with a normal fp16 step (s >= 2^-14, the fp32 step rounded
 //    to fp16 with a relative error of at most 2^-11) the product is at most
 //    top * (1 + 2^-10) < top + 1/2, so rint never passes top and the fast
@@ -173,7 +179,10 @@ __device__ __forceinline__ GroupParams group_params(float mn_raw, float mx_raw, 
 // The fast codes enter the word as two fp32 sums, one per half word, of
 // c * 2^(B * i): integers below 2^16, so the sums are exact.  The exact path
 // needs no clamp at 0 (x - mn >= 0).
-constexpr float kNearHalf = 0.5f - 0x1p-16f;
+template <int BITS>
+constexpr float near_half() {
+  return BITS <= 4 ? 0.5f - 0x1p-16f : 0.5f - 0x1p-13f;
+}
 
 // 1.0f the compiler cannot see through: fma(x, one, -mn) then stays an fma,
 // which takes an fp16 x directly (v_fma_mix_f32), and equals x - mn.
@@ -199,7 +208,7 @@ struct FastWord {
   }
   __device__ __forceinline__ bool exact_needed() const {
     const float t = lo + hi;
-    return dmax > kNearHalf || t != t;
+    return dmax > near_half<BITS>() || t != t;
   }
   __device__ __forceinline__ uint32_t word() const {
     return (uint32_t)lo | ((uint32_t)hi << (BITS * (CPW / 2)));
@@ -457,13 +466,22 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
         // w * CPW .. w * CPW + CPW - 1 of token t
         const int op = wi / (W * G), w = (wi / G) % W, t = wi % G;
         float x[CPW], cd[CPW];
+        if constexpr (CPW >= 8) {
 #pragma unroll
-        for (int i = 0; i < CPW; i += 8) {
-          const uint4 u = *reinterpret_cast<const uint4 *>(&fs.x[bf][op][t][w * CPW + i]);
+          for (int i = 0; i < CPW; i += 8) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(&fs.x[bf][op][t][w * CPW + i]);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const half2_t x2 = __builtin_bit_cast(half2_t, u4_get(u, q / 2));
-            x[i + q] = (q & 1) ? (float)x2.y : (float)x2.x;
+            for (int q = 0; q < 8; ++q) {
+              const half2_t x2 = __builtin_bit_cast(half2_t, u4_get(u, q / 2));
+              x[i + q] = (q & 1) ? (float)x2.y : (float)x2.x;
+            }
+          }
+        } else {  // B = 8: four channels per word
+          const uint2 u = *reinterpret_cast<const uint2 *>(&fs.x[bf][op][t][w * CPW]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const half2_t x2 = __builtin_bit_cast(half2_t, q < 2 ? u.x : u.y);
+            x[q] = (q & 1) ? (float)x2.y : (float)x2.x;
           }
         }
         FastWord<BITS, CPW> fw;
@@ -669,7 +687,7 @@ struct DecSmem {
   using C = DecCfg<BITS, G>;
   struct {
     float acc[kDecodeWaves][4][kD];  // [wave][row][channel]
-    float bias[kDecodeWaves][4][16]; // [wave][row][word]
+    float bias[kDecodeWaves][4][32]; // [wave][row][word]
     float m[kDecodeWaves], l[kDecodeWaves];
   } fin;
   union {
@@ -708,7 +726,8 @@ __device__ __forceinline__ int code_offset(int i) {
   constexpr int HP = 16 / BITS;
   const int p = i % HP;
   if constexpr (BITS == 2) return p <= 4 ? 2 * p : 2 * (p - 5);
-  else return p <= 1 ? 4 * p : 4 * (p - 2);
+  else if constexpr (BITS == 4) return p <= 1 ? 4 * p : 4 * (p - 2);
+  else return 0;  // B = 8: the low byte of a half, or the high one shifted down
 }
 
 // 2^(24 - e) for channel i of a word: the factor between an extracted code's
@@ -720,15 +739,18 @@ __device__ __forceinline__ float code_factor(int i) {
 
 // Word u masked to code pair p (channels p and p + HP), each half holding its
 // code at bit offset code_offset(p).  uh is u shifted right by 10 (B = 2) or
-// 8 (B = 4), which brings the upper pairs of each half into the mantissa.
+// 8 (B = 4, 8), which brings the upper pairs of each half into the mantissa.
 template <int BITS, int P>
 __device__ __forceinline__ uint32_t pair_bits(uint32_t u, uint32_t uh) {
   if constexpr (BITS == 2) {
     if constexpr (P <= 4) return u & (0x00030003u << (2 * P));
     else return uh & (0x00030003u << (2 * (P - 5)));
-  } else {
+  } else if constexpr (BITS == 4) {
     if constexpr (P <= 1) return u & (0x000F000Fu << (4 * P));
     else return uh & (0x000F000Fu << (4 * (P - 2)));
+  } else {
+    if constexpr (P == 0) return u & 0x00FF00FFu;
+    else return uh & 0x00FF00FFu;
   }
 }
 
@@ -772,13 +794,21 @@ __device__ __forceinline__ void axpy_pairs(uint32_t u, uint32_t uh, float pp, fl
 
 // Combine the per-lane states of one wave and publish them to sm.fin.
 // CPW: channels per lane; WPR: lanes per token slot; FOLD8: lanes l and l^8
-// hold the same channels (two slots per 16-lane row).
+// hold the same channels (two slots per 16-lane row).  Each published row
+// covers all kD channels: one per 16-lane row of the wave, except with 32
+// lanes per slot (B = 8), where row r is slot r and only rows 0 and 1 are
+// written (publish_rows).
+template <int WPR>
+constexpr int publish_rows() {
+  return WPR == 32 ? 2 : 4;
+}
+
 template <int CPW, int WPR, bool FOLD8>
-__device__ __forceinline__ void wave_publish(float (&fin_acc)[4][kD], float (&fin_bias)[4][16],
+__device__ __forceinline__ void wave_publish(float (&fin_acc)[4][kD], float (&fin_bias)[4][32],
                                              float &fin_m, float &fin_l, float m, float l,
                                              float *acc, float bias) {
   const int lane = threadIdx.x & 63;
-  const int w = lane % WPR, row = lane >> 4;
+  const int w = lane % WPR, row = WPR == 32 ? lane >> 5 : lane >> 4;
   const float M = wave_max(m);
   const float e = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
 #pragma unroll
@@ -1030,14 +1060,22 @@ __device__ __forceinline__ void process_sub(const SubLoads<BITS, G> &b, int T0, 
 template <int BITS, int G>
 struct WinCfg {
   using C = DecCfg<BITS, G>;
-  static constexpr int NV = C::CPW / 8;  // 16-byte vectors per lane and token
-  static constexpr int STEP = C::TQS;    // tokens per step
-  static constexpr int PF = 16 / STEP;   // steps loaded up front (16 tokens)
+  // a lane's CPW fp16 channels of one token: 16-byte vectors, or one 8-byte
+  // vector when CPW = 4 (B = 8)
+  static constexpr bool WIDE = C::CPW >= 8;
+  using Vec = typename std::conditional<WIDE, uint4, uint2>::type;
+  static constexpr int NV = WIDE ? C::CPW / 8 : 1;  // vectors per lane and token
+  static constexpr int WPV = WIDE ? 4 : 2;         // half2 words per vector
+  static constexpr int STEP = C::TQS;              // tokens per step
+  static constexpr int PF = 16 / STEP;             // steps loaded up front (16 tokens)
 };
+
+__device__ __forceinline__ uint32_t vec_get(const uint4 &v, int i) { return u4_get(v, i); }
+__device__ __forceinline__ uint32_t vec_get(const uint2 &v, int i) { return i == 0 ? v.x : v.y; }
 
 template <int BITS, int G>
 struct WinStep {
-  uint4 k[WinCfg<BITS, G>::NV], v[WinCfg<BITS, G>::NV];
+  typename WinCfg<BITS, G>::Vec k[WinCfg<BITS, G>::NV], v[WinCfg<BITS, G>::NV];
 };
 
 template <int BITS, int G>
@@ -1051,10 +1089,15 @@ struct WinStream {
   __device__ __forceinline__ void issue(WinStep<BITS, G> &x, int step) const {
     const rsrc_t rk = make_rsrc(kr, bytes), rv = make_rsrc(vr, bytes);
     const uint32_t vo = lane_voff + (uint32_t)(begin + step * WC::STEP) * (kD * 2);
+    if constexpr (WC::WIDE) {
 #pragma unroll
-    for (int v = 0; v < WC::NV; ++v) x.k[v] = bload4(rk, vo + 16 * v, 0);
+      for (int v = 0; v < WC::NV; ++v) x.k[v] = bload4(rk, vo + 16 * v, 0);
 #pragma unroll
-    for (int v = 0; v < WC::NV; ++v) x.v[v] = bload4(rv, vo + 16 * v, 0);
+      for (int v = 0; v < WC::NV; ++v) x.v[v] = bload4(rv, vo + 16 * v, 0);
+    } else {
+      x.k[0] = bload2(rk, vo, 0);
+      x.v[0] = bload2(rv, vo, 0);
+    }
   }
 };
 
@@ -1066,11 +1109,11 @@ __device__ __forceinline__ void window_step(const WinStep<BITS, G> &x, bool vali
   float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
   for (int v = 0; v < WC::NV; ++v) {
-    const uint32_t u[4] = {x.k[v].x, x.k[v].y, x.k[v].z, x.k[v].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a0 = mix_lo(qv[8 * v + 2 * e], u[e], a0);
-      a1 = mix_hi(qv[8 * v + 2 * e + 1], u[e], a1);
+    for (int e = 0; e < WC::WPV; ++e) {
+      const uint32_t u = vec_get(x.k[v], e);
+      a0 = mix_lo(qv[8 * v + 2 * e], u, a0);
+      a1 = mix_hi(qv[8 * v + 2 * e + 1], u, a1);
     }
   }
   float s = lane_group_sum<C::W>(a0 + a1);
@@ -1081,14 +1124,14 @@ __device__ __forceinline__ void window_step(const WinStep<BITS, G> &x, bool vali
   st.l += p;
 #pragma unroll
   for (int v = 0; v < WC::NV; ++v) {
-    const uint32_t u[4] = {x.v[v].x, x.v[v].y, x.v[v].z, x.v[v].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < WC::WPV; ++e) {
       // value sums hold channel values times 2^(e - 24) (see above)
+      const uint32_t u = vec_get(x.v[v], e);
       const int c0 = 8 * v + 2 * e;
-      st.acc[c0] = mix_lo(p * __builtin_ldexpf(1.0f, code_offset<BITS>(c0) - 24), u[e], st.acc[c0]);
+      st.acc[c0] = mix_lo(p * __builtin_ldexpf(1.0f, code_offset<BITS>(c0) - 24), u, st.acc[c0]);
       st.acc[c0 + 1] =
-          mix_hi(p * __builtin_ldexpf(1.0f, code_offset<BITS>(c0 + 1) - 24), u[e], st.acc[c0 + 1]);
+          mix_hi(p * __builtin_ldexpf(1.0f, code_offset<BITS>(c0 + 1) - 24), u, st.acc[c0 + 1]);
     }
   }
 }
@@ -1271,6 +1314,7 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 2 * kDecodeWavesPerSim
   constexpr int kDecodeDepth = DEPTH;
   using C = DecCfg<BITS, G>;
   using WC = WinCfg<BITS, G>;
+  static_assert(!FUSED || WC::WIDE, "the whole-step kernel holds window rows as 16-byte vectors");
   __shared__ DecSmem<BITS, G> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -1516,7 +1560,7 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 2 * kDecodeWavesPerSim
       for (int x = 0; x < kDecodeWaves; ++x) {
         float sa = 0.0f, sb = 0.0f;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
+        for (int y = 0; y < publish_rows<C::W>(); ++y) {
           sa += sm.fin.acc[x][y][tid];
           sb += sm.fin.bias[x][y][tid / C::CPW];
         }
@@ -1643,6 +1687,9 @@ int launch_encode(int bits, int G, const EncodeArgs &ea, dim3 grid, hipStream_t 
   if (bits == 4 && G == 32) return launch_encode_t<4, 32>(ea, grid, st);
   if (bits == 4 && G == 64) return launch_encode_t<4, 64>(ea, grid, st);
   if (bits == 4 && G == 128) return launch_encode_t<4, 128>(ea, grid, st);
+  if (bits == 8 && G == 32) return launch_encode_t<8, 32>(ea, grid, st);
+  if (bits == 8 && G == 64) return launch_encode_t<8, 64>(ea, grid, st);
+  if (bits == 8 && G == 128) return launch_encode_t<8, 128>(ea, grid, st);
   return (int)hipErrorInvalidValue;
 }
 
@@ -1650,9 +1697,10 @@ template <int BITS, int G>
 int launch_decode_t(const DecodeArgs &da, const EncodeArgs &ea, bool fused, int depth, dim3 grid,
                     hipStream_t st) {
   const dim3 blk(kDecodeThreads);
-  if (fused)  // one workgroup per compute unit (launch_decode_step)
-    hipLaunchKernelGGL((decode_kernel<BITS, G, true, 2>), grid, blk, 0, st, da, ea);
-  else if (depth == 1)
+  if (fused) {  // one workgroup per compute unit (launch_decode_step)
+    if constexpr (BITS == 8) return (int)hipErrorInvalidValue;  // three kernels instead
+    else hipLaunchKernelGGL((decode_kernel<BITS, G, true, 2>), grid, blk, 0, st, da, ea);
+  } else if (depth == 1)
     hipLaunchKernelGGL((decode_kernel<BITS, G, false, 1>), grid, blk, 0, st, da, ea);
   else
     hipLaunchKernelGGL((decode_kernel<BITS, G, false, 2>), grid, blk, 0, st, da, ea);
@@ -1706,6 +1754,9 @@ int launch_flush(const kivi_dims &d, const kivi_cache &c, void *stream) {
   else if (d.bits == 4 && G == 32) hipLaunchKernelGGL((flush_kernel<4, 32>), grid, dim3(kFlushThreads), 0, st, ea);
   else if (d.bits == 4 && G == 64) hipLaunchKernelGGL((flush_kernel<4, 64>), grid, dim3(kFlushThreads), 0, st, ea);
   else if (d.bits == 4 && G == 128) hipLaunchKernelGGL((flush_kernel<4, 128>), grid, dim3(kFlushThreads), 0, st, ea);
+  else if (d.bits == 8 && G == 32) hipLaunchKernelGGL((flush_kernel<8, 32>), grid, dim3(kFlushThreads), 0, st, ea);
+  else if (d.bits == 8 && G == 64) hipLaunchKernelGGL((flush_kernel<8, 64>), grid, dim3(kFlushThreads), 0, st, ea);
+  else if (d.bits == 8 && G == 128) hipLaunchKernelGGL((flush_kernel<8, 128>), grid, dim3(kFlushThreads), 0, st, ea);
   else return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
@@ -1773,6 +1824,9 @@ int launch_decode_any(const kivi_dims &d, const DecodeArgs &da, const EncodeArgs
   if (d.bits == 4 && G == 32) return launch_decode_t<4, 32>(da, ea, fused, depth, grid, st);
   if (d.bits == 4 && G == 64) return launch_decode_t<4, 64>(da, ea, fused, depth, grid, st);
   if (d.bits == 4 && G == 128) return launch_decode_t<4, 128>(da, ea, fused, depth, grid, st);
+  if (d.bits == 8 && G == 32) return launch_decode_t<8, 32>(da, ea, fused, depth, grid, st);
+  if (d.bits == 8 && G == 64) return launch_decode_t<8, 64>(da, ea, fused, depth, grid, st);
+  if (d.bits == 8 && G == 128) return launch_decode_t<8, 128>(da, ea, fused, depth, grid, st);
   return (int)hipErrorInvalidValue;
 }
 
@@ -1798,7 +1852,7 @@ int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, 
 int launch_decode_step(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
                        const void *k_new, const void *v_new, const void *q, float *out,
                        float sm_scale, void *workspace, void *stream) {
-  if (!step_in_one_kernel(p)) {
+  if (!step_in_one_kernel(d, p)) {
     int rc = launch_append(d, c, k_new, v_new, stream);
     if (rc) return rc;
     rc = launch_decode(d, c, p, q, out, sm_scale, workspace, stream);

@@ -46,7 +46,7 @@ extern "C" {
 
 /*
  * Problem dimensions.  The names follow the pages' parameters:
- *   bits      B, the code width ("nbits", [P1] section 5.2); 2 or 4.
+ *   bits      B, the code width ("nbits", [P1] section 5.2: 2, 4 or 8 bits).
  *   group     G, tokens per key group and channels per value group
  *             ("q_group_size", [P1] sections 3.1 and 5.2).  Must divide
  *             head_dim, residual and capacity.
@@ -55,7 +55,7 @@ extern "C" {
  *   capacity  quantized tokens each sequence can hold; a multiple of G.
  *   batch, heads, head_dim as in the cache-size formula of [P1] section 2.1.
  * Host validation (kivi_validate_dims): all > 0 except capacity >= 0,
- * bits in {2,4}, head_dim % group == 0, residual % group == 0,
+ * bits in {2,4,8}, head_dim % group == 0, residual % group == 0,
  * capacity % group == 0, (head_dim * bits) % 32 == 0.
  * Compiled kernels cover head_dim == 128 and group in {32, 64, 128};
  * other valid dims return KIVI_EUNSUPPORTED.
@@ -201,9 +201,9 @@ int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache,
  * are exactly those of the three calls in that order; the output is theirs
  * up to rounding (the summation order may differ).  When one workgroup
  * covers a whole (sequence, head) (kivi_decode_splits: 1) and the grid is
- * at most one workgroup per compute unit (batch * heads <= 256), it is a
- * single kernel: each workgroup appends its (sequence, head)'s token, uses it
- * from registers in the attention, and if the window is then full quantizes
+ * at most one workgroup per compute unit (batch * heads <= 256) and B is 2
+ * or 4, it is a single kernel: each workgroup appends its (sequence, head)'s
+ * token, uses it from registers in the attention, and if the window is then full quantizes
  * it (from the registers that hold it for the attention when R <= 128, else
  * re-reading it), and the last workgroup of the sequence commits the lengths
  * through cache->tickets.  Otherwise it launches the three kernels.

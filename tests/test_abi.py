@@ -57,6 +57,8 @@ def test_validate_dims_codes():
     ((1, 32, 128, 2, 128, 128, 131072), 8, 3),   # long context: 8 workgroups per head
     ((1, 32, 128, 4, 128, 128, 131072), 8, 3),
     ((1, 1, 128, 2, 32, 32, 0), 1, 1),           # window only
+    ((8, 32, 128, 8, 32, 128, 4096), 1, 3),      # 8 bits: one workgroup per head, step as three kernels
+    ((1, 32, 128, 8, 128, 128, 131072), 8, 3),
     ((1, 1, 128, 2, 32, 4096, 1 << 24), 64, 3),  # capped at 64
 ])
 def test_decode_plan(dims, splits, step_kernels):

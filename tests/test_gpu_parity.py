@@ -146,7 +146,7 @@ def test_ragged_serving_sampled_heads():
     _check_heads(c, w, sorted(heads))
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_long_context_sampled_heads(bits):
     w = workload(5, bits=bits)
     c = gpu_cache(w)
@@ -291,9 +291,10 @@ def test_byte_model_matches_buffers():
 def _near_tie_values(bits, rng, pairs=200):
     """(mn, mx, xs) triples of fp16 values for which (x - mn) / s (s the fp16
     step of a group with minimum mn and maximum mx, fp32 arithmetic) is a
-    half-integer or within 2^-15 of one: exact ties, and quotients near the
-    rounding boundaries where a reciprocal-based shortcut could round the
-    other way.  Negative minima give x - mn many significant bits."""
+    half-integer or within 2^-15 (2^-12 at B=8, whose quotients reach 255) of
+    one: exact ties, and quotients near the rounding boundaries where a
+    reciprocal-based shortcut could round the other way.  Negative minima
+    give x - mn many significant bits."""
     levels = np.float32((1 << bits) - 1)
     f16 = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
     f16 = np.concatenate([-f16[1:], f16])
@@ -305,13 +306,13 @@ def _near_tie_values(bits, rng, pairs=200):
         xs = f16[(f16 >= mn) & (f16 <= mx)]
         q = (xs.astype(np.float32) - np.float32(mn)) / s
         frac = np.abs(np.abs(q - np.rint(q)) - np.float32(0.5))
-        near = xs[frac < 2.0 ** -15]
+        near = xs[frac < (2.0 ** -15 if bits <= 4 else 2.0 ** -12)]
         if len(near):
             out.append((mn, mx, near))
     return out
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_quantizer_near_ties_bit_exact_on_both_encoders(bits):
     """Keys and values built from exact and near rounding ties: the prefill
     encoder and the flush kernel both match the oracle bit for bit."""
@@ -541,3 +542,61 @@ def test_decode_step_with_split_heads_uses_three_kernels():
     q = torch.from_numpy(w.q).cuda()
     out_a, out_b, sa, sb = _step_both(lambda: gpu_cache(w, q_len=ql, r_len=rl), kn, vn, q, 1.0)
     _assert_same_step(out_a, out_b, sa, sb)
+
+
+# ------------------------------------------------------------------ 8 bits
+# The tutorial's parameter section lists 2, 4 and 8 bits.  At B=8 a word
+# holds four channels, so a token spans 32 lanes.
+
+def test_eight_bit_llama2_7b_shape_all_heads():
+    """Two sequences of the Llama-2-7B-shaped layer at B=8: every cache buffer
+    bit for bit and every head's output against the oracle.  64 (sequence,
+    head) pairs are split four ways, so the split merge runs at B=8 too."""
+    w = workload(2, bits=8, batch=2)
+    c = gpu_cache(w)
+    assert kivi.decode_splits(kivi.make_dims(**w.dims())) == 4
+    worst = _check_heads(c, w, [(b, h) for b in range(2) for h in range(32)])
+    assert worst[0] < 2e-3
+
+
+def test_eight_bit_flush_and_step_match_oracle():
+    """At B=8 the whole step is the three kernels; after appending the last
+    window token the flush quantizes the full 128-token window bit for bit as
+    the oracle does, and the step's output matches the oracle's decode."""
+    w = workload(3, bits=8, batch=2)
+    cfg = w.config
+    d = w.dims()
+    assert kivi.decode_step_kernels(kivi.make_dims(**d)) == 3
+    rl = w.r_len - 1
+    b_idx = np.arange(2)
+    last = w.q_len + rl
+    kn = np.ascontiguousarray(w.k[b_idx, :, last])
+    vn = np.ascontiguousarray(w.v[b_idx, :, last])
+    q = torch.from_numpy(w.q).cuda()
+    out_a, out_b, sa, sb = _step_both(lambda: gpu_cache(w, r_len=rl), torch.from_numpy(kn).cuda(),
+                                      torch.from_numpy(vn).cuda(), q, cfg.sm_scale)
+    _assert_same_step(out_a, out_b, sa, sb)
+    assert (sb["r_len"] == 0).all() and (sb["q_len"] == w.q_len + 128).all()
+    out = out_b.cpu().numpy()
+    G = cfg.group
+    for b in range(2):
+        for h in (0, 17, 39):
+            t0 = int(w.q_len[b])
+            enc = ocache.encode_tokens(w.k[b, h, t0:t0 + 128], w.v[b, h, t0:t0 + 128], G, 8)
+            for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+                got = sb[name][b, h, t0 // G:(t0 + 128) // G]
+                assert np.array_equal(got.view(np.uint8), enc[name].view(np.uint8)), (name, b, h)
+            ref = ocache.decode_head(w.q[b, h], oracle_head(w, b, h), cfg.sm_scale, G, 8)
+            assert_within_tolerance(out[b, h], ref, f"b={b} h={h}")
+
+
+@pytest.mark.parametrize("q_len,r_len", [(0, 1), (32, 0), (32, 1), (4064, 31), (3968, 128)])
+def test_eight_bit_edge_lengths(q_len, r_len):
+    w = workload(2, bits=8, batch=1)
+    c = gpu_cache(w, q_len=[q_len], r_len=[r_len])
+    out = _decode(c, w)
+    for h in (0, 31):
+        st = ocache.head_state(w.k[0, h], w.v[0, h], q_len, r_len, 32, 8, 4096, 128)
+        ref = ocache.decode_head(w.q[0, h], st, 1.0, 32, 8)
+        assert_within_tolerance(out[0, h], ref, f"{q_len}+{r_len}")
+        assert_head_bit_exact(head_buffers(c, 0, h), st, 32)
