@@ -19,6 +19,8 @@ path computes, written from the pages' definitions:
   library's documented buffer layouts, one (sequence, head) at a time.
 * ``axis_ablation`` -- the four choices of grouping axis for keys and values
   and the key, score and output errors each gives (analysis, not parity).
+* ``rope``       -- the rotary embedding applied to keys after dequantization
+  (keys stored before the rotation) and the decode that uses it.
 
 Precision: the quantizer runs the fixed fp32 operation sequence stated in
 ``quantizer``; attention runs in fp64 on the exactly dequantized values.
@@ -28,4 +30,4 @@ fix (hand-worked cases, brute force, closed forms, invariants); none is
 "parity unpinned".
 """
 
-from . import attention, axis_ablation, cache, packing, quantizer  # noqa: F401
+from . import attention, axis_ablation, cache, packing, quantizer, rope  # noqa: F401
