@@ -148,6 +148,21 @@ int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache, const void 
   return kivi::hip_rc(kivi::launch_decode(*dims, *cache, p, q, out, sm_scale, workspace, stream));
 }
 
+int kivi_decode_attn_rope(const kivi_dims *dims, const kivi_cache *cache, const void *q,
+                          float *out, float sm_scale, double rope_base, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache) || !q || !out || !workspace) return KIVI_EINVAL;
+  if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
+    return KIVI_EINVAL;
+  if (!(rope_base > 1.0) || rope_base == 1.0 / 0.0) return KIVI_EINVAL;
+  const kivi::DecodePlan p = kivi::decode_plan(*dims);
+  if (workspace_bytes < p.bytes) return KIVI_ENOSPC;
+  return kivi::hip_rc(kivi::launch_decode_rope(*dims, *cache, p, q, out, sm_scale, rope_base,
+                                               workspace, stream));
+}
+
 int kivi_decode_step(const kivi_dims *dims, const kivi_cache *cache, const void *k_new,
                      const void *v_new, const void *q, float *out, float sm_scale,
                      void *workspace, size_t workspace_bytes, void *stream) {

@@ -660,6 +660,7 @@ struct DecodeArgs {
   uint32_t *tickets;
   float qscale;  // sm_scale * log2(e)
   int heads, R, cap, splits, win_per_wave, part_stride;
+  double rope_log2_base;  // log2 of the rotary base (ROPE kernels only)
 };
 
 constexpr int kMaxSplits = 128;
@@ -682,7 +683,7 @@ struct DecCfg {
   static_assert(G % TPL == 0, "a wave-load stays inside one tile");
 };
 
-template <int BITS, int G>
+template <int BITS, int G, bool ROPE = false>
 struct DecSmem {
   using C = DecCfg<BITS, G>;
   struct {
@@ -693,8 +694,9 @@ struct DecSmem {
   union {
     struct {
       float qs[kD];                     // sm_scale * log2(e) * q
-      float qp[C::NTS][C::W * C::QPW];  // key multipliers, word-padded
+      float qp[C::NTS][C::W * C::QPW];  // key multipliers, word-padded (ROPE: steps)
       float cz[C::NTS][C::W];
+      float zz[ROPE ? C::NTS : 1][ROPE ? C::W * C::QPW : 1];  // ROPE: zero-points
     } wave[kDecodeWaves];
     struct {
       float m[kMaxSplits], l[kMaxSplits];
@@ -981,18 +983,126 @@ struct QuantStream {
   }
 };
 
+// ------------------------------------------ decode: keys stored pre-rotation
+// Keys quantized before the rotary embedding and rotated after
+// dequantization: key token t (position t in the sequence, window tokens
+// after the quantized ones) is rotated by angle t * theta_f in channel pair
+// f = (2f, 2f + 1), theta_f = base^(-2f/D), and the query arrives rotated.
+// Rather than rotating every key, the score uses the query turned back by
+// the key's angle: q . R(t) k = (R(t)^T q) . k = u_t . k, per pair
+//   u[2f] = q[2f] cos + q[2f+1] sin,  u[2f+1] = q[2f+1] cos - q[2f] sin.
+// The dequantization k = z + c * s then folds in as with unrotated keys, per
+// token instead of per key group: score = sum_d u_d z_d + sum_d (u_d s_d) c_d.
+// A lane's angles come from revolutions frac(t * theta_f / 2 pi) formed in
+// fp64 (exact enough at any 32-bit position) and the hardware sine and
+// cosine; the next three tokens of a lane's quad step u by the fixed
+// rotation R(theta_f)^T in fp32.
+template <int CPW>
+struct RopeLane {
+  const float *q;         // the lane's rotated query channels (x sm_scale log2 e), in LDS
+  double rev[CPW / 2];    // theta_f / (2 pi) of the lane's pairs
+  float cs[CPW / 2], sn[CPW / 2];  // cos and sin of theta_f
+
+  // first channel c0 of the lane; qs: the wave's scaled query in LDS
+  __device__ __forceinline__ void init(const float *qs, int c0, double log2_base) {
+    q = qs + c0;
+#pragma unroll
+    for (int j = 0; j < CPW / 2; ++j) {
+      const int f = c0 / 2 + j;
+      const double th = exp2(-(2.0 * f / kD) * log2_base);
+      rev[j] = th * 0.15915494309189535;  // 1 / (2 pi)
+      cs[j] = (float)cos(th);
+      sn[j] = (float)sin(th);
+    }
+  }
+  // u = the query turned back by position p's angles
+  __device__ __forceinline__ void at(float (&u)[CPW], int p) const {
+#pragma unroll
+    for (int j = 0; j < CPW / 2; ++j) {
+      double x = (double)p * rev[j];
+      x -= floor(x);
+      const float xf = (float)x;
+      const float c = __builtin_amdgcn_cosf(xf), s = __builtin_amdgcn_sinf(xf);
+      const float2 qq = *reinterpret_cast<const float2 *>(q + 2 * j);
+      u[2 * j] = fmaf(qq.x, c, qq.y * s);
+      u[2 * j + 1] = fmaf(qq.y, c, -(qq.x * s));
+    }
+  }
+  // u for the next position
+  __device__ __forceinline__ void step(float (&u)[CPW]) const {
+#pragma unroll
+    for (int j = 0; j < CPW / 2; ++j) {
+      const float a = u[2 * j], b = u[2 * j + 1];
+      u[2 * j] = fmaf(a, cs[j], b * sn[j]);
+      u[2 * j + 1] = fmaf(b, cs[j], -(a * sn[j]));
+    }
+  }
+};
+
+// Scores of one sub-chunk with keys stored pre-rotation: staging of the
+// touched tiles' steps (times the code-offset factor) and zero-points in
+// LDS, then per token u, the multipliers u * s and the bias u . z.
 template <int BITS, int G>
-__device__ __forceinline__ void process_sub(const SubLoads<BITS, G> &b, int T0, int ql, int lane,
-                                            float qs0, float qs1, float qf0, float qf1,
+__device__ __forceinline__ void rope_scores(const SubLoads<BITS, G> &b, int T0, int nvl, int lane,
                                             float (&qp)[DecCfg<BITS, G>::NTS][DecCfg<BITS, G>::W *
                                                                              DecCfg<BITS, G>::QPW],
-                                            float (&cz)[DecCfg<BITS, G>::NTS][DecCfg<BITS, G>::W],
-                                            LaneState<DecCfg<BITS, G>::CPW> &st) {
+                                            float (&zz)[DecCfg<BITS, G>::NTS][DecCfg<BITS, G>::W *
+                                                                             DecCfg<BITS, G>::QPW],
+                                            const RopeLane<DecCfg<BITS, G>::CPW> &rl,
+                                            float (&s)[DecCfg<BITS, G>::NL * 4]) {
+  using C = DecCfg<BITS, G>;
+  const int w = lane % C::W, slot = lane / C::W;
+  const int d0 = 2 * lane;
+  const int qpo = (d0 / C::CPW) * C::QPW + d0 % C::CPW;
+#pragma unroll
+  for (int k = 0; k < C::NTS; ++k) {
+    qp[k][qpo] = mix_lo(code_factor<BITS>(d0 % C::CPW), b.ks[k], 0.0f);
+    qp[k][qpo + 1] = mix_hi(code_factor<BITS>((d0 + 1) % C::CPW), b.ks[k], 0.0f);
+    const half2_t z2 = __builtin_bit_cast(half2_t, b.kz[k]);
+    zz[k][qpo] = (float)z2.x;
+    zz[k][qpo + 1] = (float)z2.y;
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < C::NL; ++j) {
+    if (j < nvl) {
+      const int k = ((T0 % G) + j * C::TPL) / G;
+      float u[C::CPW], m[C::CPW];
+      rl.at(u, T0 + j * C::TPL + 4 * slot);  // the first token of the lane's quad
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i > 0) rl.step(u);
+        float bias = 0.0f;
+#pragma unroll
+        for (int d = 0; d < C::CPW; d += 4) {  // steps and zero-points read back from LDS
+          const float4 a4 = *reinterpret_cast<const float4 *>(&qp[k][w * C::QPW + d]);
+          const float4 z4 = *reinterpret_cast<const float4 *>(&zz[k][w * C::QPW + d]);
+          m[d] = u[d] * a4.x, m[d + 1] = u[d + 1] * a4.y;
+          m[d + 2] = u[d + 2] * a4.z, m[d + 3] = u[d + 3] * a4.w;
+          bias = fmaf(u[d], z4.x, fmaf(u[d + 1], z4.y, fmaf(u[d + 2], z4.z, fmaf(u[d + 3], z4.w, bias))));
+        }
+        s[4 * j + i] = lane_group_sum<C::W>(dot_word<BITS>(u4_get(b.kc[j], i), m, bias));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[4 * j + i] = -INFINITY;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Scores of one sub-chunk (every lane of a token slot ends with the full
+// sums): staging of q'' = qsf * s and the zero terms of the touched tiles in
+// LDS, then one dot product per token and word.
+template <int BITS, int G>
+__device__ __forceinline__ void plain_scores(const SubLoads<BITS, G> &b, int T0, int nvl, int lane,
+                                             float qs0, float qs1, float qf0, float qf1,
+                                             float (&qp)[DecCfg<BITS, G>::NTS][DecCfg<BITS, G>::W *
+                                                                              DecCfg<BITS, G>::QPW],
+                                             float (&cz)[DecCfg<BITS, G>::NTS][DecCfg<BITS, G>::W],
+                                             float (&s)[DecCfg<BITS, G>::NL * 4]) {
   using C = DecCfg<BITS, G>;
   const int w = lane % C::W;
-  const int nvl = min(C::NL, (ql - T0) / C::TPL);
-
-  // ---- stage q'' = qsf * s and the zero terms of the touched tiles
   const int d0 = 2 * lane;
   const int qpo = (d0 / C::CPW) * C::QPW + d0 % C::CPW;
 #pragma unroll
@@ -1005,8 +1115,6 @@ __device__ __forceinline__ void process_sub(const SubLoads<BITS, G> &b, int T0, 
   }
   __builtin_amdgcn_wave_barrier();
 
-  // ---- scores (every lane of a token slot ends with the full sums)
-  float s[C::NL * 4];
 #pragma unroll
   for (int j = 0; j < C::NL; ++j) {
     if (j < nvl) {
@@ -1030,6 +1138,27 @@ __device__ __forceinline__ void process_sub(const SubLoads<BITS, G> &b, int T0, 
     }
   }
   __builtin_amdgcn_wave_barrier();
+}
+
+template <int BITS, int G, bool ROPE = false>
+__device__ __forceinline__ void process_sub(const SubLoads<BITS, G> &b, int T0, int ql, int lane,
+                                            float qs0, float qs1, float qf0, float qf1,
+                                            float (&qp)[DecCfg<BITS, G>::NTS][DecCfg<BITS, G>::W *
+                                                                             DecCfg<BITS, G>::QPW],
+                                            float (&cz)[DecCfg<BITS, G>::NTS][DecCfg<BITS, G>::W],
+                                            LaneState<DecCfg<BITS, G>::CPW> &st,
+                                            float (*zz)[DecCfg<BITS, G>::W * DecCfg<BITS, G>::QPW] =
+                                                nullptr,
+                                            const RopeLane<DecCfg<BITS, G>::CPW> *rl = nullptr) {
+  using C = DecCfg<BITS, G>;
+  const int nvl = min(C::NL, (ql - T0) / C::TPL);
+  float s[C::NL * 4];
+  if constexpr (ROPE) {
+    rope_scores<BITS, G>(b, T0, nvl, lane, qp, *reinterpret_cast<float(*)[C::NTS][C::W * C::QPW]>(zz),
+                         *rl, s);
+  } else {
+    plain_scores<BITS, G>(b, T0, nvl, lane, qs0, qs1, qf0, qf1, qp, cz, s);
+  }
 
   update_max<C::CPW, C::NL * 4>(st, s);
 
@@ -1308,14 +1437,16 @@ __device__ __forceinline__ void flush_regs_keys(const EncodeArgs &ea, const RegF
 // register footprint lets two or three workgroups share a compute unit
 // (measured on the 13B layer, 640 workgroups: 37 us at depth 1 against 45 us
 // at depth 2; on the 7B layer, 256 workgroups, depth 2 is the faster).
-template <int BITS, int G, bool FUSED, int DEPTH>
+// ROPE: keys are stored before the rotary embedding (RopeLane above).
+template <int BITS, int G, bool FUSED, int DEPTH, bool ROPE = false>
 __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 2 * kDecodeWavesPerSimd : kDecodeWavesPerSimd) void decode_kernel(
     DecodeArgs a, EncodeArgs ea) {
   constexpr int kDecodeDepth = DEPTH;
   using C = DecCfg<BITS, G>;
   using WC = WinCfg<BITS, G>;
   static_assert(!FUSED || WC::WIDE, "the whole-step kernel holds window rows as 16-byte vectors");
-  __shared__ DecSmem<BITS, G> sm;
+  static_assert(!(FUSED && ROPE), "keys stored pre-rotation: the step is three kernels");
+  __shared__ DecSmem<BITS, G, ROPE> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t bh = (size_t)b * a.heads + h;
@@ -1448,6 +1579,12 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 2 * kDecodeWavesPerSim
   const float qf1 = qs1 * code_factor<BITS>((2 * lane + 1) % C::CPW);
   stg.qs[2 * lane] = qs0;  // for the window tokens
   stg.qs[2 * lane + 1] = qs1;
+  [[maybe_unused]] RopeLane<C::CPW> rope;
+  if constexpr (ROPE) {
+    __builtin_amdgcn_wave_barrier();
+    rope.init(stg.qs, w * C::CPW, a.rope_log2_base);
+  }
+  auto *zz = reinterpret_cast<float(*)[C::W * C::QPW]>(&stg.zz[0][0]);
 
   LaneState<C::CPW> st;
   st.m = -INFINITY;
@@ -1474,17 +1611,29 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 2 * kDecodeWavesPerSim
         }
       }
     };
+    // keys stored pre-rotation: the query turned back by the token's
+    // position (quantized tokens first, so window slot r is position ql + r)
+    auto step = [&](const WinStep<BITS, G> &x, int i) {
+      const int r = ws.begin + i * WC::STEP + slot;
+      if constexpr (ROPE) {
+        float u[C::CPW];
+        rope.at(u, ql + r);
+        window_step<BITS, G>(x, r < ws.end, u, st);
+      } else {
+        window_step<BITS, G>(x, r < ws.end, qv, st);
+      }
+    };
 #pragma unroll
     for (int i = 0; i < WC::PF; ++i)
       if (i < wsteps) {
         fresh(wpf[i], i);
-        window_step<BITS, G>(wpf[i], ws.begin + i * WC::STEP + slot < ws.end, qv, st);
+        step(wpf[i], i);
       }
     for (int i = WC::PF; i < wsteps; ++i) {  // windows longer than the prefetched steps
       WinStep<BITS, G> x;
       ws.issue(x, i);
       fresh(x, i);
-      window_step<BITS, G>(x, ws.begin + i * WC::STEP + slot < ws.end, qv, st);
+      step(x, i);
     }
   };
 
@@ -1512,8 +1661,8 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 2 * kDecodeWavesPerSim
 #elif KIVI_DECODE_PRIORITY
       set_progress_priority(c0 + k, qs.n);
 #endif
-      process_sub<BITS, G>(ring[k], qs.t0(c0 + k), ql, lane, qs0, qs1, qf0, qf1, stg.qp, stg.cz,
-                           st);
+      process_sub<BITS, G, ROPE>(ring[k], qs.t0(c0 + k), ql, lane, qs0, qs1, qf0, qf1, stg.qp,
+                                 stg.cz, st, zz, &rope);
       qs.issue(ring[k], c0 + k + kDecodeDepth);
     }
   }
@@ -1529,8 +1678,8 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 2 * kDecodeWavesPerSim
 #elif KIVI_DECODE_PRIORITY
       set_progress_priority(c0 + k, qs.n);
 #endif
-      process_sub<BITS, G>(ring[k], qs.t0(c0 + k), ql, lane, qs0, qs1, qf0, qf1, stg.qp, stg.cz,
-                           st);
+      process_sub<BITS, G, ROPE>(ring[k], qs.t0(c0 + k), ql, lane, qs0, qs1, qf0, qf1, stg.qp,
+                                 stg.cz, st, zz, &rope);
     }
 #if KIVI_DECODE_PRIORITY
   __builtin_amdgcn_s_setprio(0);
@@ -1695,8 +1844,16 @@ int launch_encode(int bits, int G, const EncodeArgs &ea, dim3 grid, hipStream_t 
 
 template <int BITS, int G>
 int launch_decode_t(const DecodeArgs &da, const EncodeArgs &ea, bool fused, int depth, dim3 grid,
-                    hipStream_t st) {
+                    hipStream_t st, bool rope) {
   const dim3 blk(kDecodeThreads);
+  if (rope) {
+    // keys stored pre-rotation (never the whole step): always two sub-chunks
+    // in flight, whose register budget (one workgroup per compute unit)
+    // holds the rotation's per-lane state at B=2 without spilling
+    if (fused) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_kernel<BITS, G, false, 2, true>), grid, blk, 0, st, da, ea);
+    return (int)hipGetLastError();
+  }
   if (fused) {  // one workgroup per compute unit (launch_decode_step)
     if constexpr (BITS == 8) return (int)hipErrorInvalidValue;  // three kernels instead
     else hipLaunchKernelGGL((decode_kernel<BITS, G, true, 2>), grid, blk, 0, st, da, ea);
@@ -1815,18 +1972,18 @@ DecodeArgs decode_args(const kivi_dims &d, const kivi_cache &c, const DecodePlan
 }
 
 int launch_decode_any(const kivi_dims &d, const DecodeArgs &da, const EncodeArgs &ea, bool fused,
-                      int depth, hipStream_t st) {
+                      int depth, hipStream_t st, bool rope = false) {
   const dim3 grid(da.splits, d.heads, d.batch);
   const int G = d.group;
-  if (d.bits == 2 && G == 32) return launch_decode_t<2, 32>(da, ea, fused, depth, grid, st);
-  if (d.bits == 2 && G == 64) return launch_decode_t<2, 64>(da, ea, fused, depth, grid, st);
-  if (d.bits == 2 && G == 128) return launch_decode_t<2, 128>(da, ea, fused, depth, grid, st);
-  if (d.bits == 4 && G == 32) return launch_decode_t<4, 32>(da, ea, fused, depth, grid, st);
-  if (d.bits == 4 && G == 64) return launch_decode_t<4, 64>(da, ea, fused, depth, grid, st);
-  if (d.bits == 4 && G == 128) return launch_decode_t<4, 128>(da, ea, fused, depth, grid, st);
-  if (d.bits == 8 && G == 32) return launch_decode_t<8, 32>(da, ea, fused, depth, grid, st);
-  if (d.bits == 8 && G == 64) return launch_decode_t<8, 64>(da, ea, fused, depth, grid, st);
-  if (d.bits == 8 && G == 128) return launch_decode_t<8, 128>(da, ea, fused, depth, grid, st);
+  if (d.bits == 2 && G == 32) return launch_decode_t<2, 32>(da, ea, fused, depth, grid, st, rope);
+  if (d.bits == 2 && G == 64) return launch_decode_t<2, 64>(da, ea, fused, depth, grid, st, rope);
+  if (d.bits == 2 && G == 128) return launch_decode_t<2, 128>(da, ea, fused, depth, grid, st, rope);
+  if (d.bits == 4 && G == 32) return launch_decode_t<4, 32>(da, ea, fused, depth, grid, st, rope);
+  if (d.bits == 4 && G == 64) return launch_decode_t<4, 64>(da, ea, fused, depth, grid, st, rope);
+  if (d.bits == 4 && G == 128) return launch_decode_t<4, 128>(da, ea, fused, depth, grid, st, rope);
+  if (d.bits == 8 && G == 32) return launch_decode_t<8, 32>(da, ea, fused, depth, grid, st, rope);
+  if (d.bits == 8 && G == 64) return launch_decode_t<8, 64>(da, ea, fused, depth, grid, st, rope);
+  if (d.bits == 8 && G == 128) return launch_decode_t<8, 128>(da, ea, fused, depth, grid, st, rope);
   return (int)hipErrorInvalidValue;
 }
 
@@ -1847,6 +2004,15 @@ int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, 
   const DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, workspace);
   return launch_decode_any(d, da, encode_args(d, c), false, p.depth,
                            static_cast<hipStream_t>(stream));
+}
+
+int launch_decode_rope(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
+                       const void *q, float *out, float sm_scale, double rope_base,
+                       void *workspace, void *stream) {
+  DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, workspace);
+  da.rope_log2_base = log2(rope_base);
+  return launch_decode_any(d, da, encode_args(d, c), false, p.depth,
+                           static_cast<hipStream_t>(stream), true);
 }
 
 int launch_decode_step(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,

@@ -23,7 +23,8 @@ ST_RESIDUAL_FULL, ST_CAPACITY, ST_BAD_LENGTH = 0x1, 0x2, 0x4
 # Every symbol the public header declares.
 EXPORTS = ("kivi_validate_dims", "kivi_append_kv", "kivi_flush_residual", "kivi_prefill",
            "kivi_decode_workspace_bytes", "kivi_decode_splits", "kivi_decode_step_kernels", "kivi_decode_attn",
-           "kivi_decode_step", "kivi_stream_read", "kivi_strerror")
+           "kivi_decode_attn_rope", "kivi_decode_step", "kivi_stream_read",
+           "kivi_strerror")
 
 
 class Dims(ctypes.Structure):
@@ -65,6 +66,8 @@ def lib():
         L.kivi_decode_step_kernels.argtypes = [P(Dims)]
         L.kivi_decode_attn.argtypes = [P(Dims), P(CacheStruct), V, V, ctypes.c_float, V,
                                        ctypes.c_size_t, V]
+        L.kivi_decode_attn_rope.argtypes = [P(Dims), P(CacheStruct), V, V, ctypes.c_float,
+                                            ctypes.c_double, V, ctypes.c_size_t, V]
         L.kivi_decode_step.argtypes = [P(Dims), P(CacheStruct), V, V, V, V, ctypes.c_float, V,
                                        ctypes.c_size_t, V]
         L.kivi_stream_read.argtypes = [V, ctypes.c_size_t, I32, V, V]
@@ -233,6 +236,19 @@ def decode_attn(cache, q, sm_scale, out=None, workspace=None):
     _check(lib().kivi_decode_attn(ctypes.byref(d), ctypes.byref(cache.struct()), q.data_ptr(),
                                   out.data_ptr(), ctypes.c_float(sm_scale), workspace.data_ptr(),
                                   ctypes.c_size_t(nbytes), _stream()), "kivi_decode_attn")
+    return out
+
+
+def decode_attn_rope(cache, q, sm_scale, rope_base=10000.0, out=None, workspace=None):
+    """decode_attn with the cache's keys stored before the rotary embedding:
+    each key is rotated by its position after dequantization; q is the
+    already rotated query.  fp32 output."""
+    d = cache.dims
+    out, workspace, nbytes = _decode_buffers(cache, q, out, workspace)
+    _check(lib().kivi_decode_attn_rope(ctypes.byref(d), ctypes.byref(cache.struct()), q.data_ptr(),
+                                       out.data_ptr(), ctypes.c_float(sm_scale),
+                                       ctypes.c_double(rope_base), workspace.data_ptr(),
+                                       ctypes.c_size_t(nbytes), _stream()), "kivi_decode_attn_rope")
     return out
 
 

@@ -194,6 +194,30 @@ int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kivi_decode_attn for keys stored before the rotary embedding ([P2]
+ * rotary-embedding section: quantize keys before the rotation and apply it
+ * after dequantization, since rotating first mixes an outlier channel into
+ * its partner; its list of things to do calls this a correctness matter).
+ * Every key -- quantized or in the fp16 window, exactly as
+ * kivi_append_kv / kivi_flush_residual / kivi_prefill stored it -- is
+ * rotated after dequantization by its position in the sequence: quantized
+ * tokens take positions 0 .. q_len[b] - 1, window slot r takes q_len[b] + r.
+ * Channel pair f = (2f, 2f + 1), f < head_dim / 2, turns by the angle
+ * position * rope_base^(-2f / head_dim) (the original rotary embedding; a
+ * head stored in the "rotate half" pairing maps onto it by one fixed channel
+ * permutation of queries and keys).  q must already be rotated to the new
+ * token's position.  Values are not rotated.
+ *   rope_base  > 1 and finite (10000 for Llama-2)
+ * Other arguments, layouts, workspace and errors as kivi_decode_attn;
+ * KIVI_EINVAL for a bad rope_base.  Angles are formed in fp64 and the
+ * sine and cosine taken in fp32.
+ */
+int kivi_decode_attn_rope(const kivi_dims *dims, const kivi_cache *cache,
+                          const void *q, float *out, float sm_scale,
+                          double rope_base, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
  * One whole generation step: kivi_append_kv, then kivi_decode_attn, then
  * kivi_flush_residual ([P1] section 3.1: append to the fp16 window, attend
  * over quantized and window tokens, quantize the window once it holds R

@@ -93,6 +93,13 @@ def test_entry_points_reject_bad_arguments_without_a_device():
                               fake, ctypes.c_size_t(need), None) == kivi.KIVI_EINVAL
     assert L.kivi_decode_attn(ctypes.byref(d), ctypes.byref(cs), None, fake, ctypes.c_float(1.0),
                               fake, ctypes.c_size_t(need), None) == kivi.KIVI_EINVAL
+    for base in (1.0, 0.5, float("nan"), float("inf")):
+        assert L.kivi_decode_attn_rope(ctypes.byref(d), ctypes.byref(cs), fake, fake, ctypes.c_float(1.0),
+                                       ctypes.c_double(base), fake, ctypes.c_size_t(need),
+                                       None) == kivi.KIVI_EINVAL
+    assert L.kivi_decode_attn_rope(ctypes.byref(d), ctypes.byref(cs), fake, fake, ctypes.c_float(1.0),
+                                   ctypes.c_double(1e4), fake, ctypes.c_size_t(need - 1),
+                                   None) == kivi.KIVI_ENOSPC
     # the stream-read measurement aid: null, empty, unaligned or oddly sized
     # buffers and workgroup counts outside [1, 2^20]
     sz = ctypes.c_size_t
