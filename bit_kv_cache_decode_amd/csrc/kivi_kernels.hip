@@ -696,7 +696,6 @@ struct DecSmem {
       float qs[kD];                     // sm_scale * log2(e) * q
       float qp[C::NTS][C::W * C::QPW];  // key multipliers, word-padded (ROPE: steps)
       float cz[C::NTS][C::W];
-      float zz[ROPE ? C::NTS : 1][ROPE ? C::W * C::QPW : 1];  // ROPE: zero-points
     } wave[kDecodeWaves];
     struct {
       float m[kMaxSplits], l[kMaxSplits];
@@ -704,6 +703,10 @@ struct DecSmem {
   } u;
   int ticket;
   int prog[kDecodeWaves];  // sub-chunks each wave has started (issue priority)
+  // ROPE: key zero-points of the touched tiles, word-padded like qp (kept
+  // out of the per-wave staging above so that its layout, and the 16-byte
+  // alignment of every wave's multipliers, is the same with or without)
+  alignas(16) float zz[ROPE ? kDecodeWaves : 1][ROPE ? C::NTS : 1][ROPE ? C::W * C::QPW : 1];
 };
 
 __device__ __forceinline__ void store_agent(float *p, float v) {
@@ -1584,7 +1587,7 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 2 * kDecodeWavesPerSim
     __builtin_amdgcn_wave_barrier();
     rope.init(stg.qs, w * C::CPW, a.rope_log2_base);
   }
-  auto *zz = reinterpret_cast<float(*)[C::W * C::QPW]>(&stg.zz[0][0]);
+  auto *zz = reinterpret_cast<float(*)[C::W * C::QPW]>(&sm.zz[ROPE ? wv : 0][0][0]);
 
   LaneState<C::CPW> st;
   st.m = -INFINITY;
