@@ -56,6 +56,9 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch steps eagerly instead of a graph")
+    p.add_argument("--rope", type=float, default=None, metavar="BASE",
+                   help="keys stored before the rotary embedding: the decode is "
+                        "kivi_decode_attn_rope with this base, the step its three calls")
     p.add_argument("--no-stream", action="store_true",
                    help="skip the stream-read ceiling (kivi_stream_read) measurement")
     p.add_argument("--copy-mb", type=int, default=0,
@@ -251,10 +254,21 @@ def main():
             c.q_len.copy_(q0)
             c.r_len.copy_(r0)
 
+    def decode(i, out):
+        if args.rope is None:
+            return kivi.decode_attn(copies[i], q, cfg.sm_scale, out=out, workspace=ws)
+        return kivi.decode_attn_rope(copies[i], q, cfg.sm_scale, args.rope, out=out, workspace=ws)
+
     def step(i):
         # append + decode + flush: one kernel when one workgroup covers a
-        # whole (sequence, head), else the three kernels
-        kivi.decode_step(copies[i], k_new, v_new, q, cfg.sm_scale, out=outs[i], workspace=ws)
+        # whole (sequence, head), else the three kernels (always three with
+        # keys stored before the rotary embedding)
+        if args.rope is None:
+            kivi.decode_step(copies[i], k_new, v_new, q, cfg.sm_scale, out=outs[i], workspace=ws)
+        else:
+            kivi.append_kv(copies[i], k_new, v_new)
+            decode(i, outs[i])
+            kivi.flush_residual(copies[i])
 
     # ---- warmup (eager), then back to the starting state
     for i in range(W):
@@ -297,7 +311,7 @@ def main():
     # launch cost in it (eager launches with --eager).
     phases = [
         lambda i: kivi.append_kv(copies[i], k_new, v_new),
-        lambda i: kivi.decode_attn(copies[i], q, cfg.sm_scale, out=outs[i], workspace=ws),
+        lambda i: decode(i, outs[i]),
         lambda i: kivi.flush_residual(copies[i]),
     ]
     pgraphs = []
@@ -355,7 +369,7 @@ def main():
           for _ in range(calls)]
     for i, (e0, e1) in enumerate(pc):
         e0.record()
-        kivi.decode_attn(copies[i % n_copies], q, cfg.sm_scale, out=outs[i % n_copies], workspace=ws)
+        decode(i % n_copies, outs[i % n_copies])
         e1.record()
     torch.cuda.synchronize()
     per_call = np.array([1e3 * e0.elapsed_time(e1) for e0, e1 in pc])
@@ -363,7 +377,7 @@ def main():
     torch.cuda.synchronize()
 
     step_s = wall / K
-    one_kernel = kivi.decode_step_kernels(base.dims) == 1
+    one_kernel = kivi.decode_step_kernels(base.dims) == 1 and args.rope is None
     qheads = Bt * H
     dec_bytes = wl.decode_bytes(w.q_len, r_start + 1, H, D, w.bits, cfg.group)
     achieved = dec_bytes / (decode_us * 1e-6) / 1e9
@@ -387,7 +401,9 @@ def main():
             "residual": cfg.residual,
             "context": int((w.q_len + r_start + 1).max()),
             "quantized_tokens": int(w.q_len.max()), "window_tokens": int((r_start + 1).max()),
-            "step": ("kivi_decode_step (append + decode + flush, "
+            "rope_base": args.rope,
+            "step": (("kivi_decode_step (append + decode + flush, " if args.rope is None else
+                      "kivi_append_kv + kivi_decode_attn_rope + kivi_flush_residual (")
                      + ("one kernel" if one_kernel else "three kernels")
                      + "), " + ("one HIP graph of all timed steps" if graph is not None
                                 else "eager launches")),
@@ -403,7 +419,8 @@ def main():
         "graph_replay_matches_eager": replay_ok,
         "phased_matches_step": eager_ok,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(cfg.name)},
+                     "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": measured_traffic(cfg.name) if args.rope is None else None},
     }
     if one_kernel and graph is not None:
         # the whole-step kernel itself: the step's algorithmic bytes over its
