@@ -11,6 +11,12 @@ of an fp32 buffer (``bench.py --copy-mb N`` runs one over N MiB, reading and
 writing N MiB).  Writes a Markdown table and the JSON that ``bench.py`` reads
 for ``roofline.traffic`` (only while the recorded kernel-source hash matches).
 
+``counters``: one ``rocprofv3 --pmc`` run with several instruction
+counters (``SQ_INSTS_VALU`` and the like, summed over the device per
+dispatch) as a table of per-dispatch means, with the decode's vector-ALU
+instructions per 2-bit code (lanes per wave times ``SQ_INSTS_VALU`` over the
+codes one launch dequantizes, ``--codes``).
+
 Usage (from the repository root)::
 
     python -m bit_kv_cache_decode_amd.rocprof_summary trace STATS_CSV \\
@@ -18,6 +24,8 @@ Usage (from the repository root)::
     python -m bit_kv_cache_decode_amd.rocprof_summary traffic FETCH_CSV WRITE_CSV \\
         --workload NAME --copy-mb N --fetch-command CMD --write-command CMD \\
         -o OUT.md --json OUT.json
+    python -m bit_kv_cache_decode_amd.rocprof_summary counters CSV --workload NAME \
+        --command CMD --codes N -o OUT.md
 """
 
 import argparse
@@ -30,8 +38,8 @@ import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SRC = os.path.join(HERE, "csrc", "kivi_kernels.hip")
-DECODE = "decode_kernel<2, 32, false, 2>"
-STEP = "decode_kernel<2, 32, true, 2>"
+DECODE = "decode_kernel<2, 32, false, 2, false>"
+STEP = "decode_kernel<2, 32, true, 2, false>"
 
 
 def kernel_hash():
@@ -133,6 +141,38 @@ def traffic(args):
         json.dump(out, f, indent=1)
 
 
+def counters(args):
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    names = []
+    for r in csv.DictReader(open(args.csv)):
+        if not ours(r["Kernel_Name"]):
+            continue
+        c = r["Counter_Name"]
+        if c not in names:
+            names.append(c)
+        per[short_name(r["Kernel_Name"])][c].append(float(r["Counter_Value"]))
+    lines = [f"# Instruction counters per dispatch, workload {args.workload}", "",
+             "Command (repository root, one MI355X):", "", "```", args.command, "```", "",
+             f"Kernel source sha256: `{kernel_hash()}`", "",
+             "| kernel | dispatches | " + " | ".join(names) + " |",
+             "|---|---:|" + "---:|" * len(names)]
+    for k, cs in per.items():
+        n = len(next(iter(cs.values())))
+        lines.append(f"| {k} | {n} | " + " | ".join(f"{sum(cs[c]) / len(cs[c]):.4g}" for c in names) + " |")
+    dec = next((cs for k, cs in per.items() if DECODE in k), None)
+    if dec is not None and "SQ_INSTS_VALU" in dec:
+        valu = sum(dec["SQ_INSTS_VALU"]) / len(dec["SQ_INSTS_VALU"])
+        lines += ["", f"{DECODE}: {valu:.4g} wave-level VALU instructions per dispatch, "
+                      f"{64 * valu / args.codes:.3f} lane-level VALU instructions per code "
+                      f"({args.codes} codes per launch)."]
+        if "SQ_WAVES" in dec:
+            w = sum(dec["SQ_WAVES"]) / len(dec["SQ_WAVES"])
+            lines.append(f"{w:.0f} waves per dispatch, {valu / w:.0f} VALU instructions per wave.")
+    if args.note:
+        lines += ["", args.note]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = p.add_subparsers(dest="mode", required=True)
@@ -151,8 +191,15 @@ def main():
     c.add_argument("--write-command", required=True)
     c.add_argument("-o", "--out", required=True)
     c.add_argument("--json", required=True)
+    n = sub.add_parser("counters")
+    n.add_argument("csv")
+    n.add_argument("--workload", required=True)
+    n.add_argument("--command", required=True)
+    n.add_argument("--codes", type=int, required=True)
+    n.add_argument("--note", default="")
+    n.add_argument("-o", "--out", required=True)
     a = p.parse_args()
-    trace(a) if a.mode == "trace" else traffic(a)
+    {"trace": trace, "traffic": traffic, "counters": counters}[a.mode](a)
 
 
 if __name__ == "__main__":
