@@ -199,7 +199,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         log("bench.py measures one GPU only: this build has no multi-GPU path "
-            "(decode shards by (sequence, head) with no communication; see DESIGN.md).")
+            "(decode shards by (sequence, head) with no communication).")
         sys.exit(2)
 
     import numpy as np
