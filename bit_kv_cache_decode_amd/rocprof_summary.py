@@ -144,13 +144,18 @@ def traffic(args):
 def counters(args):
     per = collections.defaultdict(lambda: collections.defaultdict(list))
     names = []
-    for r in csv.DictReader(open(args.csv)):
-        if not ours(r["Kernel_Name"]):
-            continue
+    rows = [r for r in csv.DictReader(open(args.csv)) if ours(r["Kernel_Name"])]
+    grids = collections.defaultdict(set)
+    for r in rows:
+        grids[r["Kernel_Name"]].add(r["Grid_Size"])
+    for r in rows:
         c = r["Counter_Name"]
         if c not in names:
             names.append(c)
-        per[short_name(r["Kernel_Name"])][c].append(float(r["Counter_Value"]))
+        key = short_name(r["Kernel_Name"])
+        if len(grids[r["Kernel_Name"]]) > 1:  # one row per launch shape
+            key += f" [{int(r['Grid_Size']) // int(r['Workgroup_Size'])} workgroups]"
+        per[key][c].append(float(r["Counter_Value"]))
     lines = [f"# Instruction counters per dispatch, workload {args.workload}", "",
              "Command (repository root, one MI355X):", "", "```", args.command, "```", "",
              f"Kernel source sha256: `{kernel_hash()}`", "",
@@ -160,7 +165,7 @@ def counters(args):
         n = len(next(iter(cs.values())))
         lines.append(f"| {k} | {n} | " + " | ".join(f"{sum(cs[c]) / len(cs[c]):.4g}" for c in names) + " |")
     dec = next((cs for k, cs in per.items() if DECODE in k), None)
-    if dec is not None and "SQ_INSTS_VALU" in dec:
+    if dec is not None and "SQ_INSTS_VALU" in dec and args.codes:
         valu = sum(dec["SQ_INSTS_VALU"]) / len(dec["SQ_INSTS_VALU"])
         lines += ["", f"{DECODE}: {valu:.4g} wave-level VALU instructions per dispatch, "
                       f"{64 * valu / args.codes:.3f} lane-level VALU instructions per code "
@@ -195,7 +200,7 @@ def main():
     n.add_argument("csv")
     n.add_argument("--workload", required=True)
     n.add_argument("--command", required=True)
-    n.add_argument("--codes", type=int, required=True)
+    n.add_argument("--codes", type=int, default=0)
     n.add_argument("--note", default="")
     n.add_argument("-o", "--out", required=True)
     a = p.parse_args()
