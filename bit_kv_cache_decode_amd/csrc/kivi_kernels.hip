@@ -1042,6 +1042,21 @@ struct RopeLane {
   }
 };
 
+// kh[i] = z[i] + sv[i] * (channel i's code as a masked half) over a word's
+// channels: the key dequantized (sv is the step times the code-offset
+// factor, as staged for the pre-rotation scores).
+template <int BITS, int P = 0>
+__device__ __forceinline__ void dequant_word(uint32_t u, uint32_t uh, const float *sv,
+                                             const float *z, float *kh) {
+  constexpr int HP = 16 / BITS;
+  if constexpr (P < HP) {
+    const uint32_t m = pair_bits<BITS, P>(u, uh);
+    kh[P] = mix_lo(sv[P], m, z[P]);
+    kh[P + HP] = mix_hi(sv[P + HP], m, z[P + HP]);
+    dequant_word<BITS, P + 1>(u, uh, sv, z, kh);
+  }
+}
+
 // Scores of one sub-chunk with keys stored pre-rotation: staging of the
 // touched tiles' steps (times the code-offset factor) and zero-points in
 // LDS, then per token u, the multipliers u * s and the bias u . z.
@@ -1070,21 +1085,24 @@ __device__ __forceinline__ void rope_scores(const SubLoads<BITS, G> &b, int T0, 
   for (int j = 0; j < C::NL; ++j) {
     if (j < nvl) {
       const int k = ((T0 % G) + j * C::TPL) / G;
-      float u[C::CPW], m[C::CPW];
+      float u[C::CPW], kh[C::CPW];
       rl.at(u, T0 + j * C::TPL + 4 * slot);  // the first token of the lane's quad
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (i > 0) rl.step(u);
-        float bias = 0.0f;
+        // the token's key channels, dequantized (z + s * c, the code taken as
+        // the subnormal half it is after masking, the step carrying the
+        // offset factor), then dotted with u
+        const uint32_t word = u4_get(b.kc[j], i);
+        dequant_word<BITS>(word, upper_pairs<BITS>(word), &qp[k][w * C::QPW], &zz[k][w * C::QPW],
+                           kh);
+        float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-        for (int d = 0; d < C::CPW; d += 4) {  // steps and zero-points read back from LDS
-          const float4 a4 = *reinterpret_cast<const float4 *>(&qp[k][w * C::QPW + d]);
-          const float4 z4 = *reinterpret_cast<const float4 *>(&zz[k][w * C::QPW + d]);
-          m[d] = u[d] * a4.x, m[d + 1] = u[d + 1] * a4.y;
-          m[d + 2] = u[d + 2] * a4.z, m[d + 3] = u[d + 3] * a4.w;
-          bias = fmaf(u[d], z4.x, fmaf(u[d + 1], z4.y, fmaf(u[d + 2], z4.z, fmaf(u[d + 3], z4.w, bias))));
+        for (int d = 0; d < C::CPW; d += 2) {
+          a0 = fmaf(u[d], kh[d], a0);
+          a1 = fmaf(u[d + 1], kh[d + 1], a1);
         }
-        s[4 * j + i] = lane_group_sum<C::W>(dot_word<BITS>(u4_get(b.kc[j], i), m, bias));
+        s[4 * j + i] = lane_group_sum<C::W>(a0 + a1);
       }
     } else {
 #pragma unroll
