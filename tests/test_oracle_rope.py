@@ -116,3 +116,60 @@ def test_rope_decode_differs_from_plain_decode():
     st1 = ocache.head_state(k[:1], v[:1], 0, 1, 32, 2, 64, 32)
     assert np.array_equal(orope.decode_head_rope(q, st1, 0.02, 32, 2, 10000.0),
                           ocache.decode_head(q, st1, 0.02, 32, 2))
+
+
+# ------------------------------------------------------------ planted mistakes
+# Each mutant replaces the oracle's rotation (or its decode) with a plausible
+# slip; at least one of the pins above must fail with it in place.
+
+def _rope_generic(x, positions, base, sign=1.0, half=False, expo=2.0, shift=0):
+    x = np.asarray(x, dtype=np.float64)
+    T, D = x.shape
+    f = np.arange(D // 2, dtype=np.float64)
+    th = np.float64(base) ** (-expo * f / D)
+    ang = (np.asarray(positions, dtype=np.float64)[:, None] + shift) * th[None, :]
+    c, s = np.cos(ang), sign * np.sin(ang)
+    ia, ib = (np.arange(D // 2), np.arange(D // 2) + D // 2) if half else \
+        (np.arange(0, D, 2), np.arange(1, D, 2))
+    a, b = x[:, ia], x[:, ib]
+    y = np.empty_like(x)
+    y[:, ia] = a * c - b * s
+    y[:, ib] = a * s + b * c
+    return y
+
+
+def _decode_window_restarts(q, state, alpha, group, bits, base):
+    kk, vv = ocache.context(state, group, bits)
+    ql = state["q_len"]
+    pos = np.concatenate([np.arange(ql), np.arange(kk.shape[0] - ql)])
+    return orope.attention(q, orope.rope(kk, pos, base), vv, alpha)
+
+
+_ROPE_PINS = [test_position_zero_is_the_identity,
+              test_rotation_direction_and_pairing_match_complex_multiplication,
+              test_norm_is_preserved, test_scores_depend_on_relative_position_only,
+              test_rotations_compose, test_rope_decode_of_one_token_is_its_value_row,
+              test_rope_decode_differs_from_plain_decode]
+
+
+@pytest.mark.parametrize("label,attr,mutant", [
+    ("clockwise rotation", "rope", lambda x, p, b: _rope_generic(x, p, b, sign=-1.0)),
+    ("rotate-half pairing", "rope", lambda x, p, b: _rope_generic(x, p, b, half=True)),
+    ("frequency exponent f/D", "rope", lambda x, p, b: _rope_generic(x, p, b, expo=1.0)),
+    ("positions off by one", "rope", lambda x, p, b: _rope_generic(x, p, b, shift=1)),
+    ("window positions restart at 0", "decode_head_rope", _decode_window_restarts),
+])
+def test_rope_pins_catch_planted_mistake(label, attr, mutant, monkeypatch):
+    monkeypatch.setattr(orope, attr, mutant)
+    caught = []
+    for pin in _ROPE_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught.append(pin.__name__)
+    for bits, G in [(2, 4), (4, 8)]:
+        try:
+            test_rope_decode_matches_textbook_loops(bits, G)
+        except AssertionError:
+            caught.append("textbook")
+    assert caught, f"no pin caught: {label}"
