@@ -528,13 +528,21 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
 // them again) sets q_len[b] += R, r_len[b] = 0 and clears the ticket when it
 // is done.
 constexpr int kFlushThreads = 256;
+// Window tiles a flush workgroup takes side by side (at most).  Two measured
+// best: the workgroup dispatcher starts about 230 workgroups per microsecond,
+// so 1024 tile-sized workgroups take 4.4 us only to start; two tiles per
+// workgroup halve that, four cost more in residency than they save.
+#ifndef KIVI_FLUSH_P
+#define KIVI_FLUSH_P 2
+#endif
 
-template <int BITS, int G>
-__global__ __launch_bounds__(kFlushThreads) void flush_kernel(EncodeArgs a) {
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+template <int BITS, int G, int P>
+__global__ __launch_bounds__(kFlushThreads * P) void flush_kernel(EncodeArgs a) {
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int part = tid / kFlushThreads, tile = blockIdx.x * P + part;
   const int ql = a.q_len[b], rl = a.r_len[b];
   if (!flush_ok(ql, rl, G, a.R, a.cap)) {
-    if (rl == a.R && tile == 0 && h == 0 && tid == 0)
+    if (rl == a.R && blockIdx.x == 0 && h == 0 && tid == 0)
       atomicOr(a.status, (ql < 0 || ql % G) ? KIVI_ST_BAD_LENGTH : KIVI_ST_CAPACITY);
     return;
   }
@@ -542,10 +550,12 @@ __global__ __launch_bounds__(kFlushThreads) void flush_kernel(EncodeArgs a) {
   if (tid == 0)
     ticket = __hip_atomic_fetch_add(a.tickets + (size_t)b * kTicketStride, 1u, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
-  __shared__ FlushSmem<G, G> fs;
-  flush_window<BITS, G, G, kFlushThreads>(a, (size_t)b * a.heads + h, ql, tid, fs, -1, nullptr,
-                                          nullptr, tile * G, tile * G + G);
-  if (tid == 0 && ticket == (uint32_t)(a.heads * (a.R / G)) - 1) {
+  // P tiles side by side, kFlushThreads threads and one LDS block each; they
+  // pass the same barriers in step (P divides the window's tile count)
+  __shared__ FlushSmem<G, G> fs[P];
+  flush_window<BITS, G, G, kFlushThreads>(a, (size_t)b * a.heads + h, ql, tid % kFlushThreads,
+                                          fs[part], -1, nullptr, nullptr, tile * G, tile * G + G);
+  if (tid == 0 && ticket == (uint32_t)(a.heads * (a.R / G / P)) - 1) {
     a.q_len[b] = ql + a.R;
     a.r_len[b] = 0;
     a.tickets[(size_t)b * kTicketStride] = 0u;
@@ -1917,6 +1927,26 @@ int launch_append(const kivi_dims &d, const kivi_cache &c, const void *k_new, co
   return (int)hipGetLastError();
 }
 
+// P tiles per workgroup: up to 128 window tokens (the LDS of P tile blocks)
+template <int BITS, int G>
+int launch_flush_t(const EncodeArgs &ea, dim3 grid, int P, hipStream_t st) {
+  if constexpr (4 * G <= 128) {
+    if (P == 4) {
+      hipLaunchKernelGGL((flush_kernel<BITS, G, 4>), grid, dim3(4 * kFlushThreads), 0, st, ea);
+      return (int)hipGetLastError();
+    }
+  }
+  if constexpr (2 * G <= 128) {
+    if (P == 2) {
+      hipLaunchKernelGGL((flush_kernel<BITS, G, 2>), grid, dim3(2 * kFlushThreads), 0, st, ea);
+      return (int)hipGetLastError();
+    }
+  }
+  if (P != 1) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL((flush_kernel<BITS, G, 1>), grid, dim3(kFlushThreads), 0, st, ea);
+  return (int)hipGetLastError();
+}
+
 int launch_flush(const kivi_dims &d, const kivi_cache &c, void *stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   EncodeArgs ea = encode_args(d, c);
@@ -1924,19 +1954,22 @@ int launch_flush(const kivi_dims &d, const kivi_cache &c, void *stream) {
   ea.src_v = ea.v_res;
   ea.src_tokens = d.residual;
   ea.prefill = 0;
-  const dim3 grid(d.residual / d.group, d.heads, d.batch);
-  const int G = d.group;
-  if (d.bits == 2 && G == 32) hipLaunchKernelGGL((flush_kernel<2, 32>), grid, dim3(kFlushThreads), 0, st, ea);
-  else if (d.bits == 2 && G == 64) hipLaunchKernelGGL((flush_kernel<2, 64>), grid, dim3(kFlushThreads), 0, st, ea);
-  else if (d.bits == 2 && G == 128) hipLaunchKernelGGL((flush_kernel<2, 128>), grid, dim3(kFlushThreads), 0, st, ea);
-  else if (d.bits == 4 && G == 32) hipLaunchKernelGGL((flush_kernel<4, 32>), grid, dim3(kFlushThreads), 0, st, ea);
-  else if (d.bits == 4 && G == 64) hipLaunchKernelGGL((flush_kernel<4, 64>), grid, dim3(kFlushThreads), 0, st, ea);
-  else if (d.bits == 4 && G == 128) hipLaunchKernelGGL((flush_kernel<4, 128>), grid, dim3(kFlushThreads), 0, st, ea);
-  else if (d.bits == 8 && G == 32) hipLaunchKernelGGL((flush_kernel<8, 32>), grid, dim3(kFlushThreads), 0, st, ea);
-  else if (d.bits == 8 && G == 64) hipLaunchKernelGGL((flush_kernel<8, 64>), grid, dim3(kFlushThreads), 0, st, ea);
-  else if (d.bits == 8 && G == 128) hipLaunchKernelGGL((flush_kernel<8, 128>), grid, dim3(kFlushThreads), 0, st, ea);
-  else return (int)hipErrorInvalidValue;
-  return (int)hipGetLastError();
+  const int G = d.group, tiles = d.residual / G;
+  // tiles side by side per workgroup: the most of 4, 2, 1 that divides the
+  // window's tiles and keeps to 128 tokens
+  const int pmax = min(KIVI_FLUSH_P, 128 / G);
+  const int P = tiles % 4 == 0 && pmax >= 4 ? 4 : tiles % 2 == 0 && pmax >= 2 ? 2 : 1;
+  const dim3 grid(tiles / P, d.heads, d.batch);
+  if (d.bits == 2 && G == 32) return launch_flush_t<2, 32>(ea, grid, P, st);
+  if (d.bits == 2 && G == 64) return launch_flush_t<2, 64>(ea, grid, P, st);
+  if (d.bits == 2 && G == 128) return launch_flush_t<2, 128>(ea, grid, P, st);
+  if (d.bits == 4 && G == 32) return launch_flush_t<4, 32>(ea, grid, P, st);
+  if (d.bits == 4 && G == 64) return launch_flush_t<4, 64>(ea, grid, P, st);
+  if (d.bits == 4 && G == 128) return launch_flush_t<4, 128>(ea, grid, P, st);
+  if (d.bits == 8 && G == 32) return launch_flush_t<8, 32>(ea, grid, P, st);
+  if (d.bits == 8 && G == 64) return launch_flush_t<8, 64>(ea, grid, P, st);
+  if (d.bits == 8 && G == 128) return launch_flush_t<8, 128>(ea, grid, P, st);
+  return (int)hipErrorInvalidValue;
 }
 
 int launch_prefill(const kivi_dims &d, const kivi_cache &c, const void *k, const void *v,
