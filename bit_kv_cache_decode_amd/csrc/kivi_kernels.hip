@@ -520,8 +520,9 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
   }
 }
 
-// Flush: grid (R / G, heads, batch); one workgroup of 256 threads quantizes
-// one tile of G window tokens of one (sequence, head).  Each workgroup takes
+// Flush: grid (R / (G P), heads, batch); one workgroup of P x 256 threads
+// quantizes P tiles of G window tokens of one (sequence, head), 256 threads
+// per tile (P below, chosen by the launcher).  Each workgroup takes
 // one of sequence b's tickets once it has read b's lengths (the atomic's
 // latency hides behind the window loads); the workgroup that took the last
 // one (every tile of every head has read the lengths by then, and none reads
