@@ -163,7 +163,8 @@ def counters(args):
              "|---|---:|" + "---:|" * len(names)]
     for k, cs in per.items():
         n = len(next(iter(cs.values())))
-        lines.append(f"| {k} | {n} | " + " | ".join(f"{sum(cs[c]) / len(cs[c]):.4g}" for c in names) + " |")
+        cells = [f"{sum(cs[c]) / len(cs[c]):.4g}" if cs.get(c) else "-" for c in names]
+        lines.append(f"| {k} | {n} | " + " | ".join(cells) + " |")
     dec = next((cs for k, cs in per.items() if DECODE in k), None)
     if dec is not None and "SQ_INSTS_VALU" in dec and args.codes:
         valu = sum(dec["SQ_INSTS_VALU"]) / len(dec["SQ_INSTS_VALU"])
