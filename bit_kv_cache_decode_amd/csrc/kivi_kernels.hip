@@ -1466,12 +1466,17 @@ __device__ __forceinline__ void flush_regs_keys(const EncodeArgs &ea, const RegF
 
 // DEPTH: sub-chunks whose loads each wave keeps in flight.  2 when the grid
 // is one workgroup per compute unit; 1 when it is larger, where the smaller
-// register footprint lets two or three workgroups share a compute unit
-// (measured on the 13B layer, 640 workgroups: 37 us at depth 1 against 45 us
-// at depth 2; on the 7B layer, 256 workgroups, depth 2 is the faster).
+// register footprint lets three workgroups share a compute unit (measured on
+// the 13B layer, 640 workgroups: 37 us at depth 1 against 45 us at depth 2;
+// on the 7B layer, 256 workgroups, depth 2 is the faster).  Depth 1 asks for
+// six waves per SIMD, which caps it at 80 VGPRs (registers are allocated in
+// blocks of 8 out of 512): at 82 it held only five, two workgroups per
+// compute unit, and the 13B layer's last 128 workgroups ran as a second
+// round (per-workgroup timestamps: started at 22 us); with three per
+// compute unit all 640 start at once (37.7 -> 34.3 us).
 // ROPE: keys are stored before the rotary embedding (RopeLane above).
 template <int BITS, int G, bool FUSED, int DEPTH, bool ROPE = false>
-__global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 2 * kDecodeWavesPerSimd : kDecodeWavesPerSimd) void decode_kernel(
+__global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 3 * kDecodeWavesPerSimd : kDecodeWavesPerSimd) void decode_kernel(
     DecodeArgs a, EncodeArgs ea) {
   constexpr int kDecodeDepth = DEPTH;
   using C = DecCfg<BITS, G>;
