@@ -1476,7 +1476,7 @@ __device__ __forceinline__ void flush_regs_keys(const EncodeArgs &ea, const RegF
 // compute unit all 640 start at once (37.7 -> 34.3 us).
 // ROPE: keys are stored before the rotary embedding (RopeLane above).
 template <int BITS, int G, bool FUSED, int DEPTH, bool ROPE = false>
-__global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? 3 * kDecodeWavesPerSimd : kDecodeWavesPerSimd) void decode_kernel(
+__global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDecodeWavesPerSimd : kDecodeWavesPerSimd) void decode_kernel(
     DecodeArgs a, EncodeArgs ea) {
   constexpr int kDecodeDepth = DEPTH;
   using C = DecCfg<BITS, G>;
@@ -1884,10 +1884,18 @@ int launch_decode_t(const DecodeArgs &da, const EncodeArgs &ea, bool fused, int 
                     hipStream_t st, bool rope) {
   const dim3 blk(kDecodeThreads);
   if (rope) {
-    // keys stored pre-rotation (never the whole step): always two sub-chunks
-    // in flight, whose register budget (one workgroup per compute unit)
-    // holds the rotation's per-lane state at B=2 without spilling
+    // keys stored pre-rotation (never the whole step).  At B=2 always two
+    // sub-chunks in flight: only that register budget (one workgroup per
+    // compute unit) holds the rotation's per-lane state without spilling.
+    // At B=4 and 8 large grids take depth 1 at two workgroups per compute
+    // unit (108 and 79 VGPRs), as the plain decode does.
     if (fused) return (int)hipErrorInvalidValue;
+    if constexpr (BITS >= 4) {
+      if (depth == 1) {
+        hipLaunchKernelGGL((decode_kernel<BITS, G, false, 1, true>), grid, blk, 0, st, da, ea);
+        return (int)hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((decode_kernel<BITS, G, false, 2, true>), grid, blk, 0, st, da, ea);
     return (int)hipGetLastError();
   }
