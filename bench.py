@@ -59,6 +59,9 @@ def parse_args():
     p.add_argument("--rope", type=float, default=None, metavar="BASE",
                    help="keys stored before the rotary embedding: the decode is "
                         "kivi_decode_attn_rope with this base, the step its three calls")
+    p.add_argument("--sink", type=int, default=0, metavar="N",
+                   help="N fp16 attention-sink tokens ahead of the cache: the decode is "
+                        "kivi_decode_attn_sink, the step its three calls")
     p.add_argument("--no-stream", action="store_true",
                    help="skip the stream-read ceiling (kivi_stream_read) measurement")
     p.add_argument("--copy-mb", type=int, default=0,
@@ -226,6 +229,10 @@ def main():
     k_new = torch.from_numpy(k_new).cuda()   # [batch, heads, D]
     v_new = torch.from_numpy(v_new).cuda()
     q = torch.from_numpy(w.q).cuda()
+    if args.sink and args.rope is not None:
+        log("--sink and --rope cannot be combined (the sink decode has no rotary embedding)")
+        sys.exit(2)
+    k_sink, v_sink = (torch.from_numpy(x).cuda() for x in wl.sink_tokens(w, args.sink))
     del kt, vt
     torch.cuda.synchronize()
     assert base.status_bits() == 0
@@ -255,6 +262,9 @@ def main():
             c.r_len.copy_(r0)
 
     def decode(i, out):
+        if args.sink:
+            return kivi.decode_attn_sink(copies[i], q, cfg.sm_scale, k_sink, v_sink, out=out,
+                                         workspace=ws)
         if args.rope is None:
             return kivi.decode_attn(copies[i], q, cfg.sm_scale, out=out, workspace=ws)
         return kivi.decode_attn_rope(copies[i], q, cfg.sm_scale, args.rope, out=out, workspace=ws)
@@ -262,8 +272,8 @@ def main():
     def step(i):
         # append + decode + flush: one kernel when one workgroup covers a
         # whole (sequence, head), else the three kernels (always three with
-        # keys stored before the rotary embedding)
-        if args.rope is None:
+        # keys stored before the rotary embedding or with a sink)
+        if args.rope is None and not args.sink:
             kivi.decode_step(copies[i], k_new, v_new, q, cfg.sm_scale, out=outs[i], workspace=ws)
         else:
             kivi.append_kv(copies[i], k_new, v_new)
@@ -377,9 +387,11 @@ def main():
     torch.cuda.synchronize()
 
     step_s = wall / K
-    one_kernel = kivi.decode_step_kernels(base.dims) == 1 and args.rope is None
+    plain = args.rope is None and not args.sink
+    one_kernel = kivi.decode_step_kernels(base.dims) == 1 and plain
     qheads = Bt * H
-    dec_bytes = wl.decode_bytes(w.q_len, r_start + 1, H, D, w.bits, cfg.group)
+    dec_bytes = (wl.decode_bytes(w.q_len, r_start + 1, H, D, w.bits, cfg.group)
+                 + Bt * H * args.sink * D * 2 * 2)   # fp16 sink keys and values
     achieved = dec_bytes / (decode_us * 1e-6) / 1e9
     result = {
         "metric": METRIC,
@@ -401,9 +413,10 @@ def main():
             "residual": cfg.residual,
             "context": int((w.q_len + r_start + 1).max()),
             "quantized_tokens": int(w.q_len.max()), "window_tokens": int((r_start + 1).max()),
-            "rope_base": args.rope,
-            "step": (("kivi_decode_step (append + decode + flush, " if args.rope is None else
-                      "kivi_append_kv + kivi_decode_attn_rope + kivi_flush_residual (")
+            "rope_base": args.rope, "sink_tokens": args.sink,
+            "step": (("kivi_decode_step (append + decode + flush, " if plain else
+                      "kivi_append_kv + kivi_decode_attn_%s + kivi_flush_residual ("
+                      % ("sink" if args.sink else "rope"))
                      + ("one kernel" if one_kernel else "three kernels")
                      + "), " + ("one HIP graph of all timed steps" if graph is not None
                                 else "eager launches")),
@@ -420,7 +433,7 @@ def main():
         "phased_matches_step": eager_ok,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": measured_traffic(cfg.name) if args.rope is None else None},
+                     "traffic": measured_traffic(cfg.name) if plain else None},
     }
     if one_kernel and graph is not None:
         # the whole-step kernel itself: the step's algorithmic bytes over its

@@ -20,6 +20,7 @@ constexpr double kWorkgroupOverhead = 2.0;
 constexpr int kMaxSplits = 64;
 constexpr int kMaxResidual = 4096;
 constexpr int32_t kMaxStreamWorkgroups = 1 << 20;
+constexpr int32_t kMaxSink = 4096;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -146,6 +147,22 @@ int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache, const void 
   const kivi::DecodePlan p = kivi::decode_plan(*dims);
   if (workspace_bytes < p.bytes) return KIVI_ENOSPC;
   return kivi::hip_rc(kivi::launch_decode(*dims, *cache, p, q, out, sm_scale, workspace, stream));
+}
+
+int kivi_decode_attn_sink(const kivi_dims *dims, const kivi_cache *cache, const void *k_sink,
+                          const void *v_sink, int32_t n_sink, const void *q, float *out,
+                          float sm_scale, void *workspace, size_t workspace_bytes, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache) || !q || !out || !workspace) return KIVI_EINVAL;
+  if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
+    return KIVI_EINVAL;
+  if (n_sink < 0 || n_sink > kivi::kMaxSink || (n_sink > 0 && (!k_sink || !v_sink)))
+    return KIVI_EINVAL;
+  const kivi::DecodePlan p = kivi::decode_plan(*dims);
+  if (workspace_bytes < p.bytes) return KIVI_ENOSPC;
+  return kivi::hip_rc(kivi::launch_decode_sink(*dims, *cache, p, k_sink, v_sink, n_sink, q, out,
+                                               sm_scale, workspace, stream));
 }
 
 int kivi_decode_attn_rope(const kivi_dims *dims, const kivi_cache *cache, const void *q,

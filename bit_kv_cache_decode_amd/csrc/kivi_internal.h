@@ -65,6 +65,9 @@ int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
                   void *stream);
 int launch_stream_read(const void *src, size_t bytes, int workgroups, uint32_t *sink,
                        void *stream);
+int launch_decode_sink(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
+                       const void *k_sink, const void *v_sink, int n_sink, const void *q,
+                       float *out, float sm_scale, void *workspace, void *stream);
 int launch_decode_rope(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
                        const void *q, float *out, float sm_scale, double rope_base,
                        void *workspace, void *stream);

@@ -672,6 +672,10 @@ struct DecodeArgs {
   float qscale;  // sm_scale * log2(e)
   int heads, R, cap, splits, win_per_wave, part_stride;
   double rope_log2_base;  // log2 of the rotary base (ROPE kernels only)
+  // fp16 sink tokens [batch][heads][n_sink][D] (plain decode only; n_sink 0
+  // elsewhere), sink_per_wave of them per wave
+  const half_t *k_sink, *v_sink;
+  int n_sink, sink_per_wave;
 };
 
 constexpr int kMaxSplits = 128;
@@ -1566,6 +1570,7 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
   ws.lane_voff = (uint32_t)(slot * kD + w * C::CPW) * 2;
   const int wsteps = ws.end > ws.begin ? (ws.end - ws.begin + WC::STEP - 1) / WC::STEP : 0;
 
+
   // The query (every wave reads it: lane i holds channels 2i, 2i + 1),
   // then kDecodeDepth quantized sub-chunks.  Each sub-chunk's registers are
   // refilled with sub-chunk c + kDecodeDepth as soon as sub-chunk c is done,
@@ -1722,6 +1727,31 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
   __builtin_amdgcn_s_setprio(0);
 #endif
   if (!early) window();
+  // fp16 sink tokens (the sequence's first tokens, kept unquantized ahead of
+  // the quantized ones): this wave's share [gw * sink_per_wave, ...), one
+  // load round trip per step (set up here, so that nothing of it is live
+  // during the quantized stream)
+  if constexpr (!FUSED && !ROPE) {
+    const int sb = qs.gw * a.sink_per_wave, se = min(a.n_sink, sb + a.sink_per_wave);
+    if (se > sb) {
+      WinStream<BITS, G> ss;
+      ss.kr = a.k_sink + bh * a.n_sink * kD;
+      ss.vr = a.v_sink + bh * a.n_sink * kD;
+      ss.begin = sb;
+      ss.end = se;
+      ss.bytes = (uint32_t)se * (kD * 2);
+      ss.lane_voff = (uint32_t)(slot * kD + w * C::CPW) * 2;
+      __builtin_amdgcn_wave_barrier();
+      float qv[C::CPW];
+#pragma unroll
+      for (int i = 0; i < C::CPW; ++i) qv[i] = stg.qs[w * C::CPW + i];
+      for (int i = 0; sb + i * WC::STEP < se; ++i) {
+        WinStep<BITS, G> x;
+        ss.issue(x, i);
+        window_step<BITS, G>(x, sb + i * WC::STEP + slot < se, qv, st);
+      }
+    }
+  }
   wave_publish<C::CPW, C::W, C::W == 8>(sm.fin.acc[wv], sm.fin.bias[wv], sm.fin.m[wv],
                                          sm.fin.l[wv], st.m, st.l, st.acc, st.bias);
   __syncthreads();
@@ -2070,6 +2100,21 @@ int launch_stream_read(const void *src, size_t bytes, int workgroups, uint32_t *
 int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, const void *q,
                   float *out, float sm_scale, void *workspace, void *stream) {
   const DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, workspace);
+  return launch_decode_any(d, da, encode_args(d, c), false, p.depth,
+                           static_cast<hipStream_t>(stream));
+}
+
+int launch_decode_sink(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
+                       const void *k_sink, const void *v_sink, int n_sink, const void *q,
+                       float *out, float sm_scale, void *workspace, void *stream) {
+  DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, workspace);
+  if (n_sink > 0) {
+    const int waves = kDecodeWaves * p.splits;
+    da.k_sink = static_cast<const half_t *>(k_sink);
+    da.v_sink = static_cast<const half_t *>(v_sink);
+    da.n_sink = n_sink;
+    da.sink_per_wave = ((n_sink + waves - 1) / waves + 7) / 8 * 8;
+  }
   return launch_decode_any(d, da, encode_args(d, c), false, p.depth,
                            static_cast<hipStream_t>(stream));
 }

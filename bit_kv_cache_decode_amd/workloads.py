@@ -140,6 +140,24 @@ def generate(number, bits=None, batch=None):
                     q_len=ql.astype(np.int32), r_len=rl.astype(np.int32), seed=seed)
 
 
+def sink_tokens(w, n_sink, score=24.0):
+    """fp16 attention-sink rows (k_sink, v_sink [batch, heads, n_sink, D])
+    for workload ``w``, drawn from seed 3000 + workload number: keys
+    N(0, 3^2) and values N(0, 1), except that sink token 0's key is
+    ``score / sm_scale * q / |q|^2`` for its head, so that its score is about
+    ``score`` (the large attention weight a sink token draws)."""
+    cfg = w.config
+    nb, H, D = w.q.shape
+    rng = np.random.Generator(np.random.PCG64(3000 + cfg.number))
+    ks = rng.standard_normal((nb, H, n_sink, D), dtype=np.float32) * np.float32(3.0)
+    vs = rng.standard_normal((nb, H, n_sink, D), dtype=np.float32)
+    if n_sink:
+        q = w.q.astype(np.float64)
+        n2 = np.maximum((q * q).sum(-1, keepdims=True), 1e-30)
+        ks[:, :, 0] = (score / cfg.sm_scale * q / n2).astype(np.float32)
+    return ks.astype(np.float16), vs.astype(np.float16)
+
+
 # ---------------------------------------------------------------- byte model
 
 def fp16_kv_cache_bytes(batch, seq_len, layers, hidden):

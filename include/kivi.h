@@ -12,8 +12,11 @@
  *        what quantization error is made of (uniform min/step quantizer,
  *        step = range / (2^B - 1), error <= step/2), section on keys (outliers
  *        sit in fixed channels, so keys are grouped per channel), section on
- *        values (values are grouped per token), section on the systems tax
- *        (recent tokens stay full precision until enough accumulate).
+ *        values (values are grouped per token), section on rotary
+ *        embeddings (quantize keys before the rotation), section on the
+ *        systems tax (recent tokens stay full precision until enough
+ *        accumulate), future-directions section (high-precision windows for
+ *        the recent and the attention-sink tokens).
  *
  * Everything here is asynchronous on the caller's HIP stream.  The library
  * never allocates, frees or synchronises; every buffer is caller-owned device
@@ -192,6 +195,29 @@ int kivi_decode_step_kernels(const kivi_dims *dims);
 int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache,
                      const void *q, float *out, float sm_scale,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kivi_decode_attn with an fp16 attention-sink segment ([P2]
+ * future-directions section: besides the window of recent tokens, a
+ * high-precision window is kept for the attention-sink tokens, the first
+ * tokens of the sequence).  The attention runs over the n_sink sink tokens,
+ * then the q_len[b] quantized tokens, then the r_len[b] window tokens:
+ *   out = softmax(sm_scale * q . [K_sink; K^; K_res]^T) . [V_sink; V^; V_res]
+ *   k_sink, v_sink  device fp16 [batch][heads][n_sink][head_dim], contiguous,
+ *                   owned by the caller and only read (typically the
+ *                   prompt's first n_sink rows, with the cache built from
+ *                   the rest); the same n_sink for every sequence
+ *   n_sink          0 .. 4096; 0 gives exactly kivi_decode_attn (the
+ *                   pointers are then not read and may be NULL)
+ * Positions play no part (no rotary embedding here).  Other arguments,
+ * layouts, workspace and errors as kivi_decode_attn; KIVI_EINVAL for n_sink
+ * out of range or a NULL sink pointer with n_sink > 0.  An empty cache with
+ * n_sink > 0 attends over the sink alone.
+ */
+int kivi_decode_attn_sink(const kivi_dims *dims, const kivi_cache *cache,
+                          const void *k_sink, const void *v_sink, int32_t n_sink,
+                          const void *q, float *out, float sm_scale,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * kivi_decode_attn for keys stored before the rotary embedding ([P2]

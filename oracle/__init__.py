@@ -21,6 +21,8 @@ path computes, written from the pages' definitions:
   and the key, score and output errors each gives (analysis, not parity).
 * ``rope``       -- the rotary embedding applied to keys after dequantization
   (keys stored before the rotation) and the decode that uses it.
+* ``sink``       -- the decode over an fp16 attention-sink segment followed by
+  the cache's tokens.
 
 Precision: the quantizer runs the fixed fp32 operation sequence stated in
 ``quantizer``; attention runs in fp64 on the exactly dequantized values.
@@ -30,4 +32,4 @@ fix (hand-worked cases, brute force, closed forms, invariants); none is
 "parity unpinned".
 """
 
-from . import attention, axis_ablation, cache, packing, quantizer, rope  # noqa: F401
+from . import attention, axis_ablation, cache, packing, quantizer, rope, sink  # noqa: F401

@@ -29,6 +29,25 @@ def test_library_exports_every_declared_function():
     assert sorted(kivi.EXPORTS) == names
 
 
+def test_binding_declares_argument_types_of_every_entry_point():
+    """ctypes passes an undeclared argument as a C int: a device pointer would
+    arrive cut to 32 bits.  Every entry point's argument list is declared,
+    with one ctypes type per parameter of its C declaration."""
+    L = kivi.lib()
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name in kivi.EXPORTS:
+        types = getattr(L, name).argtypes
+        assert types is not None, name
+        params = re.search(name + r"\s*\(([^)]*)\)", text).group(1)
+        n = 0 if params.strip() in ("", "void") else params.count(",") + 1
+        assert len(types) == n, (name, len(types), n)
+        # pointer parameters are declared as pointers, never as integers
+        for t, prm in zip(types, params.split(",")):
+            if "*" in prm:
+                assert t is ctypes.c_void_p or t is ctypes.c_char_p or \
+                    issubclass(t, ctypes._Pointer), (name, prm)
+
+
 def test_validate_dims_codes():
     ok = kivi.make_dims(8, 32, 128, 2, 32, 128, 4096)
     assert kivi.validate_dims(ok) == kivi.KIVI_OK
@@ -99,6 +118,19 @@ def test_entry_points_reject_bad_arguments_without_a_device():
                                        None) == kivi.KIVI_EINVAL
     assert L.kivi_decode_attn_rope(ctypes.byref(d), ctypes.byref(cs), fake, fake, ctypes.c_float(1.0),
                                    ctypes.c_double(1e4), fake, ctypes.c_size_t(need - 1),
+                                   None) == kivi.KIVI_ENOSPC
+    # the sink decode: n_sink outside [0, 4096], a NULL sink with n_sink > 0,
+    # a short workspace
+    i32 = ctypes.c_int32
+    for n, ks, vs in ((-1, fake, fake), (4097, fake, fake), (4, None, fake), (4, fake, None)):
+        assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(cs), ks, vs, i32(n), fake, fake,
+                                       ctypes.c_float(1.0), fake, ctypes.c_size_t(need),
+                                       None) == kivi.KIVI_EINVAL
+    assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(cs), fake, fake, i32(4), fake, fake,
+                                   ctypes.c_float(float("nan")), fake, ctypes.c_size_t(need),
+                                   None) == kivi.KIVI_EINVAL
+    assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(cs), fake, fake, i32(4), fake, fake,
+                                   ctypes.c_float(1.0), fake, ctypes.c_size_t(need - 1),
                                    None) == kivi.KIVI_ENOSPC
     # the stream-read measurement aid: null, empty, unaligned or oddly sized
     # buffers and workgroup counts outside [1, 2^20]

@@ -1,0 +1,97 @@
+"""GPU parity of kivi_decode_attn_sink (an fp16 attention-sink segment
+ahead of the cache's tokens; the guide's future-directions section) against
+the oracle's fp64 decode, to the plain decode's tolerance (max-abs 2e-3,
+relative L2 1e-3).  Sink rows come from the seeded sink generator: sink
+token 0 draws a large score, the rest are N(0, 9) keys and N(0, 1) values."""
+
+import numpy as np
+import pytest
+import torch
+
+from bit_kv_cache_decode_amd import kivi
+from bit_kv_cache_decode_amd import workloads as wl
+from oracle import cache as ocache
+from oracle import sink as osink
+from tests.gpu_common import assert_within_tolerance, gpu_cache, oracle_head, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(c, w, n_sink, sm_scale=None):
+    ks, vs = wl.sink_tokens(w, n_sink)
+    q = torch.from_numpy(w.q).cuda()
+    scale = w.config.sm_scale if sm_scale is None else sm_scale
+    out = kivi.decode_attn_sink(c, q, scale, torch.from_numpy(ks).cuda(),
+                                torch.from_numpy(vs).cuda())
+    torch.cuda.synchronize()
+    assert c.status_bits() == 0
+    return out.cpu().numpy(), ks, vs
+
+
+def _check(out, w, ks, vs, heads, state=oracle_head):
+    G = w.config.group
+    for b, h in heads:
+        st = state(w, b, h)
+        ref = osink.decode_head_sink(w.q[b, h], st, ks[b, h], vs[b, h], w.config.sm_scale, G,
+                                     w.bits)
+        assert_within_tolerance(out[b, h], ref, f"b={b} h={h}")
+
+
+@pytest.mark.parametrize("n_sink", [4, 64])
+def test_sink_llama2_7b_shape_all_heads(n_sink):
+    w = workload(2, batch=2)
+    c = gpu_cache(w)
+    out, ks, vs = _run(c, w, n_sink)
+    _check(out, w, ks, vs, [(b, h) for b in range(2) for h in range(32)])
+    plain = kivi.decode_attn(c, torch.from_numpy(w.q).cuda(), 1.0).cpu().numpy()
+    assert np.abs(out - plain).max() > 1e-2   # the sink took part
+
+
+def test_no_sink_is_bit_identical_to_decode_attn():
+    w = workload(2, batch=2)
+    c = gpu_cache(w)
+    out, _, _ = _run(c, w, 0)
+    plain = kivi.decode_attn(c, torch.from_numpy(w.q).cuda(), 1.0).cpu().numpy()
+    assert np.array_equal(out, plain)
+
+
+@pytest.mark.parametrize("q_len,r_len,n_sink", [(0, 0, 1), (0, 0, 33), (0, 5, 7), (32, 0, 8),
+                                                (4064, 31, 4096), (3968, 128, 2)])
+def test_sink_edge_lengths(q_len, r_len, n_sink):
+    """Empty caches (the sink alone), one sink token, shares that leave most
+    waves without sink tokens, and the largest sink (512 tokens a wave)."""
+    w = workload(2, batch=1)
+    c = gpu_cache(w, q_len=[q_len], r_len=[r_len])
+    out, ks, vs = _run(c, w, n_sink)
+
+    def state(w, b, h):
+        return ocache.head_state(w.k[b, h], w.v[b, h], q_len, r_len, 32, 2, 4096, 128)
+    _check(out, w, ks, vs, [(0, 0), (0, 17), (0, 31)], state)
+
+
+def test_sink_with_splits():
+    """A capacity that splits each (sequence, head) over several workgroups:
+    the sink is shared over every split's waves and merged with the rest."""
+    w = workload(2, batch=2)
+    c = gpu_cache(w, capacity=65536)
+    assert kivi.decode_splits(c.dims) > 1
+    out, ks, vs = _run(c, w, 100)
+    _check(out, w, ks, vs, [(0, 0), (1, 9), (1, 31)])
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_sink_13b_shape_sampled_heads(bits):
+    """640 (sequence, head) pairs: the kernels of grids above one workgroup
+    per compute unit."""
+    w = workload(3, bits=bits)
+    c = gpu_cache(w)
+    out, ks, vs = _run(c, w, 16)
+    _check(out, w, ks, vs, [(0, 0), (7, 21), (15, 39)])
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_sink_long_context_sampled_heads(bits):
+    w = workload(5, bits=bits)
+    c = gpu_cache(w)
+    out, ks, vs = _run(c, w, 4)
+    _check(out, w, ks, vs, [(0, 0), (0, 31)])
