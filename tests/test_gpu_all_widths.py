@@ -1,6 +1,7 @@
 """Every compiled code width and group size, B in {2, 4, 8} x G in {32, 64,
 128}, on a small ragged batch through the C ABI against the oracle: the
-prefilled cache bit for bit, the plain and the pre-rotation-key decode within
+prefilled cache bit for bit, the plain, the pre-rotation-key and the
+attention-sink (5 fp16 sink tokens) decode within
 max-abs 2e-3 / relative L2 1e-3 of the fp64 oracle, and a flush of the full
 windows bit for bit.  Batch 9 x 32 heads (288 pairs) runs the decode with one
 sub-chunk in flight per wave (more workgroups than compute units), batch 2
@@ -13,6 +14,7 @@ import torch
 from bit_kv_cache_decode_amd import kivi
 from oracle import cache as ocache
 from oracle import rope as orope
+from oracle import sink as osink
 from tests.gpu_common import assert_head_bit_exact, assert_within_tolerance, head_buffers
 
 pytestmark = pytest.mark.gpu
@@ -42,13 +44,19 @@ def _case(bits, G, batch, seed):
 @pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_width_group_combination(bits, G, batch):
-    k, v, q, lens, win = _case(bits, G, batch, 3000 + 10 * bits + G + batch)
+    seed = 3000 + 10 * bits + G + batch
+    k, v, q, lens, win = _case(bits, G, batch, seed)
     c = kivi.KiviCache(batch, H, D, bits, G, R, CAP)
     kivi.prefill(c, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
                  torch.from_numpy(lens).cuda(), torch.from_numpy(win).cuda())
     qt = torch.from_numpy(q).cuda()
     out = kivi.decode_attn(c, qt, 1.0).cpu().numpy()
     out_r = kivi.decode_attn_rope(c, qt, 1.0, 10000.0).cpu().numpy()
+    srng = np.random.default_rng(seed + 1)
+    sk = (srng.standard_normal((batch, H, 5, D), np.float32) * 3).astype(np.float16)
+    sv = srng.standard_normal((batch, H, 5, D), np.float32).astype(np.float16)
+    out_s = kivi.decode_attn_sink(c, qt, 1.0, torch.from_numpy(sk).cuda(),
+                                  torch.from_numpy(sv).cuda()).cpu().numpy()
     assert c.status_bits() == 0
     heads = [(b, h) for b in range(batch) for h in (0, 13, 31)]
     for b, h in heads:
@@ -60,6 +68,8 @@ def test_width_group_combination(bits, G, batch):
         assert_within_tolerance(out[b, h], ref, f"plain b={b} h={h}")
         ref_r = orope.decode_head_rope(q[b, h], st, 1.0, G, bits, 10000.0)
         assert_within_tolerance(out_r[b, h], ref_r, f"rope b={b} h={h}")
+        ref_s = osink.decode_head_sink(q[b, h], st, sk[b, h], sv[b, h], 1.0, G, bits)
+        assert_within_tolerance(out_s[b, h], ref_s, f"sink b={b} h={h}")
     # flush: only the full window moves, bit for bit as the oracle encodes it
     kivi.flush_residual(c)
     torch.cuda.synchronize()
