@@ -39,9 +39,15 @@ int check_dims(const kivi_dims *d) {
   return supported(*d) ? KIVI_OK : KIVI_EUNSUPPORTED;
 }
 
+// Non-null and aligned: the kernels move fp16 rows, codes and scales in
+// 16-byte vectors, and 32-bit lengths, counters and outputs one by one.
+bool a16(const void *p) { return p && ((uintptr_t)p & 15) == 0; }
+bool a4(const void *p) { return p && ((uintptr_t)p & 3) == 0; }
+
 bool cache_ok(const kivi_cache *c) {
-  return c && c->k_codes && c->k_scale && c->k_zero && c->v_codes && c->v_scale && c->v_zero &&
-         c->k_res && c->v_res && c->q_len && c->r_len && c->status && c->tickets;
+  return c && a16(c->k_codes) && a16(c->k_scale) && a16(c->k_zero) && a16(c->v_codes) &&
+         a16(c->v_scale) && a16(c->v_zero) && a16(c->k_res) && a16(c->v_res) && a4(c->q_len) &&
+         a4(c->r_len) && a4(c->status) && a4(c->tickets);
 }
 
 int hip_rc(int rc) { return rc == 0 ? KIVI_OK : KIVI_EHIP; }
@@ -100,7 +106,7 @@ int kivi_append_kv(const kivi_dims *dims, const kivi_cache *cache, const void *k
                    const void *v_new, void *stream) {
   const int rc = kivi::check_dims(dims);
   if (rc != KIVI_OK) return rc;
-  if (!kivi::cache_ok(cache) || !k_new || !v_new) return KIVI_EINVAL;
+  if (!kivi::cache_ok(cache) || !kivi::a16(k_new) || !kivi::a16(v_new)) return KIVI_EINVAL;
   return kivi::hip_rc(kivi::launch_append(*dims, *cache, k_new, v_new, stream));
 }
 
@@ -115,8 +121,9 @@ int kivi_prefill(const kivi_dims *dims, const kivi_cache *cache, const void *k, 
                  int32_t src_len, const int32_t *len, const int32_t *res, void *stream) {
   const int rc = kivi::check_dims(dims);
   if (rc != KIVI_OK) return rc;
-  if (!kivi::cache_ok(cache) || !len || src_len < 0) return KIVI_EINVAL;
-  if (src_len > 0 && (!k || !v)) return KIVI_EINVAL;
+  if (!kivi::cache_ok(cache) || !kivi::a4(len) || src_len < 0) return KIVI_EINVAL;
+  if (res && !kivi::a4(res)) return KIVI_EINVAL;
+  if (src_len > 0 && (!kivi::a16(k) || !kivi::a16(v))) return KIVI_EINVAL;
   return kivi::hip_rc(kivi::launch_prefill(*dims, *cache, k, v, src_len, len, res, stream));
 }
 
@@ -141,7 +148,8 @@ int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache, const void 
                      float sm_scale, void *workspace, size_t workspace_bytes, void *stream) {
   const int rc = kivi::check_dims(dims);
   if (rc != KIVI_OK) return rc;
-  if (!kivi::cache_ok(cache) || !q || !out || !workspace) return KIVI_EINVAL;
+  if (!kivi::cache_ok(cache) || !kivi::a16(q) || !kivi::a4(out) || !kivi::a16(workspace))
+    return KIVI_EINVAL;
   if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
     return KIVI_EINVAL;
   const kivi::DecodePlan p = kivi::decode_plan(*dims);
@@ -154,10 +162,12 @@ int kivi_decode_attn_sink(const kivi_dims *dims, const kivi_cache *cache, const 
                           float sm_scale, void *workspace, size_t workspace_bytes, void *stream) {
   const int rc = kivi::check_dims(dims);
   if (rc != KIVI_OK) return rc;
-  if (!kivi::cache_ok(cache) || !q || !out || !workspace) return KIVI_EINVAL;
+  if (!kivi::cache_ok(cache) || !kivi::a16(q) || !kivi::a4(out) || !kivi::a16(workspace))
+    return KIVI_EINVAL;
   if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
     return KIVI_EINVAL;
-  if (n_sink < 0 || n_sink > kivi::kMaxSink || (n_sink > 0 && (!k_sink || !v_sink)))
+  if (n_sink < 0 || n_sink > kivi::kMaxSink ||
+      (n_sink > 0 && (!kivi::a16(k_sink) || !kivi::a16(v_sink))))
     return KIVI_EINVAL;
   const kivi::DecodePlan p = kivi::decode_plan(*dims);
   if (workspace_bytes < p.bytes) return KIVI_ENOSPC;
@@ -170,7 +180,8 @@ int kivi_decode_attn_rope(const kivi_dims *dims, const kivi_cache *cache, const 
                           size_t workspace_bytes, void *stream) {
   const int rc = kivi::check_dims(dims);
   if (rc != KIVI_OK) return rc;
-  if (!kivi::cache_ok(cache) || !q || !out || !workspace) return KIVI_EINVAL;
+  if (!kivi::cache_ok(cache) || !kivi::a16(q) || !kivi::a4(out) || !kivi::a16(workspace))
+    return KIVI_EINVAL;
   if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
     return KIVI_EINVAL;
   if (!(rope_base > 1.0) || rope_base == 1.0 / 0.0) return KIVI_EINVAL;
@@ -185,7 +196,9 @@ int kivi_decode_step(const kivi_dims *dims, const kivi_cache *cache, const void 
                      void *workspace, size_t workspace_bytes, void *stream) {
   const int rc = kivi::check_dims(dims);
   if (rc != KIVI_OK) return rc;
-  if (!kivi::cache_ok(cache) || !k_new || !v_new || !q || !out || !workspace) return KIVI_EINVAL;
+  if (!kivi::cache_ok(cache) || !kivi::a16(k_new) || !kivi::a16(v_new) || !kivi::a16(q) ||
+      !kivi::a4(out) || !kivi::a16(workspace))
+    return KIVI_EINVAL;
   if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
     return KIVI_EINVAL;
   const kivi::DecodePlan p = kivi::decode_plan(*dims);

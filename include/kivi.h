@@ -21,7 +21,12 @@
  * Everything here is asynchronous on the caller's HIP stream.  The library
  * never allocates, frees or synchronises; every buffer is caller-owned device
  * memory (for example torch tensors) in the layouts documented below, dense
- * and contiguous.  No C++ exception crosses this boundary.  Calls on
+ * and contiguous.  Alignment: the 32-bit arrays (q_len, r_len, status,
+ * tickets, prefill's len and res) and the fp32 output start on a 4-byte
+ * boundary; every other buffer (codes, scales, zeros, fp16 rows, the query,
+ * the new and the sink tokens, prefill's source, the workspace) on a 16-byte
+ * boundary (torch allocations start on 256 bytes).  A null or misaligned
+ * pointer gives KIVI_EINVAL before anything is launched.  No C++ exception crosses this boundary.  Calls on
  * different caches are independent and reentrant; a cache must not be
  * touched concurrently from two streams.
  */
@@ -37,7 +42,7 @@ extern "C" {
 
 /* ---- return codes (host side) ------------------------------------------ */
 #define KIVI_OK            0
-#define KIVI_EINVAL       -1  /* bad dims, null pointer, bad scalar argument  */
+#define KIVI_EINVAL       -1  /* bad dims, null or misaligned pointer, bad scalar */
 #define KIVI_ENOSPC       -2  /* workspace smaller than kivi_decode_workspace_bytes */
 #define KIVI_EHIP         -3  /* a kernel launch failed (hipGetLastError)      */
 #define KIVI_EUNSUPPORTED -4  /* valid dims that no compiled kernel covers     */
@@ -211,7 +216,7 @@ int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache,
  *                   pointers are then not read and may be NULL)
  * Positions play no part (no rotary embedding here).  Other arguments,
  * layouts, workspace and errors as kivi_decode_attn; KIVI_EINVAL for n_sink
- * out of range or a NULL sink pointer with n_sink > 0.  An empty cache with
+ * out of range or a NULL or misaligned sink pointer with n_sink > 0.  An empty cache with
  * n_sink > 0 attends over the sink alone.
  */
 int kivi_decode_attn_sink(const kivi_dims *dims, const kivi_cache *cache,

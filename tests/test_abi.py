@@ -144,3 +144,57 @@ def test_entry_points_reject_bad_arguments_without_a_device():
     assert L.kivi_stream_read(fake, sz(1024), (1 << 20) + 1, fake, None) == kivi.KIVI_EINVAL
     for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(L.kivi_strerror(code), bytes)
+
+
+def test_misaligned_pointers_are_rejected_before_any_launch():
+    """16-byte alignment for the vector-loaded buffers, 4 bytes for the
+    32-bit arrays and the fp32 output.  A decode call whose pointers pass
+    and whose workspace is one byte short returns KIVI_ENOSPC, still before
+    any launch, which tells the two checks apart."""
+    L = kivi.lib()
+    d = kivi.make_dims(2, 2, 128, 2, 32, 32, 256)
+    need = kivi.workspace_bytes(d)
+    p = ctypes.c_void_p
+    fields = [n for n, _ in kivi.CacheStruct._fields_]
+    four = {"q_len", "r_len", "status", "tickets"}
+
+    def decode(cs, q=0x1000, out=0x1000, ws=0x1000):
+        return L.kivi_decode_attn(ctypes.byref(d), ctypes.byref(cs), p(q), p(out),
+                                  ctypes.c_float(1.0), p(ws), ctypes.c_size_t(need - 1), None)
+
+    good = kivi.CacheStruct(*([0x1000] * len(fields)))
+    assert decode(good) == kivi.KIVI_ENOSPC
+    for name in fields:
+        for addr in (0x1008, 0x1004, 0x1002):
+            cs = kivi.CacheStruct(*([0x1000] * len(fields)))
+            setattr(cs, name, addr)
+            ok = name in four and addr % 4 == 0
+            assert decode(cs) == (kivi.KIVI_ENOSPC if ok else kivi.KIVI_EINVAL), (name, addr)
+            if not ok:
+                assert L.kivi_flush_residual(ctypes.byref(d), ctypes.byref(cs), None) == \
+                    kivi.KIVI_EINVAL
+    assert decode(good, q=0x1008) == kivi.KIVI_EINVAL
+    assert decode(good, ws=0x1008) == kivi.KIVI_EINVAL
+    assert decode(good, out=0x1004) == kivi.KIVI_ENOSPC
+    assert decode(good, out=0x1002) == kivi.KIVI_EINVAL
+    f, m = p(0x1000), p(0x1008)
+    assert L.kivi_append_kv(ctypes.byref(d), ctypes.byref(good), m, f, None) == kivi.KIVI_EINVAL
+    assert L.kivi_append_kv(ctypes.byref(d), ctypes.byref(good), f, m, None) == kivi.KIVI_EINVAL
+    assert L.kivi_prefill(ctypes.byref(d), ctypes.byref(good), m, f, 64, f, None, None) == \
+        kivi.KIVI_EINVAL
+    assert L.kivi_prefill(ctypes.byref(d), ctypes.byref(good), f, f, 64, p(0x1002), None, None) == \
+        kivi.KIVI_EINVAL
+    assert L.kivi_prefill(ctypes.byref(d), ctypes.byref(good), f, f, 64, f, p(0x1001), None) == \
+        kivi.KIVI_EINVAL
+    assert L.kivi_decode_step(ctypes.byref(d), ctypes.byref(good), m, f, f, f, ctypes.c_float(1.0),
+                              f, ctypes.c_size_t(need), None) == kivi.KIVI_EINVAL
+    assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(good), m, f, 4, f, f,
+                                   ctypes.c_float(1.0), f, ctypes.c_size_t(need),
+                                   None) == kivi.KIVI_EINVAL
+    # with no sink tokens the sink pointers are not read
+    assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(good), m, None, 0, f, f,
+                                   ctypes.c_float(1.0), f, ctypes.c_size_t(need - 1),
+                                   None) == kivi.KIVI_ENOSPC
+    assert L.kivi_decode_attn_rope(ctypes.byref(d), ctypes.byref(good), m, f, ctypes.c_float(1.0),
+                                   ctypes.c_double(1e4), f, ctypes.c_size_t(need),
+                                   None) == kivi.KIVI_EINVAL
