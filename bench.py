@@ -229,9 +229,6 @@ def main():
     k_new = torch.from_numpy(k_new).cuda()   # [batch, heads, D]
     v_new = torch.from_numpy(v_new).cuda()
     q = torch.from_numpy(w.q).cuda()
-    if args.sink and args.rope is not None:
-        log("--sink and --rope cannot be combined (the sink decode has no rotary embedding)")
-        sys.exit(2)
     k_sink, v_sink = (torch.from_numpy(x).cuda() for x in wl.sink_tokens(w, args.sink))
     del kt, vt
     torch.cuda.synchronize()
@@ -263,8 +260,8 @@ def main():
 
     def decode(i, out):
         if args.sink:
-            return kivi.decode_attn_sink(copies[i], q, cfg.sm_scale, k_sink, v_sink, out=out,
-                                         workspace=ws)
+            return kivi.decode_attn_sink(copies[i], q, cfg.sm_scale, k_sink, v_sink,
+                                         rope_base=args.rope or 0.0, out=out, workspace=ws)
         if args.rope is None:
             return kivi.decode_attn(copies[i], q, cfg.sm_scale, out=out, workspace=ws)
         return kivi.decode_attn_rope(copies[i], q, cfg.sm_scale, args.rope, out=out, workspace=ws)

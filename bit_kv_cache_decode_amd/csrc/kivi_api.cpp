@@ -159,7 +159,8 @@ int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache, const void 
 
 int kivi_decode_attn_sink(const kivi_dims *dims, const kivi_cache *cache, const void *k_sink,
                           const void *v_sink, int32_t n_sink, const void *q, float *out,
-                          float sm_scale, void *workspace, size_t workspace_bytes, void *stream) {
+                          float sm_scale, double rope_base, void *workspace,
+                          size_t workspace_bytes, void *stream) {
   const int rc = kivi::check_dims(dims);
   if (rc != KIVI_OK) return rc;
   if (!kivi::cache_ok(cache) || !kivi::a16(q) || !kivi::a4(out) || !kivi::a16(workspace))
@@ -169,10 +170,11 @@ int kivi_decode_attn_sink(const kivi_dims *dims, const kivi_cache *cache, const 
   if (n_sink < 0 || n_sink > kivi::kMaxSink ||
       (n_sink > 0 && (!kivi::a16(k_sink) || !kivi::a16(v_sink))))
     return KIVI_EINVAL;
+  if (rope_base != 0.0 && (!(rope_base > 1.0) || rope_base == 1.0 / 0.0)) return KIVI_EINVAL;
   const kivi::DecodePlan p = kivi::decode_plan(*dims);
   if (workspace_bytes < p.bytes) return KIVI_ENOSPC;
   return kivi::hip_rc(kivi::launch_decode_sink(*dims, *cache, p, k_sink, v_sink, n_sink, q, out,
-                                               sm_scale, workspace, stream));
+                                               sm_scale, rope_base, workspace, stream));
 }
 
 int kivi_decode_attn_rope(const kivi_dims *dims, const kivi_cache *cache, const void *q,

@@ -67,7 +67,8 @@ int launch_stream_read(const void *src, size_t bytes, int workgroups, uint32_t *
                        void *stream);
 int launch_decode_sink(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
                        const void *k_sink, const void *v_sink, int n_sink, const void *q,
-                       float *out, float sm_scale, void *workspace, void *stream);
+                       float *out, float sm_scale, double rope_base, void *workspace,
+                       void *stream);
 int launch_decode_rope(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
                        const void *q, float *out, float sm_scale, double rope_base,
                        void *workspace, void *stream);

@@ -1020,10 +1020,12 @@ struct RopeLane {
   const float *q;         // the lane's rotated query channels (x sm_scale log2 e), in LDS
   double rev[CPW / 2];    // theta_f / (2 pi) of the lane's pairs
   float cs[CPW / 2], sn[CPW / 2];  // cos and sin of theta_f
+  int pos0;               // position of the sequence's first cache token
 
   // first channel c0 of the lane; qs: the wave's scaled query in LDS
-  __device__ __forceinline__ void init(const float *qs, int c0, double log2_base) {
+  __device__ __forceinline__ void init(const float *qs, int c0, double log2_base, int p0) {
     q = qs + c0;
+    pos0 = p0;
 #pragma unroll
     for (int j = 0; j < CPW / 2; ++j) {
       const int f = c0 / 2 + j;
@@ -1033,11 +1035,12 @@ struct RopeLane {
       sn[j] = (float)sin(th);
     }
   }
-  // u = the query turned back by position p's angles
+  // u = the query turned back by the angles of cache token p (position
+  // pos0 + p)
   __device__ __forceinline__ void at(float (&u)[CPW], int p) const {
 #pragma unroll
     for (int j = 0; j < CPW / 2; ++j) {
-      double x = (double)p * rev[j];
+      double x = (double)(pos0 + p) * rev[j];
       x -= floor(x);
       const float xf = (float)x;
       const float c = __builtin_amdgcn_cosf(xf), s = __builtin_amdgcn_sinf(xf);
@@ -1624,7 +1627,7 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
   [[maybe_unused]] RopeLane<C::CPW> rope;
   if constexpr (ROPE) {
     __builtin_amdgcn_wave_barrier();
-    rope.init(stg.qs, w * C::CPW, a.rope_log2_base);
+    rope.init(stg.qs, w * C::CPW, a.rope_log2_base, a.n_sink);
   }
   auto *zz = reinterpret_cast<float(*)[C::W * C::QPW]>(&sm.zz[ROPE ? wv : 0][0][0]);
 
@@ -1728,10 +1731,10 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
 #endif
   if (!early) window();
   // fp16 sink tokens (the sequence's first tokens, kept unquantized ahead of
-  // the quantized ones): this wave's share [gw * sink_per_wave, ...), one
-  // load round trip per step (set up here, so that nothing of it is live
-  // during the quantized stream)
-  if constexpr (!FUSED && !ROPE) {
+  // the quantized ones, at positions 0 .. n_sink - 1): this wave's share
+  // [gw * sink_per_wave, ...), one load round trip per step (set up here, so
+  // that nothing of it is live during the quantized stream)
+  if constexpr (!FUSED) {
     const int sb = qs.gw * a.sink_per_wave, se = min(a.n_sink, sb + a.sink_per_wave);
     if (se > sb) {
       WinStream<BITS, G> ss;
@@ -1748,7 +1751,14 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
       for (int i = 0; sb + i * WC::STEP < se; ++i) {
         WinStep<BITS, G> x;
         ss.issue(x, i);
-        window_step<BITS, G>(x, sb + i * WC::STEP + slot < se, qv, st);
+        const int r = sb + i * WC::STEP + slot;
+        if constexpr (ROPE) {
+          float u[C::CPW];
+          rope.at(u, r - a.n_sink);  // position r
+          window_step<BITS, G>(x, r < se, u, st);
+        } else {
+          window_step<BITS, G>(x, r < se, qv, st);
+        }
       }
     }
   }
@@ -2106,8 +2116,11 @@ int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, 
 
 int launch_decode_sink(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
                        const void *k_sink, const void *v_sink, int n_sink, const void *q,
-                       float *out, float sm_scale, void *workspace, void *stream) {
+                       float *out, float sm_scale, double rope_base, void *workspace,
+                       void *stream) {
   DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, workspace);
+  const bool rope = rope_base != 0.0;
+  if (rope) da.rope_log2_base = log2(rope_base);
   if (n_sink > 0) {
     const int waves = kDecodeWaves * p.splits;
     da.k_sink = static_cast<const half_t *>(k_sink);
@@ -2116,7 +2129,7 @@ int launch_decode_sink(const kivi_dims &d, const kivi_cache &c, const DecodePlan
     da.sink_per_wave = ((n_sink + waves - 1) / waves + 7) / 8 * 8;
   }
   return launch_decode_any(d, da, encode_args(d, c), false, p.depth,
-                           static_cast<hipStream_t>(stream));
+                           static_cast<hipStream_t>(stream), rope);
 }
 
 int launch_decode_rope(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,

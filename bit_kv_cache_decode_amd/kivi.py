@@ -69,7 +69,8 @@ def lib():
         L.kivi_decode_attn_rope.argtypes = [P(Dims), P(CacheStruct), V, V, ctypes.c_float,
                                             ctypes.c_double, V, ctypes.c_size_t, V]
         L.kivi_decode_attn_sink.argtypes = [P(Dims), P(CacheStruct), V, V, I32, V, V,
-                                            ctypes.c_float, V, ctypes.c_size_t, V]
+                                            ctypes.c_float, ctypes.c_double, V, ctypes.c_size_t,
+                                            V]
         L.kivi_decode_step.argtypes = [P(Dims), P(CacheStruct), V, V, V, V, ctypes.c_float, V,
                                        ctypes.c_size_t, V]
         L.kivi_stream_read.argtypes = [V, ctypes.c_size_t, I32, V, V]
@@ -258,10 +259,12 @@ def decode_attn_rope(cache, q, sm_scale, rope_base=10000.0, out=None, workspace=
     return out
 
 
-def decode_attn_sink(cache, q, sm_scale, k_sink, v_sink, out=None, workspace=None):
+def decode_attn_sink(cache, q, sm_scale, k_sink, v_sink, rope_base=0.0, out=None,
+                     workspace=None):
     """decode_attn over fp16 sink tokens (k_sink, v_sink: fp16
-    [batch, heads, n_sink, head_dim]) followed by the cache's tokens; fp32
-    output."""
+    [batch, heads, n_sink, head_dim]) followed by the cache's tokens; with
+    rope_base > 1, keys (the sink's too) are stored before the rotary
+    embedding and rotated by their positions (sink first); fp32 output."""
     d = cache.dims
     n_sink = k_sink.shape[2] if k_sink.dim() == 4 else -1
     _need(k_sink, torch.float16, (d.batch, d.heads, n_sink, d.head_dim), "k_sink")
@@ -270,7 +273,8 @@ def decode_attn_sink(cache, q, sm_scale, k_sink, v_sink, out=None, workspace=Non
     _check(lib().kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(cache.struct()),
                                        k_sink.data_ptr(), v_sink.data_ptr(), ctypes.c_int32(n_sink),
                                        q.data_ptr(), out.data_ptr(), ctypes.c_float(sm_scale),
-                                       workspace.data_ptr(), ctypes.c_size_t(nbytes), _stream()),
+                                       ctypes.c_double(rope_base), workspace.data_ptr(),
+                                       ctypes.c_size_t(nbytes), _stream()),
            "kivi_decode_attn_sink")
     return out
 

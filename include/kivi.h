@@ -212,16 +212,24 @@ int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache,
  *                   owned by the caller and only read (typically the
  *                   prompt's first n_sink rows, with the cache built from
  *                   the rest); the same n_sink for every sequence
- *   n_sink          0 .. 4096; 0 gives exactly kivi_decode_attn (the
- *                   pointers are then not read and may be NULL)
- * Positions play no part (no rotary embedding here).  Other arguments,
- * layouts, workspace and errors as kivi_decode_attn; KIVI_EINVAL for n_sink
- * out of range or a NULL or misaligned sink pointer with n_sink > 0.  An empty cache with
- * n_sink > 0 attends over the sink alone.
+ *   n_sink          0 .. 4096; with rope_base 0, n_sink 0 gives exactly
+ *                   kivi_decode_attn (the pointers are then not read and
+ *                   may be NULL)
+ *   rope_base       0: no rotary embedding (positions play no part).
+ *                   Otherwise > 1 and finite: keys stored before the
+ *                   rotation, as in kivi_decode_attn_rope, with sink token
+ *                   s at position s, quantized token t at n_sink + t and
+ *                   window slot r at n_sink + q_len[b] + r; q already
+ *                   rotated.  The sink keys are stored before the rotation
+ *                   too.
+ * Other arguments, layouts, workspace and errors as kivi_decode_attn;
+ * KIVI_EINVAL for n_sink out of range, a NULL or misaligned sink pointer
+ * with n_sink > 0, or a bad rope_base.  An empty cache with n_sink > 0
+ * attends over the sink alone.
  */
 int kivi_decode_attn_sink(const kivi_dims *dims, const kivi_cache *cache,
                           const void *k_sink, const void *v_sink, int32_t n_sink,
-                          const void *q, float *out, float sm_scale,
+                          const void *q, float *out, float sm_scale, double rope_base,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*

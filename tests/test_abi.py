@@ -122,16 +122,23 @@ def test_entry_points_reject_bad_arguments_without_a_device():
     # the sink decode: n_sink outside [0, 4096], a NULL sink with n_sink > 0,
     # a short workspace
     i32 = ctypes.c_int32
+    c0 = ctypes.c_double(0.0)
     for n, ks, vs in ((-1, fake, fake), (4097, fake, fake), (4, None, fake), (4, fake, None)):
         assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(cs), ks, vs, i32(n), fake, fake,
-                                       ctypes.c_float(1.0), fake, ctypes.c_size_t(need),
+                                       ctypes.c_float(1.0), c0, fake, ctypes.c_size_t(need),
                                        None) == kivi.KIVI_EINVAL
     assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(cs), fake, fake, i32(4), fake, fake,
-                                   ctypes.c_float(float("nan")), fake, ctypes.c_size_t(need),
+                                   ctypes.c_float(float("nan")), c0, fake, ctypes.c_size_t(need),
                                    None) == kivi.KIVI_EINVAL
-    assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(cs), fake, fake, i32(4), fake, fake,
-                                   ctypes.c_float(1.0), fake, ctypes.c_size_t(need - 1),
-                                   None) == kivi.KIVI_ENOSPC
+    # rope_base: 0 (none) or > 1 and finite
+    for base in (1.0, 0.5, -3.0, float("nan"), float("inf")):
+        assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(cs), fake, fake, i32(4), fake,
+                                       fake, ctypes.c_float(1.0), ctypes.c_double(base), fake,
+                                       ctypes.c_size_t(need), None) == kivi.KIVI_EINVAL
+    for base in (0.0, 1e4):
+        assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(cs), fake, fake, i32(4), fake,
+                                       fake, ctypes.c_float(1.0), ctypes.c_double(base), fake,
+                                       ctypes.c_size_t(need - 1), None) == kivi.KIVI_ENOSPC
     # the stream-read measurement aid: null, empty, unaligned or oddly sized
     # buffers and workgroup counts outside [1, 2^20]
     sz = ctypes.c_size_t
@@ -189,12 +196,12 @@ def test_misaligned_pointers_are_rejected_before_any_launch():
     assert L.kivi_decode_step(ctypes.byref(d), ctypes.byref(good), m, f, f, f, ctypes.c_float(1.0),
                               f, ctypes.c_size_t(need), None) == kivi.KIVI_EINVAL
     assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(good), m, f, 4, f, f,
-                                   ctypes.c_float(1.0), f, ctypes.c_size_t(need),
-                                   None) == kivi.KIVI_EINVAL
+                                   ctypes.c_float(1.0), ctypes.c_double(0.0), f,
+                                   ctypes.c_size_t(need), None) == kivi.KIVI_EINVAL
     # with no sink tokens the sink pointers are not read
     assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(good), m, None, 0, f, f,
-                                   ctypes.c_float(1.0), f, ctypes.c_size_t(need - 1),
-                                   None) == kivi.KIVI_ENOSPC
+                                   ctypes.c_float(1.0), ctypes.c_double(0.0), f,
+                                   ctypes.c_size_t(need - 1), None) == kivi.KIVI_ENOSPC
     assert L.kivi_decode_attn_rope(ctypes.byref(d), ctypes.byref(good), m, f, ctypes.c_float(1.0),
                                    ctypes.c_double(1e4), f, ctypes.c_size_t(need),
                                    None) == kivi.KIVI_EINVAL

@@ -1,7 +1,8 @@
 """Every compiled code width and group size, B in {2, 4, 8} x G in {32, 64,
 128}, on a small ragged batch through the C ABI against the oracle: the
 prefilled cache bit for bit, the plain, the pre-rotation-key and the
-attention-sink (5 fp16 sink tokens) decode within
+attention-sink (5 fp16 sink tokens, with and without the rotation) decode
+within
 max-abs 2e-3 / relative L2 1e-3 of the fp64 oracle, and a flush of the full
 windows bit for bit.  Batch 9 x 32 heads (288 pairs) runs the decode with one
 sub-chunk in flight per wave (more workgroups than compute units), batch 2
@@ -55,8 +56,9 @@ def test_width_group_combination(bits, G, batch):
     srng = np.random.default_rng(seed + 1)
     sk = (srng.standard_normal((batch, H, 5, D), np.float32) * 3).astype(np.float16)
     sv = srng.standard_normal((batch, H, 5, D), np.float32).astype(np.float16)
-    out_s = kivi.decode_attn_sink(c, qt, 1.0, torch.from_numpy(sk).cuda(),
-                                  torch.from_numpy(sv).cuda()).cpu().numpy()
+    skt, svt = torch.from_numpy(sk).cuda(), torch.from_numpy(sv).cuda()
+    out_s = kivi.decode_attn_sink(c, qt, 1.0, skt, svt).cpu().numpy()
+    out_rs = kivi.decode_attn_sink(c, qt, 1.0, skt, svt, rope_base=10000.0).cpu().numpy()
     assert c.status_bits() == 0
     heads = [(b, h) for b in range(batch) for h in (0, 13, 31)]
     for b, h in heads:
@@ -70,6 +72,9 @@ def test_width_group_combination(bits, G, batch):
         assert_within_tolerance(out_r[b, h], ref_r, f"rope b={b} h={h}")
         ref_s = osink.decode_head_sink(q[b, h], st, sk[b, h], sv[b, h], 1.0, G, bits)
         assert_within_tolerance(out_s[b, h], ref_s, f"sink b={b} h={h}")
+        ref_rs = osink.decode_head_sink(q[b, h], st, sk[b, h], sv[b, h], 1.0, G, bits,
+                                        rope_base=10000.0)
+        assert_within_tolerance(out_rs[b, h], ref_rs, f"rotary sink b={b} h={h}")
     # flush: only the full window moves, bit for bit as the oracle encodes it
     kivi.flush_residual(c)
     torch.cuda.synchronize()

@@ -17,23 +17,22 @@ from tests.gpu_common import assert_within_tolerance, gpu_cache, oracle_head, wo
 pytestmark = pytest.mark.gpu
 
 
-def _run(c, w, n_sink, sm_scale=None):
+def _run(c, w, n_sink, rope_base=0.0):
     ks, vs = wl.sink_tokens(w, n_sink)
     q = torch.from_numpy(w.q).cuda()
-    scale = w.config.sm_scale if sm_scale is None else sm_scale
-    out = kivi.decode_attn_sink(c, q, scale, torch.from_numpy(ks).cuda(),
-                                torch.from_numpy(vs).cuda())
+    out = kivi.decode_attn_sink(c, q, w.config.sm_scale, torch.from_numpy(ks).cuda(),
+                                torch.from_numpy(vs).cuda(), rope_base=rope_base)
     torch.cuda.synchronize()
     assert c.status_bits() == 0
     return out.cpu().numpy(), ks, vs
 
 
-def _check(out, w, ks, vs, heads, state=oracle_head):
+def _check(out, w, ks, vs, heads, state=oracle_head, rope_base=None):
     G = w.config.group
     for b, h in heads:
         st = state(w, b, h)
         ref = osink.decode_head_sink(w.q[b, h], st, ks[b, h], vs[b, h], w.config.sm_scale, G,
-                                     w.bits)
+                                     w.bits, rope_base=rope_base)
         assert_within_tolerance(out[b, h], ref, f"b={b} h={h}")
 
 
@@ -95,3 +94,43 @@ def test_sink_long_context_sampled_heads(bits):
     c = gpu_cache(w)
     out, ks, vs = _run(c, w, 4)
     _check(out, w, ks, vs, [(0, 0), (0, 31)])
+
+
+# ---- keys (the sink's too) stored before the rotary embedding: sink token s
+# at position s, the cache's tokens after the sink
+
+def test_rotary_sink_llama2_7b_shape_all_heads():
+    w = workload(2, batch=2)
+    c = gpu_cache(w)
+    out, ks, vs = _run(c, w, 4, rope_base=10000.0)
+    _check(out, w, ks, vs, [(b, h) for b in range(2) for h in range(32)], rope_base=10000.0)
+
+
+def test_rotary_no_sink_is_bit_identical_to_decode_attn_rope():
+    w = workload(2, batch=2)
+    c = gpu_cache(w)
+    out, _, _ = _run(c, w, 0, rope_base=10000.0)
+    ref = kivi.decode_attn_rope(c, torch.from_numpy(w.q).cuda(), 1.0, 10000.0).cpu().numpy()
+    assert np.array_equal(out, ref)
+
+
+@pytest.mark.parametrize("q_len,r_len,n_sink", [(0, 0, 9), (0, 5, 7), (32, 0, 8), (4064, 31, 100)])
+def test_rotary_sink_edge_lengths(q_len, r_len, n_sink):
+    w = workload(2, batch=1)
+    c = gpu_cache(w, q_len=[q_len], r_len=[r_len])
+    out, ks, vs = _run(c, w, n_sink, rope_base=10000.0)
+
+    def state(w, b, h):
+        return ocache.head_state(w.k[b, h], w.v[b, h], q_len, r_len, 32, 2, 4096, 128)
+    _check(out, w, ks, vs, [(0, 0), (0, 31)], state, rope_base=10000.0)
+
+
+@pytest.mark.parametrize("workload_number,bits", [(3, 4), (5, 4)])
+def test_rotary_sink_large_grids_and_long_context(workload_number, bits):
+    """The depth-1 rotary kernel (13B shape at B=4) and split merges with
+    positions up to 131075 (131072-token workload)."""
+    w = workload(workload_number, bits=bits)
+    c = gpu_cache(w)
+    out, ks, vs = _run(c, w, 4, rope_base=10000.0)
+    heads = [(0, 0), (7, 21), (15, 39)] if workload_number == 3 else [(0, 0), (0, 31)]
+    _check(out, w, ks, vs, heads, rope_base=10000.0)

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 from oracle import cache as ocache
+from oracle import rope as orope
 from oracle import sink as osink
 from oracle.attention import attention
 
@@ -102,12 +103,59 @@ def test_no_sink_is_the_plain_decode():
                           ocache.decode_head(q, st, 0.6, 4, 2))
 
 
+# ------------------------------------------------ with the rotary embedding
+
+def test_rotary_sink_is_the_start_of_a_window_only_cache():
+    """A cache with no quantized tokens: n_sink sink rows then r window rows
+    at positions 0 .. n_sink + r - 1 are a window-only cache holding both
+    (the rotary oracle's decode, pinned on its own)."""
+    rng = np.random.default_rng(83)
+    D, S, r = 128, 7, 20
+    k = (rng.standard_normal((S + r, D)) * 4).astype(np.float16)
+    v = rng.standard_normal((S + r, D)).astype(np.float16)
+    q = rng.standard_normal(D)
+    st = ocache.head_state(k[S:], v[S:], 0, r, 32, 2, 64, 32)
+    got = osink.decode_head_sink(q, st, k[:S], v[:S], 0.1, 32, 2, rope_base=10000.0)
+    both = ocache.head_state(k, v, 0, S + r, 32, 2, 64, 32)
+    ref = orope.decode_head_rope(q, both, 0.1, 32, 2, 10000.0)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+@pytest.mark.parametrize("bits,G,S", [(2, 4, 3), (4, 8, 2)])
+def test_rotary_sink_decode_matches_textbook_loops(bits, G, S):
+    """Quantized tokens after the sink sit at positions S, S + 1, ...:
+    loops over tokens and channel pairs with math.cos / math.sin."""
+    q, st, sk, sv = _tiny(90 + bits, S, bits, G)
+    got = osink.decode_head_sink(q, st, sk, sv, 0.6, G, bits, rope_base=50.0)
+    kk, vv = ocache.context(st, G, bits)
+    keys = sk.astype(np.float64).tolist() + kk.tolist()
+    vals = sv.astype(np.float64).tolist() + vv.tolist()
+    D, base = len(q), 50.0
+    rot = []
+    for t, row in enumerate(keys):
+        y = list(row)
+        for f in range(D // 2):
+            th = t * base ** (-2.0 * f / D)
+            a, b = row[2 * f], row[2 * f + 1]
+            y[2 * f] = a * math.cos(th) - b * math.sin(th)
+            y[2 * f + 1] = a * math.sin(th) + b * math.cos(th)
+        rot.append(y)
+    ref = _textbook(q.astype(np.float64).tolist(), rot, vals, 0.6)
+    assert np.max(np.abs(got - np.array(ref))) <= 1e-12
+
+
+def test_rotary_without_sink_is_the_rotary_decode():
+    q, st, sk, sv = _tiny(84, 0, 2, 4)
+    assert np.array_equal(osink.decode_head_sink(q, st, sk, sv, 0.6, 4, 2, rope_base=50.0),
+                          orope.decode_head_rope(q, st, 0.6, 4, 2, 50.0))
+
+
 # ------------------------------------------------------------ planted mistakes
 # Each mutant replaces the oracle's sink decode with a plausible slip; at
 # least one pin above must fail with it in place.
 
 def _mutant(kind):
-    def f(q, state, sink_k, sink_v, alpha, group, bits):
+    def f(q, state, sink_k, sink_v, alpha, group, bits, rope_base=None):
         kk, vv = ocache.context(state, group, bits)
         sk = np.asarray(sink_k, np.float64).reshape(-1, kk.shape[1])
         sv = np.asarray(sink_v, np.float64).reshape(-1, vv.shape[1])
@@ -121,16 +169,30 @@ def _mutant(kind):
             sv = np.roll(sv, 1, axis=0)
         elif kind == "unscaled":     # sink scores without alpha
             sk = sk / alpha
+        if rope_base is not None:
+            if kind == "cache_from_zero":    # cache positions not moved past the sink
+                return attention(q, np.concatenate([orope.rope(sk, np.arange(len(sk)), rope_base),
+                                                    orope.rope(kk, np.arange(len(kk)), rope_base)]),
+                                 np.concatenate([sv, vv]), alpha)
+            if kind == "sink_unrotated":
+                return attention(q, np.concatenate([sk, orope.rope(kk, np.arange(len(kk)) + len(sk),
+                                                                   rope_base)]),
+                                 np.concatenate([sv, vv]), alpha)
+            keys = orope.rope(np.concatenate([sk, kk]), np.arange(len(sk) + len(kk)), rope_base)
+            return attention(q, keys, np.concatenate([sv, vv]), alpha)
         return attention(q, np.concatenate([sk, kk]), np.concatenate([sv, vv]), alpha)
     return f
 
 
 PINS = [lambda: test_sink_decode_matches_textbook_loops(2, 4, 3),
         test_sink_tokens_count_as_window_tokens, test_sink_alone_is_exact_fp16_attention,
-        test_one_sink_and_one_window_token_closed_form]
+        test_one_sink_and_one_window_token_closed_form,
+        test_rotary_sink_is_the_start_of_a_window_only_cache,
+        lambda: test_rotary_sink_decode_matches_textbook_loops(2, 4, 3)]
 
 
-@pytest.mark.parametrize("kind", ["dropped", "twice", "swapped", "shifted", "unscaled"])
+@pytest.mark.parametrize("kind", ["dropped", "twice", "swapped", "shifted", "unscaled",
+                                  "cache_from_zero", "sink_unrotated"])
 def test_planted_mistake_is_caught(kind, monkeypatch):
     monkeypatch.setattr(osink, "decode_head_sink", _mutant(kind))
     caught = 0
