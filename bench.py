@@ -390,6 +390,8 @@ def main():
     dec_bytes = (wl.decode_bytes(w.q_len, r_start + 1, H, D, w.bits, cfg.group)
                  + Bt * H * args.sink * D * 2 * 2)   # fp16 sink keys and values
     achieved = dec_bytes / (decode_us * 1e-6) / 1e9
+    n_flush = int((r_start + 1 == cfg.residual).sum()) * H
+    flush_b = n_flush * wl.flush_bytes_per_head(cfg.residual, D, w.bits, cfg.group)
     result = {
         "metric": METRIC,
         "value": qheads / step_s,
@@ -426,6 +428,12 @@ def main():
         "phased_ms_per_step": eager_wall / K * 1e3,
         "append_us": append_us,
         "flush_us": flush_us,
+        # the flush phase: the windows the appended token filled, quantized
+        # (their algorithmic bytes over the phase's per-step time)
+        "flush": {"us": flush_us, "windows": n_flush,
+                  "algorithmic_bytes": int(flush_b),
+                  "GBps": flush_b / (flush_us * 1e-6) / 1e9 if n_flush else 0.0,
+                  "frac": flush_b / (flush_us * 1e-6) / 1e9 / PEAK_HBM_GBPS if n_flush else 0.0},
         "graph_replay_matches_eager": replay_ok,
         "phased_matches_step": eager_ok,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
