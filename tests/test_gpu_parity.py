@@ -132,6 +132,39 @@ def test_flush_only_full_windows_and_twice_in_a_row():
         assert np.array_equal(after[b, h, t0 // 32:t0 // 32 + 4].view(np.uint32), enc["k_codes"])
 
 
+def test_flush_of_a_large_batch_with_few_full_windows():
+    """Batch 64 x 32 heads: more flush units (two tiles of one (sequence,
+    head)) than flush workgroups, so each workgroup takes several units in
+    turn.  Only the sequences whose window is full move, bit for bit as the
+    oracle encodes them; the rest keep their lengths and codes."""
+    rng = np.random.default_rng(77)
+    B, H, D, G, R, cap = 64, 32, 128, 32, 128, 512
+    k = (rng.standard_normal((B, H, cap, D), np.float32) * 3).astype(np.float16)
+    v = rng.standard_normal((B, H, cap, D), np.float32).astype(np.float16)
+    ql = np.full(B, 256, np.int32)
+    rl = rng.integers(0, R, B).astype(np.int32)
+    full = np.zeros(B, bool)
+    full[[0, 13, 40, 63]] = True
+    rl[full] = R
+    c = kivi.KiviCache(B, H, D, 2, G, R, cap)
+    kivi.prefill(c, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                 torch.from_numpy(ql + rl).cuda(), torch.from_numpy(rl).cuda())
+    torch.cuda.synchronize()
+    before = c.k_codes.cpu().numpy().copy()
+    kivi.flush_residual(c)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.q_len.cpu().numpy(), np.where(full, ql + R, ql))
+    assert np.array_equal(c.r_len.cpu().numpy(), np.where(full, 0, rl))
+    assert not c.tickets.any() and c.status_bits() == 0
+    after = c.k_codes.cpu().numpy()
+    assert np.array_equal(after[~full], before[~full])
+    for b, h in [(0, 0), (13, 31), (40, 7), (63, 16)]:
+        enc = ocache.encode_tokens(k[b, h, 256:256 + R], v[b, h, 256:256 + R], G, 2)
+        for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+            got = getattr(c, name)[b, h, 256 // G:(256 + R) // G].cpu().numpy()
+            assert np.array_equal(got.view(np.uint8), enc[name].view(np.uint8)), (name, b, h)
+
+
 def test_ragged_serving_sampled_heads():
     w = workload(4)
     c = gpu_cache(w)
