@@ -99,15 +99,16 @@ def step_tokens(w):
     2000 + workload number; then every window must have room for it."""
     import numpy as np
     cfg = w.config
+    nb = len(w.r_len)  # the sequences drawn (the whole batch in the bench)
     if np.all(w.r_len >= 1):
         last = w.lengths - 1
-        b = np.arange(cfg.batch)
+        b = np.arange(nb)
         return (w.r_len - 1).astype(np.int32), np.ascontiguousarray(w.k[b, :, last]), \
             np.ascontiguousarray(w.v[b, :, last])
     if np.any(w.r_len >= cfg.residual):
         raise SystemExit("a full window cannot take the appended token")
     rng = np.random.Generator(np.random.PCG64(2000 + cfg.number))
-    shape = (cfg.batch, cfg.heads, cfg.head_dim)
+    shape = (nb, cfg.heads, cfg.head_dim)
     k_new = rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
     v_new = rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
     return w.r_len.astype(np.int32), k_new, v_new
