@@ -273,6 +273,9 @@ def main():
         # keys stored before the rotary embedding or with a sink)
         if args.rope is None and not args.sink:
             kivi.decode_step(copies[i], k_new, v_new, q, cfg.sm_scale, out=outs[i], workspace=ws)
+        elif args.rope is None:
+            kivi.decode_step_sink(copies[i], k_new, v_new, q, cfg.sm_scale, k_sink, v_sink,
+                                  out=outs[i], workspace=ws)
         else:
             kivi.append_kv(copies[i], k_new, v_new)
             decode(i, outs[i])
@@ -386,7 +389,7 @@ def main():
 
     step_s = wall / K
     plain = args.rope is None and not args.sink
-    one_kernel = kivi.decode_step_kernels(base.dims) == 1 and plain
+    one_kernel = kivi.decode_step_kernels(base.dims) == 1 and args.rope is None
     qheads = Bt * H
     dec_bytes = (wl.decode_bytes(w.q_len, r_start + 1, H, D, w.bits, cfg.group)
                  + Bt * H * args.sink * D * 2 * 2)   # fp16 sink keys and values
@@ -415,6 +418,7 @@ def main():
             "quantized_tokens": int(w.q_len.max()), "window_tokens": int((r_start + 1).max()),
             "rope_base": args.rope, "sink_tokens": args.sink,
             "step": (("kivi_decode_step (append + decode + flush, " if plain else
+                      "kivi_decode_step_sink (append + decode + flush, " if args.rope is None else
                       "kivi_append_kv + kivi_decode_attn_%s + kivi_flush_residual ("
                       % ("sink" if args.sink else "rope"))
                      + ("one kernel" if one_kernel else "three kernels")
@@ -444,13 +448,15 @@ def main():
     if one_kernel and graph is not None:
         # the whole-step kernel itself: the step's algorithmic bytes over its
         # per-step time inside the graph (HIP events around the replay)
-        sb = wl.step_bytes(w.q_len, r_start, H, D, w.bits, cfg.group, cfg.residual)
+        sb = (wl.step_bytes(w.q_len, r_start, H, D, w.bits, cfg.group, cfg.residual)
+              + Bt * H * args.sink * D * 2 * 2)
         result["step_kernel"] = {
-            "kernel": "decode_kernel whole-step variant (kivi_decode_step)",
+            "kernel": "decode_kernel whole-step variant (kivi_decode_step%s)"
+                      % ("_sink" if args.sink else ""),
             "us": step_event_us, "algorithmic_bytes": sb,
             "GBps": sb / (step_event_us * 1e-6) / 1e9,
             "frac": sb / (step_event_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
-            "traffic": measured_traffic(cfg.name, "step_bytes_per_launch")}
+            "traffic": measured_traffic(cfg.name, "step_bytes_per_launch") if plain else None}
     if not args.no_stream:
         sr = stream_ceiling(dec_bytes, K)
         result["stream_read"] = sr

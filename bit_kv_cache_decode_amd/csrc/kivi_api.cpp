@@ -193,20 +193,47 @@ int kivi_decode_attn_rope(const kivi_dims *dims, const kivi_cache *cache, const 
                                                workspace, stream));
 }
 
-int kivi_decode_step(const kivi_dims *dims, const kivi_cache *cache, const void *k_new,
-                     const void *v_new, const void *q, float *out, float sm_scale,
-                     void *workspace, size_t workspace_bytes, void *stream) {
-  const int rc = kivi::check_dims(dims);
+}  // extern "C"
+
+namespace kivi {
+namespace {
+
+int decode_step(const kivi_dims *dims, const kivi_cache *cache, const void *k_new,
+                const void *v_new, const void *k_sink, const void *v_sink, int32_t n_sink,
+                const void *q, float *out, float sm_scale, void *workspace,
+                size_t workspace_bytes, void *stream) {
+  const int rc = check_dims(dims);
   if (rc != KIVI_OK) return rc;
-  if (!kivi::cache_ok(cache) || !kivi::a16(k_new) || !kivi::a16(v_new) || !kivi::a16(q) ||
-      !kivi::a4(out) || !kivi::a16(workspace))
+  if (!cache_ok(cache) || !a16(k_new) || !a16(v_new) || !a16(q) || !a4(out) || !a16(workspace))
     return KIVI_EINVAL;
   if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
     return KIVI_EINVAL;
-  const kivi::DecodePlan p = kivi::decode_plan(*dims);
+  if (n_sink < 0 || n_sink > kMaxSink || (n_sink > 0 && (!a16(k_sink) || !a16(v_sink))))
+    return KIVI_EINVAL;
+  const DecodePlan p = decode_plan(*dims);
   if (workspace_bytes < p.bytes) return KIVI_ENOSPC;
-  return kivi::hip_rc(kivi::launch_decode_step(*dims, *cache, p, k_new, v_new, q, out, sm_scale,
-                                               workspace, stream));
+  return hip_rc(launch_decode_step(*dims, *cache, p, k_new, v_new, k_sink, v_sink, n_sink, q,
+                                   out, sm_scale, workspace, stream));
+}
+
+}  // namespace
+}  // namespace kivi
+
+extern "C" {
+
+int kivi_decode_step(const kivi_dims *dims, const kivi_cache *cache, const void *k_new,
+                     const void *v_new, const void *q, float *out, float sm_scale,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  return kivi::decode_step(dims, cache, k_new, v_new, nullptr, nullptr, 0, q, out, sm_scale,
+                           workspace, workspace_bytes, stream);
+}
+
+int kivi_decode_step_sink(const kivi_dims *dims, const kivi_cache *cache, const void *k_new,
+                          const void *v_new, const void *k_sink, const void *v_sink,
+                          int32_t n_sink, const void *q, float *out, float sm_scale,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  return kivi::decode_step(dims, cache, k_new, v_new, k_sink, v_sink, n_sink, q, out, sm_scale,
+                           workspace, workspace_bytes, stream);
 }
 
 int kivi_stream_read(const void *src, size_t bytes, int32_t workgroups, uint32_t *sink,

@@ -73,7 +73,8 @@ int launch_decode_rope(const kivi_dims &d, const kivi_cache &c, const DecodePlan
                        const void *q, float *out, float sm_scale, double rope_base,
                        void *workspace, void *stream);
 int launch_decode_step(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
-                       const void *k_new, const void *v_new, const void *q, float *out,
+                       const void *k_new, const void *v_new, const void *k_sink,
+                       const void *v_sink, int n_sink, const void *q, float *out,
                        float sm_scale, void *workspace, void *stream);
 
 }  // namespace kivi

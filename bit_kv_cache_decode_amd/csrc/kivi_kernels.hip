@@ -1734,7 +1734,7 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
   // the quantized ones, at positions 0 .. n_sink - 1): this wave's share
   // [gw * sink_per_wave, ...), one load round trip per step (set up here, so
   // that nothing of it is live during the quantized stream)
-  if constexpr (!FUSED) {
+  {
     const int sb = qs.gw * a.sink_per_wave, se = min(a.n_sink, sb + a.sink_per_wave);
     if (se > sb) {
       WinStream<BITS, G> ss;
@@ -2079,6 +2079,17 @@ DecodeArgs decode_args(const kivi_dims &d, const kivi_cache &c, const DecodePlan
   return da;
 }
 
+// n_sink fp16 sink tokens, shared over all waves of all splits
+void set_sink(DecodeArgs &da, const DecodePlan &p, const void *k_sink, const void *v_sink,
+              int n_sink) {
+  if (n_sink <= 0) return;
+  const int waves = kDecodeWaves * p.splits;
+  da.k_sink = static_cast<const half_t *>(k_sink);
+  da.v_sink = static_cast<const half_t *>(v_sink);
+  da.n_sink = n_sink;
+  da.sink_per_wave = ((n_sink + waves - 1) / waves + 7) / 8 * 8;
+}
+
 int launch_decode_any(const kivi_dims &d, const DecodeArgs &da, const EncodeArgs &ea, bool fused,
                       int depth, hipStream_t st, bool rope = false) {
   const dim3 grid(da.splits, d.heads, d.batch);
@@ -2121,13 +2132,7 @@ int launch_decode_sink(const kivi_dims &d, const kivi_cache &c, const DecodePlan
   DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, workspace);
   const bool rope = rope_base != 0.0;
   if (rope) da.rope_log2_base = log2(rope_base);
-  if (n_sink > 0) {
-    const int waves = kDecodeWaves * p.splits;
-    da.k_sink = static_cast<const half_t *>(k_sink);
-    da.v_sink = static_cast<const half_t *>(v_sink);
-    da.n_sink = n_sink;
-    da.sink_per_wave = ((n_sink + waves - 1) / waves + 7) / 8 * 8;
-  }
+  set_sink(da, p, k_sink, v_sink, n_sink);
   return launch_decode_any(d, da, encode_args(d, c), false, p.depth,
                            static_cast<hipStream_t>(stream), rope);
 }
@@ -2142,18 +2147,21 @@ int launch_decode_rope(const kivi_dims &d, const kivi_cache &c, const DecodePlan
 }
 
 int launch_decode_step(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
-                       const void *k_new, const void *v_new, const void *q, float *out,
+                       const void *k_new, const void *v_new, const void *k_sink,
+                       const void *v_sink, int n_sink, const void *q, float *out,
                        float sm_scale, void *workspace, void *stream) {
   if (!step_in_one_kernel(d, p)) {
     int rc = launch_append(d, c, k_new, v_new, stream);
     if (rc) return rc;
-    rc = launch_decode(d, c, p, q, out, sm_scale, workspace, stream);
+    rc = launch_decode_sink(d, c, p, k_sink, v_sink, n_sink, q, out, sm_scale, 0.0, workspace,
+                            stream);
     if (rc) return rc;
     return launch_flush(d, c, stream);
   }
   DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, workspace);
   da.k_new = static_cast<const half_t *>(k_new);
   da.v_new = static_cast<const half_t *>(v_new);
+  set_sink(da, p, k_sink, v_sink, n_sink);
   return launch_decode_any(d, da, encode_args(d, c), true, p.depth,
                            static_cast<hipStream_t>(stream));
 }

@@ -23,7 +23,8 @@ ST_RESIDUAL_FULL, ST_CAPACITY, ST_BAD_LENGTH = 0x1, 0x2, 0x4
 # Every symbol the public header declares.
 EXPORTS = ("kivi_validate_dims", "kivi_append_kv", "kivi_flush_residual", "kivi_prefill",
            "kivi_decode_workspace_bytes", "kivi_decode_splits", "kivi_decode_step_kernels", "kivi_decode_attn",
-           "kivi_decode_attn_rope", "kivi_decode_attn_sink", "kivi_decode_step", "kivi_stream_read",
+           "kivi_decode_attn_rope", "kivi_decode_attn_sink", "kivi_decode_step",
+           "kivi_decode_step_sink", "kivi_stream_read",
            "kivi_strerror")
 
 
@@ -73,6 +74,8 @@ def lib():
                                             V]
         L.kivi_decode_step.argtypes = [P(Dims), P(CacheStruct), V, V, V, V, ctypes.c_float, V,
                                        ctypes.c_size_t, V]
+        L.kivi_decode_step_sink.argtypes = [P(Dims), P(CacheStruct), V, V, V, V, I32, V, V,
+                                            ctypes.c_float, V, ctypes.c_size_t, V]
         L.kivi_stream_read.argtypes = [V, ctypes.c_size_t, I32, V, V]
         L.kivi_strerror.argtypes = [ctypes.c_int]
         L.kivi_strerror.restype = ctypes.c_char_p
@@ -276,6 +279,26 @@ def decode_attn_sink(cache, q, sm_scale, k_sink, v_sink, rope_base=0.0, out=None
                                        ctypes.c_double(rope_base), workspace.data_ptr(),
                                        ctypes.c_size_t(nbytes), _stream()),
            "kivi_decode_attn_sink")
+    return out
+
+
+def decode_step_sink(cache, k_new, v_new, q, sm_scale, k_sink, v_sink, out=None,
+                     workspace=None):
+    """decode_step whose decode runs over fp16 sink tokens (k_sink, v_sink:
+    fp16 [batch, heads, n_sink, head_dim]) followed by the cache's tokens."""
+    d = cache.dims
+    _need(k_new, torch.float16, (d.batch, d.heads, d.head_dim), "k_new")
+    _need(v_new, torch.float16, (d.batch, d.heads, d.head_dim), "v_new")
+    n_sink = k_sink.shape[2] if k_sink.dim() == 4 else -1
+    _need(k_sink, torch.float16, (d.batch, d.heads, n_sink, d.head_dim), "k_sink")
+    _need(v_sink, torch.float16, (d.batch, d.heads, n_sink, d.head_dim), "v_sink")
+    out, workspace, nbytes = _decode_buffers(cache, q, out, workspace)
+    _check(lib().kivi_decode_step_sink(ctypes.byref(d), ctypes.byref(cache.struct()),
+                                       k_new.data_ptr(), v_new.data_ptr(), k_sink.data_ptr(),
+                                       v_sink.data_ptr(), ctypes.c_int32(n_sink), q.data_ptr(),
+                                       out.data_ptr(), ctypes.c_float(sm_scale),
+                                       workspace.data_ptr(), ctypes.c_size_t(nbytes), _stream()),
+           "kivi_decode_step_sink")
     return out
 
 

@@ -278,6 +278,21 @@ int kivi_decode_step(const kivi_dims *dims, const kivi_cache *cache,
                      size_t workspace_bytes, void *stream);
 
 /*
+ * kivi_decode_step with the decode over an fp16 attention-sink segment
+ * first ([P2] future-directions section): the same cache state as
+ * kivi_append_kv, kivi_decode_attn_sink (rope_base 0) and
+ * kivi_flush_residual in that order, the output equal up to rounding; one
+ * kernel under the same condition as kivi_decode_step.  k_sink, v_sink and
+ * n_sink as in kivi_decode_attn_sink (n_sink 0 gives kivi_decode_step).
+ * Errors as kivi_decode_step and kivi_decode_attn_sink.
+ */
+int kivi_decode_step_sink(const kivi_dims *dims, const kivi_cache *cache,
+                          const void *k_new, const void *v_new,
+                          const void *k_sink, const void *v_sink, int32_t n_sink,
+                          const void *q, float *out, float sm_scale,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Measurement aid, not a step of the method: reads `bytes` bytes of device
  * memory at `src` once with 16-byte loads and writes one XOR fold per wave
  * to `sink`, so that its duration gives the HBM read rate the device

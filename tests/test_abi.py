@@ -198,6 +198,13 @@ def test_misaligned_pointers_are_rejected_before_any_launch():
     assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(good), m, f, 4, f, f,
                                    ctypes.c_float(1.0), ctypes.c_double(0.0), f,
                                    ctypes.c_size_t(need), None) == kivi.KIVI_EINVAL
+    for n, ks in ((-1, f), (4097, f), (4, None), (4, m)):
+        assert L.kivi_decode_step_sink(ctypes.byref(d), ctypes.byref(good), f, f, ks, f, n, f, f,
+                                       ctypes.c_float(1.0), f, ctypes.c_size_t(need),
+                                       None) == kivi.KIVI_EINVAL
+    assert L.kivi_decode_step_sink(ctypes.byref(d), ctypes.byref(good), f, f, None, None, 0, f, f,
+                                   ctypes.c_float(1.0), f, ctypes.c_size_t(need - 1),
+                                   None) == kivi.KIVI_ENOSPC
     # with no sink tokens the sink pointers are not read
     assert L.kivi_decode_attn_sink(ctypes.byref(d), ctypes.byref(good), m, None, 0, f, f,
                                    ctypes.c_float(1.0), ctypes.c_double(0.0), f,

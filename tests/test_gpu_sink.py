@@ -134,3 +134,59 @@ def test_rotary_sink_large_grids_and_long_context(workload_number, bits):
     out, ks, vs = _run(c, w, 4, rope_base=10000.0)
     heads = [(0, 0), (7, 21), (15, 39)] if workload_number == 3 else [(0, 0), (0, 31)]
     _check(out, w, ks, vs, heads, rope_base=10000.0)
+
+
+# ---- the whole step with a sink: one kernel where a workgroup covers a
+# (sequence, head), else the three calls
+
+@pytest.mark.parametrize("batch", [8, 2])
+def test_step_with_sink_matches_three_calls_and_oracle(batch):
+    w = workload(2, batch=batch) if batch != 8 else workload(2)
+    B = w.q.shape[0]
+    base = gpu_cache(w, q_len=w.q_len, r_len=w.r_len - 1)   # the step fills the window
+    assert kivi.decode_step_kernels(base.dims) == (1 if batch == 8 else 3)
+    last = w.lengths - 1
+    k_new = torch.from_numpy(np.ascontiguousarray(w.k[np.arange(B), :, last])).cuda()
+    v_new = torch.from_numpy(np.ascontiguousarray(w.v[np.arange(B), :, last])).cuda()
+    ks, vs = wl.sink_tokens(w, 8)
+    kst, vst = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
+    q = torch.from_numpy(w.q).cuda()
+    a = kivi.KiviCache(**w.dims())
+    b = kivi.KiviCache(**w.dims())
+    for c in (a, b):
+        for n, t in base.buffers().items():
+            getattr(c, n).copy_(t)
+    out_a = kivi.decode_step_sink(a, k_new, v_new, q, 1.0, kst, vst)
+    kivi.append_kv(b, k_new, v_new)
+    out_b = kivi.decode_attn_sink(b, q, 1.0, kst, vst)
+    kivi.flush_residual(b)
+    torch.cuda.synchronize()
+    for n, t in a.buffers().items():
+        assert torch.equal(t, getattr(b, n)), n
+    assert int(a.r_len[0]) == 0 and a.status_bits() == 0
+    assert torch.allclose(out_a, out_b, rtol=1e-5, atol=1e-6)
+    out = out_a.cpu().numpy()
+    # the oracle over the state before the flush (every token in place)
+    _check(out, w, ks, vs, [(0, 0), (B - 1, 31)])
+
+
+def test_step_with_no_sink_is_the_plain_step():
+    w = workload(2)
+    base = gpu_cache(w, q_len=w.q_len, r_len=w.r_len - 1)
+    B = w.q.shape[0]
+    last = w.lengths - 1
+    k_new = torch.from_numpy(np.ascontiguousarray(w.k[np.arange(B), :, last])).cuda()
+    v_new = torch.from_numpy(np.ascontiguousarray(w.v[np.arange(B), :, last])).cuda()
+    empty = torch.empty((B, 32, 0, 128), dtype=torch.float16, device="cuda")
+    q = torch.from_numpy(w.q).cuda()
+    a = kivi.KiviCache(**w.dims())
+    b = kivi.KiviCache(**w.dims())
+    for c in (a, b):
+        for n, t in base.buffers().items():
+            getattr(c, n).copy_(t)
+    out_a = kivi.decode_step_sink(a, k_new, v_new, q, 1.0, empty, empty)
+    out_b = kivi.decode_step(b, k_new, v_new, q, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    for n, t in a.buffers().items():
+        assert torch.equal(t, getattr(b, n)), n
