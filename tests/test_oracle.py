@@ -191,6 +191,26 @@ def test_packing_hand_cases(golden_dir):
         assert np.array_equal(opack.unpack_tiles(packed, bits), codes)
 
 
+def test_value_group_tile_order_hand_cases(golden_dir):
+    """Value zero-points and steps land in the documented tile order
+    [n / G][j][n % G] (hand-worked fixtures), and dequantizing a cache that
+    holds those tiles gives the rows back exactly (every value of the
+    fixtures is on a level of its group)."""
+    rows = _read_cases(os.path.join(golden_dir, "value_tile_cases.txt"))
+    assert len(rows) >= 2
+    for bits, G, D, toks, zeros, steps, _why in rows:
+        bits, G, D = int(bits), int(G), int(D)
+        v = np.array([[float(x) for x in t.split()] for t in toks.split("|")], np.float16)
+        assert v.shape[1] == D and v.shape[0] % G == 0
+        enc = ocache.encode_tokens(v, v, G, bits)
+        assert enc["v_zero"].shape == (v.shape[0] // G, D // G, G)
+        assert enc["v_zero"].reshape(-1).tolist() == [float(x) for x in zeros.split()]
+        assert enc["v_scale"].reshape(-1).tolist() == [float(x) for x in steps.split()]
+        st = ocache.head_state(v, v, v.shape[0], 0, G, bits, v.shape[0], G)
+        _, vv = ocache.context(st, G, bits)
+        assert np.array_equal(vv, v.astype(np.float64))
+
+
 @pytest.mark.parametrize("bits,G", [(2, 32), (2, 128), (4, 32), (4, 128), (8, 32), (8, 128)])
 def test_pack_unpack_round_trip(bits, G):
     rng = np.random.default_rng(bits * G)
@@ -414,3 +434,50 @@ def test_per_channel_keys_beat_per_token_keys_on_outlier_channels():
     kf = keys.astype(np.float64)
     assert np.abs(per_channel - kf).mean() < np.abs(per_token - kf).mean()
     assert np.abs((per_channel - kf) @ q).mean() < np.abs((per_token - kf) @ q).mean()
+
+
+# ------------------------------------------------------------- axis ablation
+
+def test_axis_ablation_errors_hand_case():
+    """The four error measures of the axis ablation on a 4-token, 4-channel
+    case worked out by hand (G = 4, B = 2).
+
+    Keys K (rows are tokens): (1 2 -1 0), (1 2 -1 1), (1 2 -1 2), (1 2 -1 6);
+    values 3 * I; q = (1, 0, 0, 1); alpha = ln 2, so exp(alpha s) = 2^s.
+    * Per channel, columns 0-2 are constant (exact) and column 3 is the group
+      (0, 1, 2, 6): step 2, token 1's quotient 0.5 rounds to the even code
+      0, so K_hat - K is -1 at (1, 3) and 0 elsewhere.
+    * Per token, rows 0-2 span -1..2 with step 1 (exact); row 3 spans -1..6:
+      step fp16(7/3) = 1195/512, codes (1, 1, 0, 3), dequantized
+      (683/512, 683/512, -1, 3073/512), error (171, -341, 0, 1) / 512.
+    * The values 3 * I are exact on either axis (groups {0, 3}, step 1).
+    sum |K| = 25, ||K||_F^2 = 65, K q = (1, 2, 3, 7).  The unquantized
+    attention weights are (2, 4, 8, 128) / 142 and the output is 3 times
+    them, so the output error is the relative error of the weights: per
+    channel the scores become (1, 1, 3, 7), weights (2, 2, 8, 128) / 140;
+    per token (1, 2, 3, 7 + 43/128)."""
+    from oracle import axis_ablation as ab
+
+    k = np.array([[1, 2, -1, 0], [1, 2, -1, 1], [1, 2, -1, 2], [1, 2, -1, 6]], np.float16)
+    v = (3 * np.eye(4)).astype(np.float16)
+    q = np.array([1, 0, 0, 1], np.float16)
+
+    def norm(x):
+        return math.sqrt(sum(float(a) ** 2 for a in x))
+
+    p = [Fraction(x, 142) for x in (2, 4, 8, 128)]
+    p_ch = [Fraction(x, 140) for x in (2, 2, 8, 128)]
+    t = 128 * 2 ** (43 / 128)
+    p_tok = [x / (14 + t) for x in (2, 4, 8, t)]
+    want = {
+        "channel": {"key_mean": 1 / 25, "key": 1 / math.sqrt(65), "score": 1 / math.sqrt(63),
+                    "output": norm([a - b for a, b in zip(p_ch, p)]) / norm(p)},
+        "token": {"key_mean": 513 / 12800, "key": math.sqrt(171 ** 2 + 341 ** 2 + 1) / 512 / math.sqrt(65),
+                  "score": (172 / 512) / math.sqrt(63),
+                  "output": norm([a - float(b) for a, b in zip(p_tok, p)]) / norm(p)},
+    }
+    for ka in ("channel", "token"):
+        for va in ("channel", "token"):
+            got = ab.errors(k, v, q, math.log(2), 4, 2, ka, va)
+            for m, x in want[ka].items():
+                assert got[m] == pytest.approx(x, rel=1e-12), (ka, va, m)

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as oatt
+import oracle.axis_ablation as oab
 import oracle.cache as ocache
 import oracle.packing as opack
 import oracle.quantizer as oq
@@ -100,6 +101,42 @@ def _merge_without_rescale(parts):
     return sum(a for _, _, a in parts) / sum(l for _, l, _ in parts)
 
 
+def _tile_token_major(a, group):
+    n, ng = a.shape
+    return np.ascontiguousarray(a.reshape(n // group, group, ng))
+
+
+def _untile_token_major(a):
+    t, group, ng = a.shape
+    return a.reshape(t * group, ng)
+
+
+def _untile_group_major_misread(a):
+    # reads the tiles as if they were token-major
+    t, ng, group = a.shape
+    return a.reshape(t * group, ng)
+
+
+_ERRORS = oab.errors
+
+
+def _errors_score_undivided(k, v, q, alpha, group, bits, k_axis, v_axis):
+    e = _ERRORS(k, v, q, alpha, group, bits, k_axis, v_axis)
+    kf, qf = k.astype(np.float64), np.asarray(q, np.float64)
+    e["score"] *= float(np.linalg.norm(kf @ qf))
+    return e
+
+
+def _errors_output_over_quantized(k, v, q, alpha, group, bits, k_axis, v_axis):
+    e = _ERRORS(k, v, q, alpha, group, bits, k_axis, v_axis)
+    kf, vf, qf = k.astype(np.float64), v.astype(np.float64), np.asarray(q, np.float64)
+    kh = oab.quantize_axis(k, k_axis, group, bits)
+    vh = oab.quantize_axis(v, v_axis, group, bits)
+    ref, got = oatt.attention(qf, kf, vf, alpha), oatt.attention(qf, kh, vh, alpha)
+    e["output"] = float(np.linalg.norm(got - ref) / np.linalg.norm(got))
+    return e
+
+
 _ATT = oatt.attention
 _ORIG_FLUSH = ocache.Cache.flush
 
@@ -140,6 +177,14 @@ MUTANTS = [
     ("merge without exp(m_j - M) rescaling", oatt, "merge", _merge_without_rescale,
      ["test_split_merge_equals_single_pass"]),
     ("flush keeps the window length", ocache.Cache, "flush", _flush_keeps_window, STREAM_PINS),
+    ("value tiles stored and read token-major", ocache, ("tile_value_groups", "untile_value_groups"),
+     (_tile_token_major, _untile_token_major), ["test_value_group_tile_order_hand_cases"]),
+    ("value tiles read token-major", ocache, "untile_value_groups", _untile_group_major_misread,
+     ["test_value_group_tile_order_hand_cases"]),
+    ("ablation score error without its denominator", oab, "errors", _errors_score_undivided,
+     ["test_axis_ablation_errors_hand_case"]),
+    ("ablation output error relative to the quantized output", oab, "errors",
+     _errors_output_over_quantized, ["test_axis_ablation_errors_hand_case"]),
 ]
 
 
@@ -161,7 +206,11 @@ def _run(name, golden_dir):
 
 @pytest.mark.parametrize("label,module,attr,mutant,pin_names", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_planted_mistake(label, module, attr, mutant, pin_names, monkeypatch, golden_dir):
-    monkeypatch.setattr(module, attr, mutant)
+    if isinstance(attr, tuple):  # a mistake made the same way in several functions
+        for a, m in zip(attr, mutant):
+            monkeypatch.setattr(module, a, m)
+    else:
+        monkeypatch.setattr(module, attr, mutant)
     caught = []
     for name in pin_names:
         try:
