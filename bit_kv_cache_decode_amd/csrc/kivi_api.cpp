@@ -102,6 +102,24 @@ int kivi_validate_dims(const kivi_dims *d) {
   return KIVI_OK;
 }
 
+int kivi_cache_init(const kivi_dims *dims, const kivi_cache *cache, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache)) return KIVI_EINVAL;
+  return kivi::hip_rc(kivi::launch_cache_init(*dims, *cache, stream));
+}
+
+int kivi_workspace_init(const kivi_dims *dims, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::a16(workspace)) return KIVI_EINVAL;
+  const kivi::DecodePlan p = kivi::decode_plan(*dims);
+  if (workspace_bytes < p.bytes) return KIVI_ENOSPC;
+  return kivi::hip_rc(kivi::launch_fill_zero(static_cast<char *>(workspace) + p.counters_off,
+                                             p.bytes - p.counters_off, stream));
+}
+
 int kivi_append_kv(const kivi_dims *dims, const kivi_cache *cache, const void *k_new,
                    const void *v_new, void *stream) {
   const int rc = kivi::check_dims(dims);

@@ -63,6 +63,8 @@ int launch_prefill(const kivi_dims &d, const kivi_cache &c, const void *k,
 int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
                   const void *q, float *out, float sm_scale, void *workspace,
                   void *stream);
+int launch_cache_init(const kivi_dims &d, const kivi_cache &c, void *stream);
+int launch_fill_zero(void *p, size_t bytes, void *stream);
 int launch_stream_read(const void *src, size_t bytes, int workgroups, uint32_t *sink,
                        void *stream);
 int launch_decode_sink(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,

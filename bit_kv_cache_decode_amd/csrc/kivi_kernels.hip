@@ -17,6 +17,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "kivi_internal.h"
@@ -522,12 +523,14 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
 
 // Flush: grid (R / (G P), heads, batch); one workgroup of P x 256 threads
 // quantizes P tiles of G window tokens of one (sequence, head), 256 threads
-// per tile (P below, chosen by the launcher).  Each workgroup takes
-// one of sequence b's tickets once it has read b's lengths (the atomic's
-// latency hides behind the window loads); the workgroup that took the last
-// one (every tile of every head has read the lengths by then, and none reads
-// them again) sets q_len[b] += R, r_len[b] = 0 and clears the ticket when it
-// is done.
+// per tile (P below, chosen by the launcher).  Thread 0 reads b's lengths
+// and hands them to the other threads through LDS behind a barrier, then
+// takes one of sequence b's tickets (the atomic's latency hides behind the
+// window loads); the workgroup that took the last one (every workgroup of
+// the sequence has read the lengths by then, and none reads them again)
+// sets q_len[b] += R, r_len[b] = 0 and clears the ticket when it is done.
+// A ticket at or past the count means the counter did not start at zero
+// (cache->tickets not initialised): KIVI_ST_TICKETS, and no commit.
 constexpr int kFlushThreads = 256;
 // Window tiles a flush workgroup takes side by side (at most).  Two measured
 // best: the workgroup dispatcher starts about 230 workgroups per microsecond,
@@ -541,13 +544,20 @@ template <int BITS, int G, int P>
 __global__ __launch_bounds__(kFlushThreads * P) void flush_kernel(EncodeArgs a) {
   const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int part = tid / kFlushThreads, tile = blockIdx.x * P + part;
-  const int ql = a.q_len[b], rl = a.r_len[b];
+  __shared__ int lens[2];
+  if (tid == 0) {
+    lens[0] = a.q_len[b];
+    lens[1] = a.r_len[b];
+  }
+  __syncthreads();
+  const int ql = lens[0], rl = lens[1];
   if (!flush_ok(ql, rl, G, a.R, a.cap)) {
     if (rl == a.R && blockIdx.x == 0 && h == 0 && tid == 0)
       atomicOr(a.status, (ql < 0 || ql % G) ? KIVI_ST_BAD_LENGTH : KIVI_ST_CAPACITY);
     return;
   }
   uint32_t ticket = 0;
+  const uint32_t n_tickets = (uint32_t)(a.heads * (a.R / G / P));
   if (tid == 0)
     ticket = __hip_atomic_fetch_add(a.tickets + (size_t)b * kTicketStride, 1u, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
@@ -556,11 +566,12 @@ __global__ __launch_bounds__(kFlushThreads * P) void flush_kernel(EncodeArgs a) 
   __shared__ FlushSmem<G, G> fs[P];
   flush_window<BITS, G, G, kFlushThreads>(a, (size_t)b * a.heads + h, ql, tid % kFlushThreads,
                                           fs[part], -1, nullptr, nullptr, tile * G, tile * G + G);
-  if (tid == 0 && ticket == (uint32_t)(a.heads * (a.R / G / P)) - 1) {
+  if (tid == 0 && ticket == n_tickets - 1) {
     a.q_len[b] = ql + a.R;
     a.r_len[b] = 0;
     a.tickets[(size_t)b * kTicketStride] = 0u;
   }
+  if (tid == 0 && ticket >= n_tickets) atomicOr(a.status, KIVI_ST_TICKETS);
 }
 
 // Prefill: copy the window part [n - r, n) of each valid prompt to slots [0, r).
@@ -672,8 +683,9 @@ struct DecodeArgs {
   float qscale;  // sm_scale * log2(e)
   int heads, R, cap, splits, win_per_wave, part_stride;
   double rope_log2_base;  // log2 of the rotary base (ROPE kernels only)
-  // fp16 sink tokens [batch][heads][n_sink][D] (plain decode only; n_sink 0
-  // elsewhere), sink_per_wave of them per wave
+  // fp16 sink tokens [batch][heads][n_sink][D] (every decode variant: plain,
+  // rotary and whole step; n_sink 0 when there is none), sink_per_wave of
+  // them per wave
   const half_t *k_sink, *v_sink;
   int n_sink, sink_per_wave;
 };
@@ -717,6 +729,7 @@ struct DecSmem {
     } mg;
   } u;
   int ticket;
+  int lens[2];             // whole step: the sequence's lengths, read once
   int prog[kDecodeWaves];  // sub-chunks each wave has started (issue priority)
   // ROPE: key zero-points of the touched tiles, word-padded like qp (kept
   // out of the per-wave staging above so that its layout, and the 16-byte
@@ -1496,7 +1509,22 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
   const size_t bh = (size_t)b * a.heads + h;
   const int S = a.splits;
 
-  int ql = a.q_len[b], rl = a.r_len[b];
+  int ql, rl;
+  if constexpr (FUSED) {
+    // the lengths this kernel commits: thread 0 reads them and hands them to
+    // every wave behind a barrier, so every read of them in this workgroup
+    // comes before its ticket (and so before any workgroup commits)
+    if (tid == 0) {
+      sm.lens[0] = a.q_len[b];
+      sm.lens[1] = a.r_len[b];
+    }
+    __syncthreads();
+    ql = sm.lens[0];
+    rl = sm.lens[1];
+  } else {
+    ql = a.q_len[b];
+    rl = a.r_len[b];
+  }
   // Whole step (FUSED, one workgroup per (sequence, head)): append the new
   // token at window slot rnew, decode over the window including it, and
   // flush the window if that filled it; the same results as the three
@@ -1813,6 +1841,8 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
         ea.r_len[b] = flush ? 0 : rl1;
         ea.tickets[(size_t)b * kTicketStride] = 0u;
       }
+      // a counter that did not start at zero: no commit, and the caller is told
+      if (commit && tid == 0 && ticket >= (uint32_t)a.heads) atomicOr(a.status, KIVI_ST_TICKETS);
     }
     return;
   }
@@ -1838,7 +1868,13 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
     sm.ticket = (int)__hip_atomic_fetch_add(a.tickets + bh * kTicketStride, 1u, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (sm.ticket != S - 1) return;
+  if (sm.ticket != S - 1) {
+    // a ticket at or past the split count: the workspace's counter did not
+    // start at zero (workspace not initialised), so no workgroup can tell it
+    // is the last; the caller is told through the status word
+    if (tid == 0 && (uint32_t)sm.ticket >= (uint32_t)S) atomicOr(a.status, KIVI_ST_TICKETS);
+    return;
+  }
 
   // ---- last workgroup of this (sequence, head): merge all partials, read
   // with device-scope atomic loads (coherent with the stores above)
@@ -1898,6 +1934,28 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off);
   if ((threadIdx.x & 63) == 0) sink[(size_t)blockIdx.x * (kStreamThreads / 64) + threadIdx.x / 64] = x;
+}
+
+// Zero-fill n 32-bit words (a kernel, not a memset, so that a caller may
+// capture it in a HIP graph).
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(uint32_t *p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * kThreads)
+    p[i] = 0u;
+}
+
+// An empty cache: lengths, ticket counters and the status word zero.
+__global__ __launch_bounds__(kThreads) void cache_init_kernel(int32_t *q_len, int32_t *r_len,
+                                                              uint32_t *tickets, uint32_t *status,
+                                                              int batch) {
+  for (int i = threadIdx.x; i < batch * kTicketStride; i += kThreads) {
+    tickets[i] = 0u;
+    if (i < batch) {
+      q_len[i] = 0;
+      r_len[i] = 0;
+    }
+  }
+  if (threadIdx.x == 0) *status = 0u;
 }
 
 template <int BITS, int G>
@@ -2107,6 +2165,22 @@ int launch_decode_any(const kivi_dims &d, const DecodeArgs &da, const EncodeArgs
 }
 
 }  // namespace
+
+int launch_cache_init(const kivi_dims &d, const kivi_cache &c, void *stream) {
+  hipLaunchKernelGGL(cache_init_kernel, dim3(1), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), c.q_len, c.r_len, c.tickets, c.status,
+                     d.batch);
+  return (int)hipGetLastError();
+}
+
+int launch_fill_zero(void *p, size_t bytes, void *stream) {
+  const size_t n = bytes / 4;
+  if (n == 0) return 0;
+  const size_t blocks = std::min<size_t>((n + kThreads - 1) / kThreads, 1024);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint32_t *>(p), n);
+  return (int)hipGetLastError();
+}
 
 int launch_stream_read(const void *src, size_t bytes, int workgroups, uint32_t *sink,
                        void *stream) {

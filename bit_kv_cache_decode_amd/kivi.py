@@ -18,10 +18,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkivi.so")
 
 KIVI_OK, KIVI_EINVAL, KIVI_ENOSPC, KIVI_EHIP, KIVI_EUNSUPPORTED = 0, -1, -2, -3, -4
-ST_RESIDUAL_FULL, ST_CAPACITY, ST_BAD_LENGTH = 0x1, 0x2, 0x4
+ST_RESIDUAL_FULL, ST_CAPACITY, ST_BAD_LENGTH, ST_TICKETS = 0x1, 0x2, 0x4, 0x8
 
 # Every symbol the public header declares.
-EXPORTS = ("kivi_validate_dims", "kivi_append_kv", "kivi_flush_residual", "kivi_prefill",
+EXPORTS = ("kivi_validate_dims", "kivi_cache_init", "kivi_workspace_init", "kivi_append_kv", "kivi_flush_residual", "kivi_prefill",
            "kivi_decode_workspace_bytes", "kivi_decode_splits", "kivi_decode_step_kernels", "kivi_decode_attn",
            "kivi_decode_attn_rope", "kivi_decode_attn_sink", "kivi_decode_step",
            "kivi_decode_step_sink", "kivi_stream_read",
@@ -58,6 +58,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, V, I32 = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int32
         L.kivi_validate_dims.argtypes = [P(Dims)]
+        L.kivi_cache_init.argtypes = [P(Dims), P(CacheStruct), V]
+        L.kivi_workspace_init.argtypes = [P(Dims), V, ctypes.c_size_t, V]
         L.kivi_append_kv.argtypes = [P(Dims), P(CacheStruct), V, V, V]
         L.kivi_flush_residual.argtypes = [P(Dims), P(CacheStruct), V]
         L.kivi_prefill.argtypes = [P(Dims), P(CacheStruct), V, V, I32, V, V, V]
@@ -184,6 +186,23 @@ class KiviCache:
 
     def nbytes(self):
         return sum(t.numel() * t.element_size() for t in self.buffers().values())
+
+
+def cache_init(cache):
+    """kivi_cache_init: empty the cache (lengths, ticket counters, status)."""
+    d = cache.dims
+    _check(lib().kivi_cache_init(ctypes.byref(d), ctypes.byref(cache.struct()), _stream()),
+           "kivi_cache_init")
+
+
+def workspace_init(dims, workspace):
+    """kivi_workspace_init: zero the split-merge counters of a workspace."""
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    _check(lib().kivi_workspace_init(ctypes.byref(dims), workspace.data_ptr(),
+                                     ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                     _stream()), "kivi_workspace_init")
 
 
 def append_kv(cache, k_new, v_new):

@@ -51,6 +51,10 @@ extern "C" {
 #define KIVI_ST_RESIDUAL_FULL 0x1u /* append found r_len == R: token dropped  */
 #define KIVI_ST_CAPACITY      0x2u /* flush/prefill would pass capacity       */
 #define KIVI_ST_BAD_LENGTH    0x4u /* a length array held an impossible value */
+#define KIVI_ST_TICKETS       0x8u /* a ticket counter (cache->tickets or the
+                                      decode workspace) did not start at zero:
+                                      it was never initialised; that call's
+                                      length commit or split merge is lost */
 
 /*
  * Problem dimensions.  The names follow the pages' parameters:
@@ -97,8 +101,11 @@ typedef struct {
  *   tickets uint32 [batch][64]  per-sequence counters of kivi_flush_residual
  *                          and kivi_decode_step (element [b][0]; the rest
  *                          of each row keeps counters on separate cache
- *                          lines); zero-filled before first use, left
- *                          zero-filled by every call.
+ *                          lines); zero before first use (kivi_cache_init
+ *                          or a zero-filled allocation), left zero by every
+ *                          call.  A counter found non-zero is reported as
+ *                          KIVI_ST_TICKETS and that sequence's lengths are
+ *                          then not committed.
  * Sequence b's context is its q_len[b] quantized tokens followed by its
  * r_len[b] window tokens, oldest first.
  *
@@ -121,6 +128,30 @@ typedef struct {
 
 /* Host-only check of dims; KIVI_OK, KIVI_EINVAL or KIVI_EUNSUPPORTED. */
 int kivi_validate_dims(const kivi_dims *dims);
+
+/*
+ * Make a freshly allocated cache empty and ready: q_len[b] = r_len[b] = 0
+ * for every sequence, every element of cache->tickets and *status zero.
+ * Codes, scales, zeros and the window are left as they are (an empty
+ * cache never reads them).  Enqueued as one kernel on `stream` (no memset,
+ * so it may be captured in a HIP graph); allocates nothing.  Every other
+ * call leaves cache->tickets zero again, so this is needed once per cache
+ * (or after a KIVI_ST_TICKETS report).  KIVI_EINVAL for bad dims or a null
+ * or misaligned pointer.
+ */
+int kivi_cache_init(const kivi_dims *dims, const kivi_cache *cache, void *stream);
+
+/*
+ * Make a decode workspace ready for use: zero-fills the counters that
+ * kivi_decode_attn and its variants use to find the last workgroup of a
+ * split (sequence, head).  workspace_bytes must be at least
+ * kivi_decode_workspace_bytes(dims) (else KIVI_ENOSPC).  One kernel on
+ * `stream` (no memset); allocates nothing.  Every decode leaves the counters
+ * zero again, so this is needed once per workspace (or after a
+ * KIVI_ST_TICKETS report); a workspace allocated zero-filled needs no call.
+ */
+int kivi_workspace_init(const kivi_dims *dims, void *workspace, size_t workspace_bytes,
+                        void *stream);
 
 /*
  * Append one new token per sequence to the fp16 window ([P1] section 3.2:
@@ -190,9 +221,13 @@ int kivi_decode_step_kernels(const kivi_dims *dims);
  *   q        fp16 [batch][heads][D], device
  *   out      fp32 [batch][heads][D], device (written)
  *   workspace  device buffer of at least kivi_decode_workspace_bytes(dims)
- *            bytes.  It must be zero-filled before its first use; every call
- *            leaves it zero-filled again.  One workspace must not be used by
- *            two calls that can run at the same time.
+ *            bytes.  Before its first use it must go through
+ *            kivi_workspace_init (or be allocated zero-filled); every call
+ *            leaves its counters zero again.  A workspace whose counters
+ *            were not zero makes the split merge of that call lose its
+ *            output for the (sequence, head) pairs split over several
+ *            workgroups, and sets KIVI_ST_TICKETS.  One workspace must not
+ *            be used by two calls that can run at the same time.
  * Read-only on the cache.  A sequence whose lengths are impossible (q_len not
  * a multiple of G or above capacity, r_len outside [0, R]) gets out = 0 and
  * KIVI_ST_BAD_LENGTH.  Returns KIVI_ENOSPC if workspace_bytes is too small.

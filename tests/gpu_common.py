@@ -1,7 +1,10 @@
 """Shared helpers of the GPU parity tests (imported only by tests)."""
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
+from threadpoolctl import threadpool_limits
 
 from bit_kv_cache_decode_amd import kivi
 from bit_kv_cache_decode_amd import workloads as wl
@@ -23,11 +26,13 @@ def workload(number, bits=None, batch=None):
     return _WORKLOADS[key]
 
 
-def gpu_cache(w, capacity=None, q_len=None, r_len=None):
+def gpu_cache(w, capacity=None, q_len=None, r_len=None, residual=None):
     """Cache on the GPU holding the workload's tokens, built by kivi_prefill."""
     d = w.dims()
     if capacity is not None:
         d["capacity"] = capacity
+    if residual is not None:
+        d["residual"] = residual
     ql = w.q_len if q_len is None else np.asarray(q_len, np.int32)
     rl = w.r_len if r_len is None else np.asarray(r_len, np.int32)
     c = kivi.KiviCache(**d)
@@ -84,3 +89,28 @@ def assert_within_tolerance(out, ref, label=""):
     mx, rel = decode_errors(out, ref)
     assert mx <= MAX_ABS and rel <= REL_L2, f"{label}: max-abs {mx:.3e}, rel-L2 {rel:.3e}"
     return mx, rel
+
+
+def parallel_map(fn, items, workers=8):
+    """fn over items on a pool of threads, numpy's BLAS held to one thread
+    each (the oracle's array work releases the interpreter lock); returns the
+    results in order."""
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, items))
+
+
+def host_buffers(c):
+    """Every buffer of a GPU cache as numpy arrays (codes as uint32)."""
+    out = {n: t.cpu().numpy() for n, t in c.buffers().items()}
+    for n in ("k_codes", "v_codes", "tickets", "status"):
+        out[n] = out[n].view(np.uint32)
+    return out
+
+
+def head_of(buffers, b, h):
+    """One (sequence, head) of host_buffers() in the head_buffers() form."""
+    out = {n: buffers[n][b, h] for n in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale",
+                                          "v_zero", "k_res", "v_res")}
+    out["q_len"] = int(buffers["q_len"][b])
+    out["r_len"] = int(buffers["r_len"][b])
+    return out

@@ -165,27 +165,6 @@ def test_flush_of_a_large_batch_with_few_full_windows():
             assert np.array_equal(got.view(np.uint8), enc[name].view(np.uint8)), (name, b, h)
 
 
-def test_ragged_serving_sampled_heads():
-    w = workload(4)
-    c = gpu_cache(w)
-    assert np.array_equal(c.q_len.cpu().numpy(), w.q_len)
-    assert np.array_equal(c.r_len.cpu().numpy(), w.r_len)
-    rng = np.random.default_rng(404)
-    heads = {(int(b), int(h)) for b, h in zip(rng.integers(0, 64, 48), rng.integers(0, 32, 48))}
-    # the shortest and longest sequences, and ones with empty / full-ish windows
-    for b in {int(np.argmin(w.lengths)), int(np.argmax(w.lengths)), int(np.argmin(w.r_len)),
-              int(np.argmax(w.r_len))}:
-        heads.update({(b, 0), (b, 31)})
-    _check_heads(c, w, sorted(heads))
-
-
-@pytest.mark.parametrize("bits", [2, 4, 8])
-def test_long_context_sampled_heads(bits):
-    w = workload(5, bits=bits)
-    c = gpu_cache(w)
-    _check_heads(c, w, [(0, 0), (0, 9), (0, 22), (0, 31)])
-
-
 def test_streaming_appends_and_flushes_match_prefill():
     """Token-by-token appends with a flush after each, on the GPU, give the
     same buffers as one GPU prefill and as the oracle's streaming cache."""

@@ -139,20 +139,30 @@ def test_rotary_sink_large_grids_and_long_context(workload_number, bits):
 # ---- the whole step with a sink: one kernel where a workgroup covers a
 # (sequence, head), else the three calls
 
-@pytest.mark.parametrize("batch", [8, 2])
-def test_step_with_sink_matches_three_calls_and_oracle(batch):
+@pytest.mark.parametrize("batch,case", [(8, "fills"), (2, "fills"), (8, "append_only"),
+                                        (8, "long_window")])
+def test_step_with_sink_matches_three_calls_and_oracle(batch, case):
+    """The step with a sink in one kernel (batch 8) or three (batch 2), for a
+    step whose append fills the window (flushed from registers), an append
+    that leaves it short of full (the common step), and a 256-token window
+    (flushed by re-reading it through LDS): the cache as the three calls
+    leave it, bit for bit, and the output against the oracle."""
     w = workload(2, batch=batch) if batch != 8 else workload(2)
     B = w.q.shape[0]
-    base = gpu_cache(w, q_len=w.q_len, r_len=w.r_len - 1)   # the step fills the window
+    R = 256 if case == "long_window" else 128
+    ql = w.q_len - (128 if case == "long_window" else 0)
+    rl = {"fills": w.r_len - 1, "append_only": w.r_len - 3,
+          "long_window": np.full(B, 255, np.int32)}[case].astype(np.int32)
+    base = gpu_cache(w, q_len=ql, r_len=rl, residual=R)
     assert kivi.decode_step_kernels(base.dims) == (1 if batch == 8 else 3)
-    last = w.lengths - 1
+    last = ql + rl                                           # the appended token
     k_new = torch.from_numpy(np.ascontiguousarray(w.k[np.arange(B), :, last])).cuda()
     v_new = torch.from_numpy(np.ascontiguousarray(w.v[np.arange(B), :, last])).cuda()
     ks, vs = wl.sink_tokens(w, 8)
     kst, vst = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
     q = torch.from_numpy(w.q).cuda()
-    a = kivi.KiviCache(**w.dims())
-    b = kivi.KiviCache(**w.dims())
+    a = kivi.KiviCache(**base.shape)
+    b = kivi.KiviCache(**base.shape)
     for c in (a, b):
         for n, t in base.buffers().items():
             getattr(c, n).copy_(t)
@@ -163,11 +173,17 @@ def test_step_with_sink_matches_three_calls_and_oracle(batch):
     torch.cuda.synchronize()
     for n, t in a.buffers().items():
         assert torch.equal(t, getattr(b, n)), n
-    assert int(a.r_len[0]) == 0 and a.status_bits() == 0
+    flushed = case != "append_only"
+    assert a.r_len.cpu().tolist() == ([0] * B if flushed else (rl + 1).tolist())
+    assert a.status_bits() == 0
     assert torch.allclose(out_a, out_b, rtol=1e-5, atol=1e-6)
     out = out_a.cpu().numpy()
-    # the oracle over the state before the flush (every token in place)
-    _check(out, w, ks, vs, [(0, 0), (B - 1, 31)])
+
+    # the oracle over the state before any flush (every token in place)
+    def state(w, bb, h):
+        return ocache.head_state(w.k[bb, h], w.v[bb, h], int(ql[bb]), int(rl[bb]) + 1, 32, 2,
+                                 4096, R)
+    _check(out, w, ks, vs, [(0, 0), (B - 1, 31), (B // 2, 7)], state)
 
 
 def test_step_with_no_sink_is_the_plain_step():
