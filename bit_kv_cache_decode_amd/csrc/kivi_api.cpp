@@ -175,6 +175,22 @@ int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache, const void 
   return kivi::hip_rc(kivi::launch_decode(*dims, *cache, p, q, out, sm_scale, workspace, stream));
 }
 
+int kivi_decode_attn_noalloc(const kivi_dims *dims, const kivi_cache *cache, const void *q,
+                             float *out, float sm_scale, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache) || !kivi::a16(q) || !kivi::a4(out)) return KIVI_EINVAL;
+  if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
+    return KIVI_EINVAL;
+  const kivi::DecodePlan p = kivi::decode_plan(*dims);
+  const long pairs = (long)dims->batch * dims->heads;
+  const size_t parts = (size_t)pairs * p.splits * p.part_floats * sizeof(float);
+  if (pairs > kivi::kNoAllocPairs ||
+      parts > kivi::kNoAllocScratchBytes - kivi::kNoAllocTicketBytes)
+    return KIVI_ENOSPC;
+  return kivi::hip_rc(kivi::launch_decode_noalloc(*dims, *cache, p, q, out, sm_scale, stream));
+}
+
 int kivi_decode_attn_sink(const kivi_dims *dims, const kivi_cache *cache, const void *k_sink,
                           const void *v_sink, int32_t n_sink, const void *q, float *out,
                           float sm_scale, double rope_base, void *workspace,

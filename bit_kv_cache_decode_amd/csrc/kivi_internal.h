@@ -63,6 +63,21 @@ int launch_prefill(const kivi_dims &d, const kivi_cache &c, const void *k,
 int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
                   const void *q, float *out, float sm_scale, void *workspace,
                   void *stream);
+// Allocation-free decode (kivi_decode_attn_noalloc): its split partials and
+// counters live in one file-scope device array of kNoAllocScratchBytes per
+// GPU.  The counters take the first kNoAllocTicketBytes at a fixed place (one
+// 256-byte line per (sequence, head), at most kNoAllocPairs pairs), so no
+// call's partials ever land where a later call expects zeroed counters; the
+// partials follow.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+constexpr size_t kNoAllocTicketBytes = (size_t)1 << 20;
+constexpr long kNoAllocPairs = (long)(kNoAllocTicketBytes / (kTicketStride * 4));
+
+// 0, a hipError_t value, or -1 when the device array's address could not be
+// obtained.
+int launch_decode_noalloc(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
+                          const void *q, float *out, float sm_scale, void *stream);
+
 int launch_cache_init(const kivi_dims &d, const kivi_cache &c, void *stream);
 int launch_fill_zero(void *p, size_t bytes, void *stream);
 int launch_stream_read(const void *src, size_t bytes, int workgroups, uint32_t *sink,

@@ -18,6 +18,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "kivi_internal.h"
@@ -2197,6 +2198,74 @@ int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, 
   const DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, workspace);
   return launch_decode_any(d, da, encode_args(d, c), false, p.depth,
                            static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------- allocation-free decode scratch
+// One array per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is used.  A static
+// __device__ array starts zero-filled; the counters are cleared once more at
+// that set-up, by a kernel on the caller's stream, and every decode leaves
+// them zero.
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+  std::once_flag once;
+  void *ptr = nullptr;
+  int rc = 0;
+};
+
+ScratchSlot g_scratch[kMaxDevices];
+
+// The device address of this GPU's scratch (nullptr on failure), set up on
+// the first call made on each device.
+void *scratch_for_current_device(hipStream_t st, int *rc) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = e != hipSuccess ? (int)e : -1;
+    return nullptr;
+  }
+  ScratchSlot &slot = g_scratch[dev];
+  std::call_once(slot.once, [&]() {
+    void *ptr = nullptr;
+    const hipError_t ge = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (ge != hipSuccess || ptr == nullptr) {
+      slot.rc = ge != hipSuccess ? (int)ge : -1;
+      return;
+    }
+    const size_t n = kNoAllocTicketBytes / 4;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, st, static_cast<uint32_t *>(ptr), n);
+    const hipError_t le = hipGetLastError();
+    if (le != hipSuccess) {
+      slot.rc = (int)le;
+      return;
+    }
+    slot.ptr = ptr;
+  });
+  *rc = slot.rc;
+  return slot.ptr;
+}
+
+}  // namespace
+
+int launch_decode_noalloc(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
+                          const void *q, float *out, float sm_scale, void *stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  int rc = 0;
+  char *base = static_cast<char *>(scratch_for_current_device(st, &rc));
+  if (base == nullptr) return rc != 0 ? rc : -1;
+  // counters first (fixed place), partials after them; the sizes were checked
+  // against the array by the caller
+  DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, base + kNoAllocTicketBytes);
+  da.tickets = reinterpret_cast<uint32_t *>(base);
+  return launch_decode_any(d, da, encode_args(d, c), false, p.depth, st);
 }
 
 int launch_decode_sink(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,

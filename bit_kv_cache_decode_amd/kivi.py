@@ -23,6 +23,7 @@ ST_RESIDUAL_FULL, ST_CAPACITY, ST_BAD_LENGTH, ST_TICKETS = 0x1, 0x2, 0x4, 0x8
 # Every symbol the public header declares.
 EXPORTS = ("kivi_validate_dims", "kivi_cache_init", "kivi_workspace_init", "kivi_append_kv", "kivi_flush_residual", "kivi_prefill",
            "kivi_decode_workspace_bytes", "kivi_decode_splits", "kivi_decode_step_kernels", "kivi_decode_attn",
+           "kivi_decode_attn_noalloc",
            "kivi_decode_attn_rope", "kivi_decode_attn_sink", "kivi_decode_step",
            "kivi_decode_step_sink", "kivi_stream_read",
            "kivi_strerror")
@@ -69,6 +70,7 @@ def lib():
         L.kivi_decode_step_kernels.argtypes = [P(Dims)]
         L.kivi_decode_attn.argtypes = [P(Dims), P(CacheStruct), V, V, ctypes.c_float, V,
                                        ctypes.c_size_t, V]
+        L.kivi_decode_attn_noalloc.argtypes = [P(Dims), P(CacheStruct), V, V, ctypes.c_float, V]
         L.kivi_decode_attn_rope.argtypes = [P(Dims), P(CacheStruct), V, V, ctypes.c_float,
                                             ctypes.c_double, V, ctypes.c_size_t, V]
         L.kivi_decode_attn_sink.argtypes = [P(Dims), P(CacheStruct), V, V, I32, V, V,
@@ -265,6 +267,18 @@ def decode_attn(cache, q, sm_scale, out=None, workspace=None):
     _check(lib().kivi_decode_attn(ctypes.byref(d), ctypes.byref(cache.struct()), q.data_ptr(),
                                   out.data_ptr(), ctypes.c_float(sm_scale), workspace.data_ptr(),
                                   ctypes.c_size_t(nbytes), _stream()), "kivi_decode_attn")
+    return out
+
+
+def decode_attn_noalloc(cache, q, sm_scale, out):
+    """kivi_decode_attn_noalloc: decode_attn with the library's own device
+    array as scratch (nothing is allocated; `out` is required)."""
+    d = cache.dims
+    _need(q, torch.float16, (d.batch, d.heads, d.head_dim), "q")
+    _need(out, torch.float32, (d.batch, d.heads, d.head_dim), "out")
+    _check(lib().kivi_decode_attn_noalloc(ctypes.byref(d), ctypes.byref(cache.struct()),
+                                          q.data_ptr(), out.data_ptr(), ctypes.c_float(sm_scale),
+                                          _stream()), "kivi_decode_attn_noalloc")
     return out
 
 

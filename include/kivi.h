@@ -237,6 +237,25 @@ int kivi_decode_attn(const kivi_dims *dims, const kivi_cache *cache,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kivi_decode_attn without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split partials and their counters
+ * live in one device array inside the library, 8 MiB per GPU, held until the
+ * process ends; this call allocates nothing (no hipMalloc, no hipFree, no
+ * allocating library routine).  The same result as kivi_decode_attn bit for
+ * bit (the same kernels).  Limits: batch * heads <= 4096 and
+ * batch * heads * kivi_decode_splits(dims) * (head_dim + 4) * 4 bytes <= 7 MiB
+ * (the 131072-token, 32-head workload takes 135 KB), else KIVI_ENOSPC with
+ * nothing launched.  Every call on one GPU shares that GPU's array: calls
+ * that can overlap on one GPU (on two streams, or from two threads without
+ * ordering) race and give wrong outputs.  The first call on a device takes
+ * the array's device address and clears its counters with a kernel on
+ * `stream`.  Other arguments and errors as kivi_decode_attn.
+ */
+int kivi_decode_attn_noalloc(const kivi_dims *dims, const kivi_cache *cache,
+                             const void *q, float *out, float sm_scale, void *stream);
+
+/*
  * kivi_decode_attn with an fp16 attention-sink segment ([P2]
  * future-directions section: besides the window of recent tokens, a
  * high-precision window is kept for the attention-sink tokens, the first
