@@ -18,8 +18,12 @@ decodes, all flushes), each phase a HIP graph replayed between HIP events on
 the launch stream, which give the per-kernel average GPU durations of the
 three separate kernels (the decode kernel's feeds the roofline); they must
 leave the cache exactly as the whole-step kernel does, and give its output up
-to rounding.  The CPU oracle is timed beside it on a
-bounded sample of (sequence, head) steps.
+to rounding.  The decode of every other workload (the tiny, 13B, ragged
+batch-64 and 131072-token ones, the last at B=2 and B=4) is then timed the
+same way on rotated cache copies, with the 13B layer's full-window flush
+timed separately, each beside its stream-read ceiling.  The CPU oracle is
+timed beside it on bounded samples of (sequence, head) steps and decodes of
+every workload.
 
 Prints one JSON line on stdout; diagnostics go to stderr.
 """
@@ -53,7 +57,8 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", type=int, default=2, help="workload number (1-5)")
     p.add_argument("--bits", type=int, default=None)
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=8.0,
+                   help="budget of the CPU oracle's whole-step sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch steps eagerly instead of a graph")
     p.add_argument("--rope", type=float, default=None, metavar="BASE",
@@ -61,9 +66,14 @@ def parse_args():
                         "kivi_decode_attn_rope with this base, the step its three calls")
     p.add_argument("--sink", type=int, default=0, metavar="N",
                    help="N fp16 attention-sink tokens ahead of the cache: the decode is "
-                        "kivi_decode_attn_sink, the step its three calls")
+                        "kivi_decode_attn_sink, the step kivi_decode_step_sink (one kernel "
+                        "where one workgroup covers a (sequence, head), else three)")
     p.add_argument("--no-stream", action="store_true",
                    help="skip the stream-read ceiling (kivi_stream_read) measurement")
+    p.add_argument("--no-extra", action="store_true",
+                   help="time only the chosen workload, not the decode of every other one")
+    p.add_argument("--extra-steps", type=int, default=20,
+                   help="decode launches timed per additional workload")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="after the run, copy a buffer of this many MiB once (a known-size "
                         "reference dispatch for scaling hardware byte counters)")
@@ -120,7 +130,6 @@ def cpu_baseline(w, budget_s):
     the budget of timed work is spent.  Each pair's starting state is built
     once, untimed; every timed step runs on a fresh copy of it."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     from oracle import cache as ocache
 
@@ -130,32 +139,33 @@ def cpu_baseline(w, budget_s):
     pairs = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
     states = {}
     done, spent = 0, 0.0
-    with threadpool_limits(limits=1):
-        while spent < budget_s:
-            b, h = pairs[done % len(pairs)]
-            ql, r0 = int(w.q_len[b]), int(r_start[b])
-            if (b, h) not in states:
-                states[(b, h)] = ocache.head_state(w.k[b, h], w.v[b, h], ql, r0, G, B,
-                                                   cfg.capacity, R)
-            st = {k: (v.copy() if isinstance(v, np.ndarray) else v)
-                  for k, v in states[(b, h)].items()}
-            t0 = time.perf_counter()
-            st["k_res"][r0] = k_new[b, h]                         # append
-            st["v_res"][r0] = v_new[b, h]
-            st["r_len"] = rl = r0 + 1
-            ocache.decode_head(w.q[b, h], st, cfg.sm_scale, G, B)  # decode
-            if rl == R:                                           # flush
-                enc = ocache.encode_tokens(st["k_res"], st["v_res"], G, B)
-                g0 = ql // G
-                st["k_codes"][g0:g0 + R // G] = enc["k_codes"]
-                st["v_codes"][g0:g0 + R // G] = enc["v_codes"]
-            spent += time.perf_counter() - t0
-            done += 1
-    return {"value": done / spent, "unit": "query-heads/s", "cores": 1, "kind": "oracle",
+    while spent < budget_s:
+        b, h = pairs[done % len(pairs)]
+        ql, r0 = int(w.q_len[b]), int(r_start[b])
+        if (b, h) not in states:
+            states[(b, h)] = ocache.head_state(w.k[b, h], w.v[b, h], ql, r0, G, B,
+                                               cfg.capacity, R)
+        st = {k: (v.copy() if isinstance(v, np.ndarray) else v)
+              for k, v in states[(b, h)].items()}
+        t0 = time.perf_counter()
+        st["k_res"][r0] = k_new[b, h]                         # append
+        st["v_res"][r0] = v_new[b, h]
+        st["r_len"] = rl = r0 + 1
+        ocache.decode_head(w.q[b, h], st, cfg.sm_scale, G, B)  # decode
+        if rl == R:                                           # flush
+            enc = ocache.encode_tokens(st["k_res"], st["v_res"], G, B)
+            g0 = ql // G
+            st["k_codes"][g0:g0 + R // G] = enc["k_codes"]
+            st["v_codes"][g0:g0 + R // G] = enc["v_codes"]
+        spent += time.perf_counter() - t0
+        done += 1
+    nt = blas_threads()
+    return {"value": done / spent, "unit": "query-heads/s", "cores": nt or 1, "kind": "oracle",
             "sample": f"{done} (sequence, head) steps (append + decode + flush each) cycling "
-                      f"over the {len(pairs)} pairs of the same workload, numpy with 1 BLAS "
-                      f"thread, {spent:.1f} s of timed work",
-            "host_cpus": len(os.sched_getaffinity(0))}
+                      f"over the {len(pairs)} pairs of the same workload, numpy with its BLAS "
+                      f"threads at their default ({nt}), {spent:.1f} s of timed work",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas_threads": nt}
 
 
 def stream_ceiling(nbytes, steps):
@@ -168,7 +178,7 @@ def stream_ceiling(nbytes, steps):
     from bit_kv_cache_decode_amd import kivi
 
     n16 = (int(nbytes) + 15) // 16
-    n_rot = max(2, -(-int(1.2e9) // (n16 * 16)))
+    n_rot = min(64, max(2, -(-int(ROTATE_BYTES) // (n16 * 16))))
     bufs = [torch.full((n16 * 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(n_rot)]
     by_wg = {}
     for wg in (256, 512, 1024, 2048):
@@ -196,6 +206,159 @@ def stream_ceiling(nbytes, steps):
             "frac_of_peak": n16 * 16 / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
             "us_by_workgroups": {str(k): round(v, 3) for k, v in by_wg.items()},
             "rotated_buffers": n_rot}
+
+
+# The other workloads' decodes, each timed beside the headline one: (workload
+# number, B) in the order they run.  The long-context draws serve B=2 and
+# B=4 (the same fp16 tokens, quantized at either width).
+EXTRA_WORKLOADS = ((1, None), (3, None), (4, None), (5, 2), (5, 4))
+ROTATE_BYTES = 1.2e9
+
+
+def time_graph(fn, n):
+    """HIP graph of fn(0) .. fn(n - 1), replayed once to warm up and once
+    between HIP events on the launch stream; microseconds per call."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / n
+
+
+def measure_workload(w, steps, no_stream):
+    """Decode of workload ``w`` at its own lengths (and, where every window
+    is full, the flush of those windows), timed over ``steps`` launches
+    rotated over cache copies that together exceed the 256 MB Infinity
+    Cache several times; the rate against 8 TB/s and against the stream-read
+    ceiling at the same byte count."""
+    import torch
+    from bit_kv_cache_decode_amd import kivi
+    from bit_kv_cache_decode_amd import workloads as wl
+
+    cfg = w.config
+    dims = w.dims()
+    Bt, H, D = dims["batch"], cfg.heads, cfg.head_dim
+    base = kivi.KiviCache(**dims)
+    kt = torch.from_numpy(w.k).cuda()
+    vt = torch.from_numpy(w.v).cuda()
+    q0 = torch.from_numpy(w.q_len).cuda()
+    r0 = torch.from_numpy(w.r_len).cuda()
+    kivi.prefill(base, kt, vt, q0 + r0, r0)
+    del kt, vt
+    q = torch.from_numpy(w.q).cuda()
+    torch.cuda.synchronize()
+    assert base.status_bits() == 0
+    cb = base.nbytes()
+    n = int(max(1, min(steps, max(2, -(-ROTATE_BYTES // cb)), COPY_BUDGET_BYTES // cb)))
+    copies = [base]
+    for _ in range(n - 1):
+        c = kivi.KiviCache(**dims)
+        for name, t in base.buffers().items():
+            getattr(c, name).copy_(t)
+        copies.append(c)
+    outs = [torch.empty((Bt, H, D), dtype=torch.float32, device="cuda") for _ in range(n)]
+    ws = kivi.new_workspace(base.dims)
+    us = time_graph(lambda i: kivi.decode_attn(copies[i % n], q, cfg.sm_scale, out=outs[i % n],
+                                               workspace=ws), steps)
+    ok = all(c.status_bits() == 0 for c in copies)
+    nbytes = int(wl.decode_bytes(w.q_len, w.r_len, H, D, w.bits, cfg.group))
+    gbps = nbytes / (us * 1e-6) / 1e9
+    res = {"workload": cfg.name + (f" at B={w.bits}" if w.bits != cfg.bits else ""),
+           "description": cfg.description, "batch": Bt, "heads": H, "bits": w.bits,
+           "group": cfg.group, "quantized_tokens": int(w.q_len.sum()),
+           "window_tokens": int(w.r_len.sum()), "splits": kivi.decode_splits(base.dims),
+           "decode_us": us, "algorithmic_bytes": nbytes, "GBps": gbps,
+           "frac": gbps / PEAK_HBM_GBPS, "query_heads_per_s": Bt * H / (us * 1e-6),
+           "launches": steps, "cache_copies": n, "status_clean": ok}
+    if bool((w.r_len == cfg.residual).all()):
+        # every window is full: the flush of all of them, each launch on a
+        # fresh copy (the lengths put back between the warm-up and the timed
+        # replay)
+        nf = min(steps, n)
+
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(nf):
+                kivi.flush_residual(copies[i])
+        times = []
+        for _ in range(2):
+            for c in copies[:nf]:
+                c.q_len.copy_(q0)
+                c.r_len.copy_(r0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(1e3 * e0.elapsed_time(e1) / nf)
+        fus = times[-1]
+        fb = Bt * H * wl.flush_bytes_per_head(cfg.residual, D, w.bits, cfg.group)
+        res["flush"] = {"us": fus, "windows": Bt * H, "algorithmic_bytes": int(fb),
+                        "GBps": fb / (fus * 1e-6) / 1e9,
+                        "frac": fb / (fus * 1e-6) / 1e9 / PEAK_HBM_GBPS, "launches": nf,
+                        "committed": bool(all(int(c.q_len[0]) == int(w.q_len[0]) + cfg.residual
+                                              for c in copies[:nf]))}
+    del copies, outs, ws, base
+    torch.cuda.empty_cache()
+    if not no_stream:
+        sr = stream_ceiling(nbytes, steps)
+        res["stream_read_us"] = sr["us"]
+        res["stream_read_frac"] = sr["frac_of_peak"]
+        res["decode_frac_of_stream_read"] = gbps / sr["GBps"]
+    return res
+
+
+def oracle_sample(w, n_heads, seed, flush=False):
+    """Wall time of the CPU oracle's decode (dequantization plus fp64
+    attention) on ``n_heads`` (sequence, head) pairs of workload ``w`` drawn
+    with ``seed`` (their cache states are encoded beforehand, untimed), and,
+    with ``flush``, of quantizing and packing their full windows; numpy with
+    its BLAS threads at their default."""
+    import numpy as np
+    from oracle import cache as ocache
+
+    cfg = w.config
+    rng = np.random.default_rng(seed)
+    nb = w.q.shape[0]
+    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, nb, n_heads),
+                                              rng.integers(0, cfg.heads, n_heads))]
+    states = [ocache.head_state(w.k[b, h], w.v[b, h], int(w.q_len[b]), int(w.r_len[b]),
+                                cfg.group, w.bits, cfg.capacity, cfg.residual) for b, h in pairs]
+    t0 = time.perf_counter()
+    for (b, h), st in zip(pairs, states):
+        ocache.decode_head(w.q[b, h], st, cfg.sm_scale, cfg.group, w.bits)
+    dec = time.perf_counter() - t0
+    out = {"heads": n_heads, "decode_s": dec, "query_heads_per_s": n_heads / dec}
+    if flush:
+        t0 = time.perf_counter()
+        for st in states:
+            ocache.encode_tokens(st["k_res"], st["v_res"], cfg.group, w.bits)
+        fl = time.perf_counter() - t0
+        out.update({"flush_s": fl, "flushes_per_s": n_heads / fl})
+    return out
+
+
+# (sequence, head) pairs the oracle decodes per workload for the CPU baseline
+ORACLE_SAMPLE_HEADS = {1: 1, 2: 64, 3: 64, 4: 64, 5: 2}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 0) for i in threadpool_info()
+                    if i.get("user_api") == "blas"), default=None)
+    except Exception:
+        return None
 
 
 def main():
@@ -311,6 +474,24 @@ def main():
         replay_ok = bool(torch.equal(outs[0], eager_out0))
         states_ok = bool(all(c.status_bits() == 0 for c in copies[:K]))
         step_state = {n: t.clone() for n, t in copies[0].buffers().items()}
+        # the same graph from windows two tokens shorter: every step appends
+        # and decodes without filling the window (the common step in serving,
+        # where one step in R flushes); the copies' bytes are the same
+        noflush_us = None
+        if bool((r0 >= 2).all()):
+            for c in copies:
+                c.q_len.copy_(q0)
+                c.r_len.copy_(r0 - 2)
+            torch.cuda.synchronize()
+            g0.record()
+            graph.replay()
+            g1.record()
+            torch.cuda.synchronize()
+            noflush_us = 1e3 * g0.elapsed_time(g1) / K
+            noflush_ok = bool(all(c.status_bits() == 0 for c in copies[:K])) and bool(
+                (copies[0].r_len == r0 - 1).all())
+            if not noflush_ok:
+                log("WARNING: the non-flushing steps left an unexpected state")
         reset()
         torch.cuda.synchronize()
 
@@ -457,6 +638,15 @@ def main():
             "GBps": sb / (step_event_us * 1e-6) / 1e9,
             "frac": sb / (step_event_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
             "traffic": measured_traffic(cfg.name, "step_bytes_per_launch") if plain else None}
+        if noflush_us is not None:
+            nb = (wl.step_bytes(w.q_len, r_start - 2, H, D, w.bits, cfg.group, cfg.residual)
+                  + Bt * H * args.sink * D * 2 * 2)
+            result["step_kernel_noflush"] = {
+                "what": "the same whole-step kernel on windows two tokens short of full: "
+                        "append and decode, no flush (the serving case)",
+                "us": noflush_us, "query_heads_per_s": qheads / (noflush_us * 1e-6),
+                "algorithmic_bytes": nb, "GBps": nb / (noflush_us * 1e-6) / 1e9,
+                "frac": nb / (noflush_us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
     if not args.no_stream:
         sr = stream_ceiling(dec_bytes, K)
         result["stream_read"] = sr
@@ -469,8 +659,37 @@ def main():
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         result["copy_reference_bytes"] = int(src.numel() * 4)
+    # ---- every other workload's decode (and the 13B layer's flush), on
+    # the GPU and, as a baseline, the oracle on the host
+    del graph, pgraphs, phases, copies, outs, base, ws
+    torch.cuda.empty_cache()
+    per_cpu = {}
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        per_cpu[cfg.name] = oracle_sample(w, ORACLE_SAMPLE_HEADS[cfg.number], 7000 + cfg.number,
+                                          flush=cfg.number == 3)
+    extra = {}
+    if not args.no_extra and args.rope is None and not args.sink:
+        import dataclasses
+        drawn = None
+        for number, bits in EXTRA_WORKLOADS:
+            if number == cfg.number and (bits or wl.CONFIGS[number].bits) == w.bits:
+                continue
+            if drawn is None or drawn.config.number != number:
+                drawn = None
+                drawn = wl.generate(number)
+            we = drawn if bits is None else dataclasses.replace(drawn, bits=bits)
+            log(f"workload {we.config.name} at B={we.bits}")
+            r = measure_workload(we, args.extra_steps, args.no_stream)
+            extra[r["workload"]] = r
+            if not args.no_cpu:
+                per_cpu[r["workload"]] = oracle_sample(we, ORACLE_SAMPLE_HEADS[number],
+                                                       7000 + number, flush=number == 3)
+        del drawn
+        result["workloads"] = extra
+    if not args.no_cpu:
+        cb = cpu_baseline(w, args.cpu_seconds)
+        cb["per_workload"] = per_cpu
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
 

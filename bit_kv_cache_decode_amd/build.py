@@ -17,6 +17,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every atomic in the library is issued by one lane; the atomic optimizer
+    # would turn it into a per-wave atomic whose result is read back at once,
+    # stalling the wave on a device-scope round trip where the result is
+    # only needed at the end of the kernel
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]

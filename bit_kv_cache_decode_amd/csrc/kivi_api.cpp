@@ -142,7 +142,45 @@ int kivi_prefill(const kivi_dims *dims, const kivi_cache *cache, const void *k, 
   if (!kivi::cache_ok(cache) || !kivi::a4(len) || src_len < 0) return KIVI_EINVAL;
   if (res && !kivi::a4(res)) return KIVI_EINVAL;
   if (src_len > 0 && (!kivi::a16(k) || !kivi::a16(v))) return KIVI_EINVAL;
-  return kivi::hip_rc(kivi::launch_prefill(*dims, *cache, k, v, src_len, len, res, stream));
+  return kivi::hip_rc(kivi::launch_prefill(*dims, *cache, k, v, src_len, len, res, stream, false));
+}
+
+int kivi_prefill_vq(const kivi_dims *dims, const kivi_cache *cache, const void *k, const void *v,
+                    int32_t src_len, const int32_t *len, const int32_t *res, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache) || !kivi::a4(len) || src_len < 0) return KIVI_EINVAL;
+  if (res && !kivi::a4(res)) return KIVI_EINVAL;
+  if (src_len > 0 && (!kivi::a16(k) || !kivi::a16(v))) return KIVI_EINVAL;
+  return kivi::hip_rc(kivi::launch_prefill(*dims, *cache, k, v, src_len, len, res, stream, true));
+}
+
+int kivi_append_kv_vq(const kivi_dims *dims, const kivi_cache *cache, const void *k_new,
+                      const void *v_new, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache) || !kivi::a16(k_new) || !kivi::a16(v_new)) return KIVI_EINVAL;
+  return kivi::hip_rc(kivi::launch_append_vq(*dims, *cache, k_new, v_new, stream));
+}
+
+int kivi_flush_residual_vq(const kivi_dims *dims, const kivi_cache *cache, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache)) return KIVI_EINVAL;
+  return kivi::hip_rc(kivi::launch_flush_keys(*dims, *cache, stream));
+}
+
+int kivi_decode_attn_vq(const kivi_dims *dims, const kivi_cache *cache, const void *q, float *out,
+                        float sm_scale, void *workspace, size_t workspace_bytes, void *stream) {
+  const int rc = kivi::check_dims(dims);
+  if (rc != KIVI_OK) return rc;
+  if (!kivi::cache_ok(cache) || !kivi::a16(q) || !kivi::a4(out) || !kivi::a16(workspace))
+    return KIVI_EINVAL;
+  if (!(sm_scale == sm_scale) || sm_scale == 1.0f / 0.0f || sm_scale == -1.0f / 0.0f)
+    return KIVI_EINVAL;
+  const kivi::DecodePlan p = kivi::decode_plan(*dims);
+  if (workspace_bytes < p.bytes) return KIVI_ENOSPC;
+  return kivi::hip_rc(kivi::launch_decode_vq(*dims, *cache, p, q, out, sm_scale, workspace, stream));
 }
 
 size_t kivi_decode_workspace_bytes(const kivi_dims *dims) {

@@ -59,7 +59,14 @@ int launch_append(const kivi_dims &d, const kivi_cache &c, const void *k_new,
 int launch_flush(const kivi_dims &d, const kivi_cache &c, void *stream);
 int launch_prefill(const kivi_dims &d, const kivi_cache &c, const void *k,
                    const void *v, int32_t src_len, const int32_t *len,
-                   const int32_t *res, void *stream);
+                   const int32_t *res, void *stream, bool value_queue);
+// Value queue: key flush only, and the append that moves the oldest value
+// out of the queue.
+int launch_flush_keys(const kivi_dims &d, const kivi_cache &c, void *stream);
+int launch_append_vq(const kivi_dims &d, const kivi_cache &c, const void *k_new,
+                     const void *v_new, void *stream);
+int launch_decode_vq(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, const void *q,
+                     float *out, float sm_scale, void *workspace, void *stream);
 int launch_decode(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,
                   const void *q, float *out, float sm_scale, void *workspace,
                   void *stream);

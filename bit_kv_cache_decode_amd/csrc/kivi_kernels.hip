@@ -242,6 +242,11 @@ struct EncodeArgs {
   const int32_t *len, *res;      // prefill: prompt lengths, window sizes (res may be null)
   uint32_t *status, *tickets;
   int heads, R, cap, prefill;
+  // value queue (discosf KIVI tutorial, section 3.2): values leave an fp16
+  // queue of the newest R one token at a time, quantized as they leave; the
+  // queue is a ring in the value window (token t in slot t mod R).  Prefill
+  // then quantizes only the first max(0, len - R) values.
+  int vq;
 };
 
 // Window size and validity of one prompt, identical in every prefill kernel.
@@ -327,7 +332,16 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
       mn = fminf(mn, x);
       mx = fmaxf(mx, x);
     }
-    const GroupParams g = group_params(mn, mx, kTop);
+    GroupParams g = group_params(mn, mx, kTop);
+    if (a.vq && tile * G + t >= n - a.R) {
+      // value queue: this token's value is still in the fp16 queue; its
+      // group stays zero (step 0, zero-point 0, codes 0)
+      g.mn = 0.0f;
+      g.s = 0.0f;
+      g.rs = 0.0f;
+      g.zero16 = (half_t)0.0f;
+      g.scale16 = (half_t)0.0f;
+    }
     a.v_zero[ktile * kD + e] = g.zero16;
     a.v_scale[ktile * kD + e] = g.scale16;
     vmn[e] = g.mn;
@@ -381,7 +395,22 @@ struct FlushSmem {
   float4 kp[NB][kD], vp[NB][kD];                  // {minimum, step, 1 / step, -}
 };
 
-template <int BITS, int G, int TB, int NTHREADS>
+// A 16-byte piece of a window row, read once by the flush: non-temporal
+// unless KIVI_FLUSH_NT is 0.
+#ifndef KIVI_FLUSH_NT
+#define KIVI_FLUSH_NT 1
+#endif
+__device__ __forceinline__ uint4 load_window_row(const uint4 *p) {
+#if KIVI_FLUSH_NT
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
+
+template <int BITS, int G, int TB, int NTHREADS, bool VALUES = true>
 __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int ql, int tid,
                                              FlushSmem<G, TB> &fs, int rnew, const uint4 *knew,
                                              const uint4 *vnew, int blk0, int blk1) {
@@ -405,7 +434,7 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
       for (int i = 0; i < PE; ++i) {
         const int e = tid + i * NTHREADS, op = e / TE, f = e % TE;
         const int t = blk + min(tl, nt - 1) * G + f / (kD / 8);  // clamped: unused past nt
-        r[tl][i] = src[op][(size_t)t * (kD / 8) + f % (kD / 8)];
+        if (VALUES || op == 0) r[tl][i] = load_window_row(&src[op][(size_t)t * (kD / 8) + f % (kD / 8)]);
       }
     }
 #pragma unroll
@@ -419,10 +448,10 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
         const int t = f / (kD / 8), c = f % (kD / 8);
         uint4 val = r[tl][i];
         if (knew != nullptr && blk + tl * G + t == rnew) val = fresh_row[op][c];
-        *reinterpret_cast<uint4 *>(&fs.x[bf][op][t][c * 8]) = val;
+        if (VALUES || op == 0) *reinterpret_cast<uint4 *>(&fs.x[bf][op][t][c * 8]) = val;
       }
       __syncthreads();
-      for (int gi = tid; gi < kD / 2 + kD; gi += NTHREADS) {
+      for (int gi = tid; gi < kD / 2 + (VALUES ? kD : 0); gi += NTHREADS) {
         if (gi < kD / 2) {
           // key groups: channels 2 * gi and 2 * gi + 1 over the tile's G tokens
           const int c = 2 * gi;
@@ -463,7 +492,7 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
         }
       }
       __syncthreads();
-      for (int wi = tid; wi < 2 * W * G; wi += NTHREADS) {
+      for (int wi = tid; wi < (VALUES ? 2 : 1) * W * G; wi += NTHREADS) {
         // key words first, then value words; word (w, t) holds channels
         // w * CPW .. w * CPW + CPW - 1 of token t
         const int op = wi / (W * G), w = (wi / G) % W, t = wi % G;
@@ -541,7 +570,7 @@ constexpr int kFlushThreads = 256;
 #define KIVI_FLUSH_P 2
 #endif
 
-template <int BITS, int G, int P>
+template <int BITS, int G, int P, bool VALUES = true>
 __global__ __launch_bounds__(kFlushThreads * P) void flush_kernel(EncodeArgs a) {
   const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int part = tid / kFlushThreads, tile = blockIdx.x * P + part;
@@ -565,8 +594,9 @@ __global__ __launch_bounds__(kFlushThreads * P) void flush_kernel(EncodeArgs a) 
   // P tiles side by side, kFlushThreads threads and one LDS block each; they
   // pass the same barriers in step (P divides the window's tile count)
   __shared__ FlushSmem<G, G> fs[P];
-  flush_window<BITS, G, G, kFlushThreads>(a, (size_t)b * a.heads + h, ql, tid % kFlushThreads,
-                                          fs[part], -1, nullptr, nullptr, tile * G, tile * G + G);
+  flush_window<BITS, G, G, kFlushThreads, VALUES>(a, (size_t)b * a.heads + h, ql,
+                                                  tid % kFlushThreads, fs[part], -1, nullptr,
+                                                  nullptr, tile * G, tile * G + G);
   if (tid == 0 && ticket == n_tickets - 1) {
     a.q_len[b] = ql + a.R;
     a.r_len[b] = 0;
@@ -585,7 +615,18 @@ __global__ __launch_bounds__(kThreads) void prefill_window_kernel(EncodeArgs a, 
   const size_t dst = bh * (size_t)a.R * kD;
   for (int i = threadIdx.x; i < r * (kD / 8); i += kThreads) {
     reinterpret_cast<uint4 *>(a.k_res + dst)[i] = reinterpret_cast<const uint4 *>(a.src_k + src)[i];
-    reinterpret_cast<uint4 *>(a.v_res + dst)[i] = reinterpret_cast<const uint4 *>(a.src_v + src)[i];
+    if (!a.vq)
+      reinterpret_cast<uint4 *>(a.v_res + dst)[i] = reinterpret_cast<const uint4 *>(a.src_v + src)[i];
+  }
+  if (a.vq) {
+    // the newest min(n, R) values, token t in ring slot t mod R
+    const int v0 = max(0, n - a.R);
+    const size_t vsrc = bh * a.src_tokens * kD;
+    for (int i = threadIdx.x; i < (n - v0) * (kD / 8); i += kThreads) {
+      const int t = v0 + i / (kD / 8), c = i % (kD / 8);
+      reinterpret_cast<uint4 *>(a.v_res + dst + (size_t)(t % a.R) * kD)[c] =
+          reinterpret_cast<const uint4 *>(a.src_v + vsrc + (size_t)t * kD)[c];
+    }
   }
 }
 
@@ -633,6 +674,70 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
   }
   __syncthreads();
   if (tid == 0) r_len[b] = r + 1;
+}
+
+// ------------------------------------------------------ value-queue append
+// The value queue (discosf KIVI tutorial, section 3.2): the value window is
+// a ring of R slots holding the newest min(T, R) values (token t in slot
+// t mod R, T = q_len + r_len tokens in all).  Appending token T: its key goes
+// to key-window slot r_len (as in append_kernel); once the ring is full
+// (T >= R) the value in slot T mod R -- token T - R, the oldest -- is
+// quantized on its own (D / G groups of G channels) into value position
+// T - R of the tiles, then the slot takes the new value.  One workgroup of
+// 16 waves per sequence, a wave per head at a time; lane i holds channels
+// 2i and 2i + 1.  Every thread reads the lengths before the barrier that
+// precedes thread 0's update of r_len.
+constexpr int kAppendVqThreads = 1024;
+
+template <int BITS, int G>
+__global__ __launch_bounds__(kAppendVqThreads) void append_vq_kernel(EncodeArgs a,
+                                                                     const half_t *k_new,
+                                                                     const half_t *v_new) {
+  constexpr int W = kD * BITS / 32, CPW = 32 / BITS, LPW = CPW / 2, LPG = G / 2;
+  constexpr float kTop = (float)((1 << BITS) - 1);
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int ql = a.q_len[b], r = a.r_len[b];
+  __syncthreads();
+  if (r < 0 || r >= a.R || ql < 0 || ql % G || ql > a.cap) {
+    if (tid == 0)
+      atomicOr(a.status, (r >= a.R && ql >= 0 && ql % G == 0 && ql <= a.cap)
+                             ? KIVI_ST_RESIDUAL_FULL : KIVI_ST_BAD_LENGTH);
+    return;
+  }
+  const int T = ql + r, slot = T % a.R, te = T - a.R;
+  const size_t tiles = (size_t)(a.cap / G);
+  for (int h = wv; h < a.heads; h += kAppendVqThreads / 64) {
+    const size_t bh = (size_t)b * a.heads + h;
+    uint32_t *vrow = reinterpret_cast<uint32_t *>(a.v_res + (bh * a.R + slot) * kD);
+    if (te >= 0) {
+      const half2_t x2 = __builtin_bit_cast(half2_t, vrow[lane]);
+      const float x0 = (float)x2.x, x1 = (float)x2.y;
+      float mn = fminf(x0, x1), mx = fmaxf(x0, x1);
+#pragma unroll
+      for (int o = 1; o < LPG; o <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o));
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+      }
+      const GroupParams g = group_params(mn, mx, kTop);
+      const uint32_t c0 = (uint32_t)fminf(code_exact(x0, g.mn, g.s), kTop);
+      const uint32_t c1 = (uint32_t)fminf(code_exact(x1, g.mn, g.s), kTop);
+      uint32_t word = (c0 << ((2 * lane) % CPW * BITS)) | (c1 << ((2 * lane + 1) % CPW * BITS));
+#pragma unroll
+      for (int o = 1; o < LPW; o <<= 1) word |= (uint32_t)__shfl_xor((int)word, o);
+      const size_t tile = bh * tiles + (size_t)(te / G);
+      if (lane % LPW == 0) a.v_codes[(tile * W + lane / LPW) * G + te % G] = word;
+      if (lane % LPG == 0) {
+        a.v_zero[tile * kD + (lane / LPG) * G + te % G] = g.zero16;
+        a.v_scale[tile * kD + (lane / LPG) * G + te % G] = g.scale16;
+      }
+    }
+    // the slot's old value has been read (same lanes, same addresses)
+    vrow[lane] = reinterpret_cast<const uint32_t *>(v_new + bh * kD)[lane];
+    reinterpret_cast<uint32_t *>(a.k_res + (bh * a.R + r) * kD)[lane] =
+        reinterpret_cast<const uint32_t *>(k_new + bh * kD)[lane];
+  }
+  __syncthreads();
+  if (tid == 0) a.r_len[b] = r + 1;
 }
 
 // ----------------------------------------------------------------- decode
@@ -691,8 +796,14 @@ struct DecodeArgs {
   int n_sink, sink_per_wave;
 };
 
+// Sub-chunks in flight per wave in the plain decode on grids of at most one
+// workgroup per compute unit.
+#ifndef KIVI_WIDE_DEPTH
+#define KIVI_WIDE_DEPTH 2
+#endif
 constexpr int kMaxSplits = 128;
 constexpr int kPartHead = 4;   // m, l, 2 pad floats before the 128 values
+
 
 
 template <int BITS, int G>
@@ -882,17 +993,28 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
                                            0x00020000);
 }
 
+// Cache policy of the decode's loads (the buffer instructions' auxiliary
+// bits: 1 sc0, 2 nt).  Every byte the decode reads is read once per call, so
+// the loads are marked non-temporal; measured against plain loads (HIP-graph
+// timings of 30 launches, alternating, one box): 7B layer 26.1 -> 24.3 us,
+// 13B layer 33.5 -> 30.7, ragged batch 64 203 -> 192, 131072 tokens at B=2
+// 78.9 -> 76.9, at B=4 unchanged; nt alone measured within noise of sc0 nt.
+#ifndef KIVI_DECODE_LOAD_AUX
+#define KIVI_DECODE_LOAD_AUX 3
+#endif
+constexpr int kLoadAux = KIVI_DECODE_LOAD_AUX;
+
 __device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, kLoadAux);
 }
 
 __device__ __forceinline__ uint2 bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
-  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kLoadAux);
   return make_uint2(v.x, v.y);
 }
 
 __device__ __forceinline__ uint4 bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kLoadAux);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -1318,6 +1440,86 @@ __device__ __forceinline__ void window_step(const WinStep<BITS, G> &x, bool vali
   }
 }
 
+// --------------------------------------------- value queue: token by token
+// With a value queue the context splits into tokens [0, vq) with quantized
+// keys and values, [vq, q_len) with quantized keys and fp16 values (in the
+// ring) and [q_len, T) with fp16 keys (the key window) and values.  The
+// quantized stream covers whole key groups below vq; the rest, [qlq, T)
+// with qlq = G * floor(vq / G), at most R + G - 1 tokens, is taken token by
+// token: lane (slot, w) loads or dequantizes channels w * CPW .. of its
+// token's key and value, each from wherever that token has it.
+
+// CPW consecutive fp16 values at p (aligned to 2 * CPW bytes) as floats
+template <int CPW>
+__device__ __forceinline__ void load_halves(const half_t *p, float (&x)[CPW]) {
+  if constexpr (CPW == 4) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const half2_t h = __builtin_bit_cast(half2_t, i < 2 ? u.x : u.y);
+      x[i] = (i & 1) ? (float)h.y : (float)h.x;
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < CPW / 8; ++v) {
+      const uint4 u = reinterpret_cast<const uint4 *>(p)[v];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const half2_t h = __builtin_bit_cast(half2_t, u4_get(u, e));
+        x[8 * v + 2 * e] = (float)h.x;
+        x[8 * v + 2 * e + 1] = (float)h.y;
+      }
+    }
+  }
+}
+
+template <int BITS, int G>
+__device__ __forceinline__ void vq_token(const DecodeArgs &a, size_t bh, int t, bool valid, int ql,
+                                         int vqn, int w, const float *qv,
+                                         LaneState<DecCfg<BITS, G>::CPW> &st) {
+  using C = DecCfg<BITS, G>;
+  constexpr uint32_t kMask = (1u << BITS) - 1u;
+  const size_t tps = (size_t)(a.cap / G);
+  const size_t tile = bh * tps + (size_t)(t / G);
+  const int pos = t % G;
+  float k[C::CPW], v[C::CPW];
+  if (t < ql) {  // quantized key: z + c * s per channel
+    const uint32_t word = a.k_codes[(tile * C::W + w) * G + pos];
+    float z[C::CPW], sc[C::CPW];
+    load_halves<C::CPW>(a.k_zero + tile * kD + w * C::CPW, z);
+    load_halves<C::CPW>(a.k_scale + tile * kD + w * C::CPW, sc);
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) k[i] = fmaf((float)((word >> (i * BITS)) & kMask), sc[i], z[i]);
+  } else {
+    load_halves<C::CPW>(a.k_res + (bh * a.R + (t - ql)) * kD + w * C::CPW, k);
+  }
+  if (t < vqn) {  // quantized value: one group per token
+    const uint32_t word = a.v_codes[(tile * C::W + w) * G + pos];
+    const int j = (w * C::CPW) / G;
+    const float z = (float)a.v_zero[tile * kD + j * G + pos];
+    const float sc = (float)a.v_scale[tile * kD + j * G + pos];
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) v[i] = fmaf((float)((word >> (i * BITS)) & kMask), sc, z);
+  } else {
+    load_halves<C::CPW>(a.v_res + (bh * a.R + (t % a.R)) * kD + w * C::CPW, v);
+  }
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int d = 0; d < C::CPW; d += 2) {
+    a0 = fmaf(qv[d], k[d], a0);
+    a1 = fmaf(qv[d + 1], k[d + 1], a1);
+  }
+  float s = lane_group_sum<C::W>(a0 + a1);
+  s = valid ? s : -INFINITY;
+  update_max<C::CPW, 1>(st, &s);
+  const float p = s > -INFINITY ? exp2_fast(s - st.m) : 0.0f;
+  st.l += p;
+  // value sums hold channel values times 2^(e - 24), as the window's do
+#pragma unroll
+  for (int i = 0; i < C::CPW; ++i)
+    st.acc[i] = fmaf(p * __builtin_ldexpf(1.0f, code_offset<BITS>(i) - 24), v[i], st.acc[i]);
+}
+
 // ------------------------------------------ whole step: flush from registers
 // When the step's append fills the window and every wave holds all of its
 // window tokens in its prefetched registers (at most 16 per wave, R <= 128),
@@ -1496,14 +1698,16 @@ __device__ __forceinline__ void flush_regs_keys(const EncodeArgs &ea, const RegF
 // round (per-workgroup timestamps: started at 22 us); with three per
 // compute unit all 640 start at once (37.7 -> 34.3 us).
 // ROPE: keys are stored before the rotary embedding (RopeLane above).
-template <int BITS, int G, bool FUSED, int DEPTH, bool ROPE = false>
-__global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDecodeWavesPerSimd : kDecodeWavesPerSimd) void decode_kernel(
+// VQ: the cache keeps a value queue (vq_token above).
+template <int BITS, int G, bool FUSED, int DEPTH, bool ROPE = false, bool VQ = false>
+__global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) * kDecodeWavesPerSimd : kDecodeWavesPerSimd) void decode_kernel(
     DecodeArgs a, EncodeArgs ea) {
   constexpr int kDecodeDepth = DEPTH;
   using C = DecCfg<BITS, G>;
   using WC = WinCfg<BITS, G>;
   static_assert(!FUSED || WC::WIDE, "the whole-step kernel holds window rows as 16-byte vectors");
   static_assert(!(FUSED && ROPE), "keys stored pre-rotation: the step is three kernels");
+  static_assert(!(VQ && (FUSED || ROPE)), "the value queue has the plain decode only");
   __shared__ DecSmem<BITS, G, ROPE> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -1541,15 +1745,12 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
     knew = reinterpret_cast<const uint4 *>(a.k_new + bh * kD);
     vnew = reinterpret_cast<const uint4 *>(a.v_new + bh * kD);
     if (rl >= 0 && rl < a.R) {
+      // the row itself is written from the registers that hold it for the
+      // attention (store_new below), not by a load and a store here, whose
+      // wait would stall the first wave at the start
       rnew = rl;
       rl += 1;
       commit = true;
-      if (tid < 2 * (kD / 8)) {  // 16 bytes of the key or value row per thread
-        const int c = tid % (kD / 8);
-        const uint4 x = tid < kD / 8 ? knew[c] : vnew[c];
-        half_t *dst = (tid < kD / 8 ? ea.k_res : ea.v_res) + (bh * a.R + rnew) * kD;
-        reinterpret_cast<uint4 *>(dst)[c] = x;
-      }
     } else if (h == 0 && tid == 0) {
       atomicOr(a.status, rl < 0 ? KIVI_ST_BAD_LENGTH : KIVI_ST_RESIDUAL_FULL);
     }
@@ -1570,6 +1771,15 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
     rl = 0;
   }
 
+  // value queue: values are quantized for tokens [0, vqn); the quantized
+  // stream covers the whole key groups below that, [0, qlq)
+  [[maybe_unused]] int vqn = 0;
+  int qlq = ql;
+  if constexpr (VQ) {
+    vqn = max(0, ql + rl - a.R);
+    qlq = (vqn / G) * G;
+  }
+
   // ---- this wave's share: quantized sub-chunks gw, gw + nw, ... and
   // window tokens [gw * win_per_wave, (gw + 1) * win_per_wave)
   const int w = lane % C::W, slot = lane / C::W;
@@ -1587,17 +1797,17 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
   qs.code_voff = (uint32_t)(w * G + 4 * slot) * 4;
   qs.vmeta_voff = (uint32_t)(jg * G + 4 * slot) * 2;
   qs.kmeta_voff = (uint32_t)lane * 4;
-  qs.ql = ql;
-  qs.last_tile = ql / G - 1;
+  qs.ql = qlq;
+  qs.last_tile = qlq / G - 1;
   qs.gw = split * kDecodeWaves + wv;
   qs.nw = kDecodeWaves * S;
-  qs.n = qs.gw * C::SUB < ql ? (ql - qs.gw * C::SUB + qs.nw * C::SUB - 1) / (qs.nw * C::SUB) : 0;
+  qs.n = qs.gw * C::SUB < qlq ? (qlq - qs.gw * C::SUB + qs.nw * C::SUB - 1) / (qs.nw * C::SUB) : 0;
 
   WinStream<BITS, G> ws;
   ws.kr = a.k_res + bh * a.R * kD;
   ws.vr = a.v_res + bh * a.R * kD;
   ws.begin = qs.gw * a.win_per_wave;
-  ws.end = min(rl, ws.begin + a.win_per_wave);
+  ws.end = VQ ? ws.begin : min(rl, ws.begin + a.win_per_wave);  // VQ: no window pass
   ws.bytes = (uint32_t)max(0, ws.end) * (kD * 2);
   ws.lane_voff = (uint32_t)(slot * kD + w * C::CPW) * 2;
   const int wsteps = ws.end > ws.begin ? (ws.end - ws.begin + WC::STEP - 1) / WC::STEP : 0;
@@ -1711,22 +1921,41 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
     }
   };
 
-  if constexpr (FUSED) {
-    if (early) {
-      // the window's attention and the flush's value words and key
-      // partials, which need no other wave; the key groups (across waves)
-      // are finished after the workgroup's combine barrier
-      window();
-      if (wsteps > 0)
-        flush_regs_values<BITS, G>(ea, fused_flush_smem<BITS, G>().reg, wpf, wsteps, tile0,
-                                   ws.begin, wv, w, slot);
+  // FUSED: the appended row into window slot rnew of the cache, from the
+  // registers of wave 0's first token slot (lane w holds channels w * CPW ..)
+  [[maybe_unused]] auto store_new = [&]() {
+    if constexpr (FUSED) {
+      if (rnew >= 0 && wv == 0 && slot == 0) {
+        uint4 *kd = reinterpret_cast<uint4 *>(ea.k_res + (bh * a.R + rnew) * kD + w * C::CPW);
+        uint4 *vd = reinterpret_cast<uint4 *>(ea.v_res + (bh * a.R + rnew) * kD + w * C::CPW);
+#pragma unroll
+        for (int v = 0; v < WC::NV; ++v) {
+          kd[v] = xnew.k[v];
+          vd[v] = xnew.v[v];
+        }
+      }
     }
-  }
+  };
 
   // Whole rounds of kDecodeDepth sub-chunks (no branch inside a round, so
   // the wait before each sub-chunk only covers its own loads), then the
   // remaining n mod kDecodeDepth, whose loads are already in flight.
   int c0 = 0;
+  if constexpr (FUSED) {
+    if (early) {
+      // The window's attention and the flush's value words and key
+      // partials, which need no other wave (the key groups across waves are
+      // finished after the workgroup's combine barrier).  (Running them after
+      // the first round of sub-chunks instead, with that round's refills in
+      // flight, measured the same: 34.1 against 33.3 us a step on the 7B
+      // layer.)
+      window();
+      if (wsteps > 0)
+        flush_regs_values<BITS, G>(ea, fused_flush_smem<BITS, G>().reg, wpf, wsteps, tile0,
+                                   ws.begin, wv, w, slot);
+      store_new();
+    }
+  }
   for (; c0 + kDecodeDepth <= qs.n; c0 += kDecodeDepth) {
 #pragma unroll
     for (int k = 0; k < kDecodeDepth; ++k) {
@@ -1735,7 +1964,7 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
 #elif KIVI_DECODE_PRIORITY
       set_progress_priority(c0 + k, qs.n);
 #endif
-      process_sub<BITS, G, ROPE>(ring[k], qs.t0(c0 + k), ql, lane, qs0, qs1, qf0, qf1, stg.qp,
+      process_sub<BITS, G, ROPE>(ring[k], qs.t0(c0 + k), qs.ql, lane, qs0, qs1, qf0, qf1, stg.qp,
                                  stg.cz, st, zz, &rope);
       qs.issue(ring[k], c0 + k + kDecodeDepth);
     }
@@ -1752,13 +1981,30 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
 #elif KIVI_DECODE_PRIORITY
       set_progress_priority(c0 + k, qs.n);
 #endif
-      process_sub<BITS, G, ROPE>(ring[k], qs.t0(c0 + k), ql, lane, qs0, qs1, qf0, qf1, stg.qp,
+      process_sub<BITS, G, ROPE>(ring[k], qs.t0(c0 + k), qs.ql, lane, qs0, qs1, qf0, qf1, stg.qp,
                                  stg.cz, st, zz, &rope);
     }
 #if KIVI_DECODE_PRIORITY
   __builtin_amdgcn_s_setprio(0);
 #endif
-  if (!early) window();
+  if constexpr (VQ) {
+    // tokens [qlq, T) one at a time, this wave's share of them
+    const int ub = qs.gw * a.win_per_wave, ue = min(ql + rl - qlq, ub + a.win_per_wave);
+    if (ue > ub) {
+      __builtin_amdgcn_wave_barrier();
+      float qv[C::CPW];
+#pragma unroll
+      for (int i = 0; i < C::CPW; ++i) qv[i] = stg.qs[w * C::CPW + i];
+      for (int u0 = ub; u0 < ue; u0 += WC::STEP) {
+        const int u = u0 + slot;
+        const bool valid = u < ue;
+        vq_token<BITS, G>(a, bh, qlq + (valid ? u : ub), valid, ql, vqn, w, qv, st);
+      }
+    }
+  } else if (!early) {
+    window();
+    store_new();
+  }
   // fp16 sink tokens (the sequence's first tokens, kept unquantized ahead of
   // the quantized ones, at positions 0 .. n_sink - 1): this wave's share
   // [gw * sink_per_wave, ...), one load round trip per step (set up here, so
@@ -1795,32 +2041,44 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
                                          sm.fin.l[wv], st.m, st.l, st.acc, st.bias);
   __syncthreads();
 
-  // ---- combine the waves into the workgroup's state (channel tid)
+  // ---- combine the waves into the workgroup's state (channel tid).
+  // Every published value is read first, then reduced: one LDS round trip
+  // instead of one per wave.  (Every wave published finite sums, zeros
+  // without tokens, so all can be read before any test.)
+  constexpr int NR = publish_rows<C::W>();
+  float fm[kDecodeWaves], fl[kDecodeWaves];
+  float ra[kDecodeWaves][NR], rb[kDecodeWaves][NR];
+#pragma unroll
+  for (int x = 0; x < kDecodeWaves; ++x) {
+    fm[x] = sm.fin.m[x];
+    fl[x] = sm.fin.l[x];
+  }
+  const int ch = tid < kD ? tid : 0;
+#pragma unroll
+  for (int x = 0; x < kDecodeWaves; ++x)
+#pragma unroll
+    for (int y = 0; y < NR; ++y) {
+      ra[x][y] = sm.fin.acc[x][y][ch];
+      rb[x][y] = sm.fin.bias[x][y][ch / C::CPW];
+    }
   float M = -INFINITY;
 #pragma unroll
   for (int x = 0; x < kDecodeWaves; ++x)
-    if (sm.fin.l[x] > 0.0f) M = fmaxf(M, sm.fin.m[x]);
+    if (fl[x] > 0.0f) M = fmaxf(M, fm[x]);
   float L = 0.0f, acc_out = 0.0f;
   if (M != -INFINITY) {
-    float ex[kDecodeWaves];
+    const float cf = code_factor<BITS>(ch % C::CPW);
 #pragma unroll
     for (int x = 0; x < kDecodeWaves; ++x) {
-      ex[x] = sm.fin.l[x] > 0.0f ? exp2_fast(sm.fin.m[x] - M) : 0.0f;
-      L += ex[x] * sm.fin.l[x];
-    }
-    // every wave published finite sums (zeros without tokens), so all are
-    // read at once instead of one wave's behind another's test
-    if (tid < kD) {
+      const float ex = fl[x] > 0.0f ? exp2_fast(fm[x] - M) : 0.0f;
+      L += ex * fl[x];
+      float sa = 0.0f, sb = 0.0f;
 #pragma unroll
-      for (int x = 0; x < kDecodeWaves; ++x) {
-        float sa = 0.0f, sb = 0.0f;
-#pragma unroll
-        for (int y = 0; y < publish_rows<C::W>(); ++y) {
-          sa += sm.fin.acc[x][y][tid];
-          sb += sm.fin.bias[x][y][tid / C::CPW];
-        }
-        acc_out += ex[x] * fmaf(sa, code_factor<BITS>(tid % C::CPW), sb);
+      for (int y = 0; y < NR; ++y) {
+        sa += ra[x][y];
+        sb += rb[x][y];
       }
+      acc_out += ex * fmaf(sa, cf, sb);
     }
   }
   if (S == 1) {  // the workgroup saw every token: finish here
@@ -1903,34 +2161,31 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE ? 2 : 3) * kDeco
 }
 
 // ------------------------------------------------ measurement: stream read
-// Reads a buffer once with 16-byte loads and folds it into one word per wave:
-// the HBM read rate this chip sustains for a given size and grid, the
-// ceiling the decode's rate is compared with.  Workgroup i streams its own
-// contiguous slice (as a decode workgroup streams its (sequence, head)),
-// kStreamUnroll loads in flight per lane, the lanes of a wave on consecutive
-// 16-byte pieces.
+// Reads a buffer once and folds it into one word per wave: the HBM read rate
+// this chip sustains for a given size and grid, the ceiling the decode's
+// rate is compared with.  Workgroup i streams its own contiguous slice (as a
+// decode workgroup streams its (sequence, head)) through a buffer
+// descriptor bounded by the slice, with the decode's load policy (kLoadAux),
+// kStreamUnroll 16-byte loads in flight per lane, the lanes of a wave on
+// consecutive 16-byte pieces.  Measured on 114.5 MB: plain global loads
+// 20.7 us at best, these 18.3 us.
 constexpr int kStreamThreads = 512;
 constexpr int kStreamUnroll = 8;
 
-__global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4 *src, size_t n16,
+__global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const char *src, size_t bytes,
                                                                      size_t per_wg,
                                                                      uint32_t *sink) {
   const size_t begin = (size_t)blockIdx.x * per_wg;
-  const size_t end = begin < n16 ? min(n16, begin + per_wg) : begin;
+  const uint32_t len = (uint32_t)(begin < bytes ? min(bytes - begin, per_wg) : 0);
+  const rsrc_t r = make_rsrc(src + (begin < bytes ? begin : 0), len);
+  constexpr uint32_t kStep = kStreamThreads * 16;
   uint32_t x = 0;
-  size_t i = begin + threadIdx.x;
-  // every index of a round is below end: the largest is i + (U - 1) * T
-  for (; i + (size_t)(kStreamUnroll - 1) * kStreamThreads < end;
-       i += (size_t)kStreamUnroll * kStreamThreads) {
+  for (uint32_t o = threadIdx.x * 16; o < len; o += kStep * kStreamUnroll) {
     uint4 v[kStreamUnroll];
 #pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) v[u] = src[i + (size_t)u * kStreamThreads];
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = bload4(r, o + (uint32_t)u * kStep, 0);
 #pragma unroll
     for (int u = 0; u < kStreamUnroll; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
-  for (; i < end; i += kStreamThreads) {
-    const uint4 v = src[i];
-    x ^= v.x ^ v.y ^ v.z ^ v.w;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off);
@@ -1980,8 +2235,16 @@ int launch_encode(int bits, int G, const EncodeArgs &ea, dim3 grid, hipStream_t 
 
 template <int BITS, int G>
 int launch_decode_t(const DecodeArgs &da, const EncodeArgs &ea, bool fused, int depth, dim3 grid,
-                    hipStream_t st, bool rope) {
+                    hipStream_t st, bool rope, bool vq) {
   const dim3 blk(kDecodeThreads);
+  if (vq) {  // value queue: the plain decode with the token-by-token tail
+    if (fused || rope) return (int)hipErrorInvalidValue;
+    if (depth == 1)
+      hipLaunchKernelGGL((decode_kernel<BITS, G, false, 1, false, true>), grid, blk, 0, st, da, ea);
+    else
+      hipLaunchKernelGGL((decode_kernel<BITS, G, false, 2, false, true>), grid, blk, 0, st, da, ea);
+    return (int)hipGetLastError();
+  }
   if (rope) {
     // keys stored pre-rotation (never the whole step).  At B=2 always two
     // sub-chunks in flight: only that register budget (one workgroup per
@@ -2004,7 +2267,7 @@ int launch_decode_t(const DecodeArgs &da, const EncodeArgs &ea, bool fused, int 
   } else if (depth == 1)
     hipLaunchKernelGGL((decode_kernel<BITS, G, false, 1>), grid, blk, 0, st, da, ea);
   else
-    hipLaunchKernelGGL((decode_kernel<BITS, G, false, 2>), grid, blk, 0, st, da, ea);
+    hipLaunchKernelGGL((decode_kernel<BITS, G, false, KIVI_WIDE_DEPTH>), grid, blk, 0, st, da, ea);
   return (int)hipGetLastError();
 }
 
@@ -2040,27 +2303,36 @@ int launch_append(const kivi_dims &d, const kivi_cache &c, const void *k_new, co
   return (int)hipGetLastError();
 }
 
-// P tiles per workgroup: up to 128 window tokens (the LDS of P tile blocks)
-template <int BITS, int G>
-int launch_flush_t(const EncodeArgs &ea, dim3 grid, int P, hipStream_t st) {
+// P tiles per workgroup: up to 128 window tokens (the LDS of P tile blocks);
+// VALUES false: keys only (the value queue's flush)
+template <int BITS, int G, bool VALUES>
+int launch_flush_p(const EncodeArgs &ea, dim3 grid, int P, hipStream_t st) {
   if constexpr (4 * G <= 128) {
     if (P == 4) {
-      hipLaunchKernelGGL((flush_kernel<BITS, G, 4>), grid, dim3(4 * kFlushThreads), 0, st, ea);
+      hipLaunchKernelGGL((flush_kernel<BITS, G, 4, VALUES>), grid, dim3(4 * kFlushThreads), 0, st,
+                         ea);
       return (int)hipGetLastError();
     }
   }
   if constexpr (2 * G <= 128) {
     if (P == 2) {
-      hipLaunchKernelGGL((flush_kernel<BITS, G, 2>), grid, dim3(2 * kFlushThreads), 0, st, ea);
+      hipLaunchKernelGGL((flush_kernel<BITS, G, 2, VALUES>), grid, dim3(2 * kFlushThreads), 0, st,
+                         ea);
       return (int)hipGetLastError();
     }
   }
   if (P != 1) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL((flush_kernel<BITS, G, 1>), grid, dim3(kFlushThreads), 0, st, ea);
+  hipLaunchKernelGGL((flush_kernel<BITS, G, 1, VALUES>), grid, dim3(kFlushThreads), 0, st, ea);
   return (int)hipGetLastError();
 }
 
-int launch_flush(const kivi_dims &d, const kivi_cache &c, void *stream) {
+template <int BITS, int G>
+int launch_flush_t(const EncodeArgs &ea, dim3 grid, int P, hipStream_t st, bool keys_only) {
+  return keys_only ? launch_flush_p<BITS, G, false>(ea, grid, P, st)
+                   : launch_flush_p<BITS, G, true>(ea, grid, P, st);
+}
+
+int launch_flush_any(const kivi_dims &d, const kivi_cache &c, void *stream, bool keys_only) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   EncodeArgs ea = encode_args(d, c);
   ea.src_k = ea.k_res;
@@ -2073,22 +2345,58 @@ int launch_flush(const kivi_dims &d, const kivi_cache &c, void *stream) {
   const int pmax = min(KIVI_FLUSH_P, 128 / G);
   const int P = tiles % 4 == 0 && pmax >= 4 ? 4 : tiles % 2 == 0 && pmax >= 2 ? 2 : 1;
   const dim3 grid(tiles / P, d.heads, d.batch);
-  if (d.bits == 2 && G == 32) return launch_flush_t<2, 32>(ea, grid, P, st);
-  if (d.bits == 2 && G == 64) return launch_flush_t<2, 64>(ea, grid, P, st);
-  if (d.bits == 2 && G == 128) return launch_flush_t<2, 128>(ea, grid, P, st);
-  if (d.bits == 4 && G == 32) return launch_flush_t<4, 32>(ea, grid, P, st);
-  if (d.bits == 4 && G == 64) return launch_flush_t<4, 64>(ea, grid, P, st);
-  if (d.bits == 4 && G == 128) return launch_flush_t<4, 128>(ea, grid, P, st);
-  if (d.bits == 8 && G == 32) return launch_flush_t<8, 32>(ea, grid, P, st);
-  if (d.bits == 8 && G == 64) return launch_flush_t<8, 64>(ea, grid, P, st);
-  if (d.bits == 8 && G == 128) return launch_flush_t<8, 128>(ea, grid, P, st);
+  const bool k = keys_only;
+  if (d.bits == 2 && G == 32) return launch_flush_t<2, 32>(ea, grid, P, st, k);
+  if (d.bits == 2 && G == 64) return launch_flush_t<2, 64>(ea, grid, P, st, k);
+  if (d.bits == 2 && G == 128) return launch_flush_t<2, 128>(ea, grid, P, st, k);
+  if (d.bits == 4 && G == 32) return launch_flush_t<4, 32>(ea, grid, P, st, k);
+  if (d.bits == 4 && G == 64) return launch_flush_t<4, 64>(ea, grid, P, st, k);
+  if (d.bits == 4 && G == 128) return launch_flush_t<4, 128>(ea, grid, P, st, k);
+  if (d.bits == 8 && G == 32) return launch_flush_t<8, 32>(ea, grid, P, st, k);
+  if (d.bits == 8 && G == 64) return launch_flush_t<8, 64>(ea, grid, P, st, k);
+  if (d.bits == 8 && G == 128) return launch_flush_t<8, 128>(ea, grid, P, st, k);
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_flush(const kivi_dims &d, const kivi_cache &c, void *stream) {
+  return launch_flush_any(d, c, stream, false);
+}
+
+int launch_flush_keys(const kivi_dims &d, const kivi_cache &c, void *stream) {
+  return launch_flush_any(d, c, stream, true);
+}
+
+template <int BITS, int G>
+int launch_append_vq_t(const EncodeArgs &ea, int batch, const void *k_new, const void *v_new,
+                       hipStream_t st) {
+  hipLaunchKernelGGL((append_vq_kernel<BITS, G>), dim3(batch), dim3(kAppendVqThreads), 0, st, ea,
+                     static_cast<const half_t *>(k_new), static_cast<const half_t *>(v_new));
+  return (int)hipGetLastError();
+}
+
+int launch_append_vq(const kivi_dims &d, const kivi_cache &c, const void *k_new,
+                     const void *v_new, void *stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const EncodeArgs ea = encode_args(d, c);
+  const int G = d.group;
+  if (d.bits == 2 && G == 32) return launch_append_vq_t<2, 32>(ea, d.batch, k_new, v_new, st);
+  if (d.bits == 2 && G == 64) return launch_append_vq_t<2, 64>(ea, d.batch, k_new, v_new, st);
+  if (d.bits == 2 && G == 128) return launch_append_vq_t<2, 128>(ea, d.batch, k_new, v_new, st);
+  if (d.bits == 4 && G == 32) return launch_append_vq_t<4, 32>(ea, d.batch, k_new, v_new, st);
+  if (d.bits == 4 && G == 64) return launch_append_vq_t<4, 64>(ea, d.batch, k_new, v_new, st);
+  if (d.bits == 4 && G == 128) return launch_append_vq_t<4, 128>(ea, d.batch, k_new, v_new, st);
+  if (d.bits == 8 && G == 32) return launch_append_vq_t<8, 32>(ea, d.batch, k_new, v_new, st);
+  if (d.bits == 8 && G == 64) return launch_append_vq_t<8, 64>(ea, d.batch, k_new, v_new, st);
+  if (d.bits == 8 && G == 128) return launch_append_vq_t<8, 128>(ea, d.batch, k_new, v_new, st);
   return (int)hipErrorInvalidValue;
 }
 
 int launch_prefill(const kivi_dims &d, const kivi_cache &c, const void *k, const void *v,
-                   int32_t src_len, const int32_t *len, const int32_t *res, void *stream) {
+                   int32_t src_len, const int32_t *len, const int32_t *res, void *stream,
+                   bool value_queue) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   EncodeArgs ea = encode_args(d, c);
+  ea.vq = value_queue ? 1 : 0;
   ea.src_k = static_cast<const half_t *>(k);
   ea.src_v = static_cast<const half_t *>(v);
   ea.src_tokens = src_len;
@@ -2150,18 +2458,18 @@ void set_sink(DecodeArgs &da, const DecodePlan &p, const void *k_sink, const voi
 }
 
 int launch_decode_any(const kivi_dims &d, const DecodeArgs &da, const EncodeArgs &ea, bool fused,
-                      int depth, hipStream_t st, bool rope = false) {
+                      int depth, hipStream_t st, bool rope = false, bool vq = false) {
   const dim3 grid(da.splits, d.heads, d.batch);
   const int G = d.group;
-  if (d.bits == 2 && G == 32) return launch_decode_t<2, 32>(da, ea, fused, depth, grid, st, rope);
-  if (d.bits == 2 && G == 64) return launch_decode_t<2, 64>(da, ea, fused, depth, grid, st, rope);
-  if (d.bits == 2 && G == 128) return launch_decode_t<2, 128>(da, ea, fused, depth, grid, st, rope);
-  if (d.bits == 4 && G == 32) return launch_decode_t<4, 32>(da, ea, fused, depth, grid, st, rope);
-  if (d.bits == 4 && G == 64) return launch_decode_t<4, 64>(da, ea, fused, depth, grid, st, rope);
-  if (d.bits == 4 && G == 128) return launch_decode_t<4, 128>(da, ea, fused, depth, grid, st, rope);
-  if (d.bits == 8 && G == 32) return launch_decode_t<8, 32>(da, ea, fused, depth, grid, st, rope);
-  if (d.bits == 8 && G == 64) return launch_decode_t<8, 64>(da, ea, fused, depth, grid, st, rope);
-  if (d.bits == 8 && G == 128) return launch_decode_t<8, 128>(da, ea, fused, depth, grid, st, rope);
+  if (d.bits == 2 && G == 32) return launch_decode_t<2, 32>(da, ea, fused, depth, grid, st, rope, vq);
+  if (d.bits == 2 && G == 64) return launch_decode_t<2, 64>(da, ea, fused, depth, grid, st, rope, vq);
+  if (d.bits == 2 && G == 128) return launch_decode_t<2, 128>(da, ea, fused, depth, grid, st, rope, vq);
+  if (d.bits == 4 && G == 32) return launch_decode_t<4, 32>(da, ea, fused, depth, grid, st, rope, vq);
+  if (d.bits == 4 && G == 64) return launch_decode_t<4, 64>(da, ea, fused, depth, grid, st, rope, vq);
+  if (d.bits == 4 && G == 128) return launch_decode_t<4, 128>(da, ea, fused, depth, grid, st, rope, vq);
+  if (d.bits == 8 && G == 32) return launch_decode_t<8, 32>(da, ea, fused, depth, grid, st, rope, vq);
+  if (d.bits == 8 && G == 64) return launch_decode_t<8, 64>(da, ea, fused, depth, grid, st, rope, vq);
+  if (d.bits == 8 && G == 128) return launch_decode_t<8, 128>(da, ea, fused, depth, grid, st, rope, vq);
   return (int)hipErrorInvalidValue;
 }
 
@@ -2185,10 +2493,11 @@ int launch_fill_zero(void *p, size_t bytes, void *stream) {
 
 int launch_stream_read(const void *src, size_t bytes, int workgroups, uint32_t *sink,
                        void *stream) {
-  const size_t n16 = bytes / 16;
-  const size_t per_wg = (n16 + (size_t)workgroups - 1) / (size_t)workgroups;
+  // slices of whole 16-byte pieces, each below 4 GiB (32-bit buffer offsets)
+  const size_t per_wg = ((bytes + (size_t)workgroups - 1) / (size_t)workgroups + 15) / 16 * 16;
+  if (per_wg >= ((size_t)1 << 32)) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(stream_read_kernel, dim3(workgroups), dim3(kStreamThreads), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint4 *>(src), n16,
+                     static_cast<hipStream_t>(stream), static_cast<const char *>(src), bytes,
                      per_wg, sink);
   return (int)hipGetLastError();
 }
@@ -2266,6 +2575,16 @@ int launch_decode_noalloc(const kivi_dims &d, const kivi_cache &c, const DecodeP
   DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, base + kNoAllocTicketBytes);
   da.tickets = reinterpret_cast<uint32_t *>(base);
   return launch_decode_any(d, da, encode_args(d, c), false, p.depth, st);
+}
+
+int launch_decode_vq(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p, const void *q,
+                     float *out, float sm_scale, void *workspace, void *stream) {
+  DecodeArgs da = decode_args(d, c, p, q, out, sm_scale, workspace);
+  // the token-by-token tail: at most R + G - 1 tokens over all waves
+  const int waves = kDecodeWaves * p.splits;
+  da.win_per_wave = ((d.residual + d.group + waves - 1) / waves + 7) / 8 * 8;
+  return launch_decode_any(d, da, encode_args(d, c), false, p.depth,
+                           static_cast<hipStream_t>(stream), false, true);
 }
 
 int launch_decode_sink(const kivi_dims &d, const kivi_cache &c, const DecodePlan &p,

@@ -23,7 +23,8 @@ ST_RESIDUAL_FULL, ST_CAPACITY, ST_BAD_LENGTH, ST_TICKETS = 0x1, 0x2, 0x4, 0x8
 # Every symbol the public header declares.
 EXPORTS = ("kivi_validate_dims", "kivi_cache_init", "kivi_workspace_init", "kivi_append_kv", "kivi_flush_residual", "kivi_prefill",
            "kivi_decode_workspace_bytes", "kivi_decode_splits", "kivi_decode_step_kernels", "kivi_decode_attn",
-           "kivi_decode_attn_noalloc",
+           "kivi_decode_attn_noalloc", "kivi_prefill_vq", "kivi_append_kv_vq",
+           "kivi_flush_residual_vq", "kivi_decode_attn_vq",
            "kivi_decode_attn_rope", "kivi_decode_attn_sink", "kivi_decode_step",
            "kivi_decode_step_sink", "kivi_stream_read",
            "kivi_strerror")
@@ -64,6 +65,11 @@ def lib():
         L.kivi_append_kv.argtypes = [P(Dims), P(CacheStruct), V, V, V]
         L.kivi_flush_residual.argtypes = [P(Dims), P(CacheStruct), V]
         L.kivi_prefill.argtypes = [P(Dims), P(CacheStruct), V, V, I32, V, V, V]
+        L.kivi_prefill_vq.argtypes = [P(Dims), P(CacheStruct), V, V, I32, V, V, V]
+        L.kivi_append_kv_vq.argtypes = [P(Dims), P(CacheStruct), V, V, V]
+        L.kivi_flush_residual_vq.argtypes = [P(Dims), P(CacheStruct), V]
+        L.kivi_decode_attn_vq.argtypes = [P(Dims), P(CacheStruct), V, V, ctypes.c_float, V,
+                                          ctypes.c_size_t, V]
         L.kivi_decode_workspace_bytes.argtypes = [P(Dims)]
         L.kivi_decode_workspace_bytes.restype = ctypes.c_size_t
         L.kivi_decode_splits.argtypes = [P(Dims)]
@@ -235,6 +241,49 @@ def prefill(cache, k, v, lengths, window=None):
                               v.data_ptr(), int(src_len), lengths.data_ptr(),
                               None if window is None else window.data_ptr(), _stream()),
            "kivi_prefill")
+
+
+# ---- value queue: a cache kept with these four calls holds its values in
+# an fp16 ring of the newest R, the older ones quantized token by token
+
+def prefill_vq(cache, k, v, lengths, window=None):
+    """kivi_prefill_vq: prefill with a value queue (arguments as prefill)."""
+    d = cache.dims
+    src_len = k.shape[2]
+    _need(k, torch.float16, (d.batch, d.heads, src_len, d.head_dim), "k")
+    _need(v, torch.float16, (d.batch, d.heads, src_len, d.head_dim), "v")
+    _need(lengths, torch.int32, (d.batch,), "lengths")
+    if window is not None:
+        _need(window, torch.int32, (d.batch,), "window")
+    _check(lib().kivi_prefill_vq(ctypes.byref(d), ctypes.byref(cache.struct()), k.data_ptr(),
+                                 v.data_ptr(), int(src_len), lengths.data_ptr(),
+                                 None if window is None else window.data_ptr(), _stream()),
+           "kivi_prefill_vq")
+
+
+def append_kv_vq(cache, k_new, v_new):
+    d = cache.dims
+    _need(k_new, torch.float16, (d.batch, d.heads, d.head_dim), "k_new")
+    _need(v_new, torch.float16, (d.batch, d.heads, d.head_dim), "v_new")
+    _check(lib().kivi_append_kv_vq(ctypes.byref(d), ctypes.byref(cache.struct()),
+                                   k_new.data_ptr(), v_new.data_ptr(), _stream()),
+           "kivi_append_kv_vq")
+
+
+def flush_residual_vq(cache):
+    d = cache.dims
+    _check(lib().kivi_flush_residual_vq(ctypes.byref(d), ctypes.byref(cache.struct()), _stream()),
+           "kivi_flush_residual_vq")
+
+
+def decode_attn_vq(cache, q, sm_scale, out=None, workspace=None):
+    """decode_attn over a value-queue cache; fp32 output."""
+    d = cache.dims
+    out, workspace, nbytes = _decode_buffers(cache, q, out, workspace)
+    _check(lib().kivi_decode_attn_vq(ctypes.byref(d), ctypes.byref(cache.struct()), q.data_ptr(),
+                                     out.data_ptr(), ctypes.c_float(sm_scale), workspace.data_ptr(),
+                                     ctypes.c_size_t(nbytes), _stream()), "kivi_decode_attn_vq")
+    return out
 
 
 def new_workspace(dims, device="cuda"):

@@ -311,6 +311,49 @@ int kivi_decode_attn_rope(const kivi_dims *dims, const kivi_cache *cache,
                           size_t workspace_bytes, void *stream);
 
 /*
+ * ---- value queue ([P1] section 3.2, value cache management) -----------
+ * A cache kept with these four calls (and only these) holds its values in
+ * an fp16 queue of the newest R: each appended value enters the queue and,
+ * once R are queued, the oldest leaves it and is quantized on its own (per
+ * token, D/G groups of G channels, the quantizer above).  Keys keep the
+ * window of kivi_append_kv / kivi_flush_residual ([P1] section 3.1).  With
+ * T = q_len[b] + r_len[b] tokens in all, the first vq = max(0, T - R) values
+ * are quantized (value position t at [t / G][..][t % G] of the value tiles,
+ * exactly the codes the bulk per-token quantizer gives token t), and v_res
+ * is a ring: the value of token t >= vq is in slot t mod R.  The context is
+ * tokens [0, vq) with quantized keys and values, [vq, q_len) with quantized
+ * keys and fp16 values, [q_len, T) with fp16 keys and values.  The buffers,
+ * lengths, status bits and errors are those of the calls without _vq.
+ */
+
+/* kivi_prefill for a value-queue cache: keys as kivi_prefill; of the values,
+ * tokens [0, max(0, len - R)) quantized, the rest copied to ring slots
+ * t mod R; value positions past the quantized ones left zero. */
+int kivi_prefill_vq(const kivi_dims *dims, const kivi_cache *cache,
+                    const void *k, const void *v, int32_t src_len,
+                    const int32_t *len, const int32_t *res, void *stream);
+
+/* Append one token per sequence: the key to key-window slot r_len[b] (as
+ * kivi_append_kv); with T = q_len[b] + r_len[b] >= R, the value in ring slot
+ * T mod R (token T - R) is first quantized into value position T - R; the
+ * slot then takes the new value; r_len[b] += 1.  One kernel (a workgroup
+ * per sequence); KIVI_ST_RESIDUAL_FULL / KIVI_ST_BAD_LENGTH as
+ * kivi_append_kv. */
+int kivi_append_kv_vq(const kivi_dims *dims, const kivi_cache *cache,
+                      const void *k_new, const void *v_new, void *stream);
+
+/* kivi_flush_residual for a value-queue cache: a full key window becomes R/G
+ * key groups (q_len += R, r_len = 0); the values are not touched. */
+int kivi_flush_residual_vq(const kivi_dims *dims, const kivi_cache *cache,
+                           void *stream);
+
+/* kivi_decode_attn over a value-queue cache's context (above), in token
+ * order; arguments, workspace and errors as kivi_decode_attn. */
+int kivi_decode_attn_vq(const kivi_dims *dims, const kivi_cache *cache,
+                        const void *q, float *out, float sm_scale,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One whole generation step: kivi_append_kv, then kivi_decode_attn, then
  * kivi_flush_residual ([P1] section 3.1: append to the fp16 window, attend
  * over quantized and window tokens, quantize the window once it holds R

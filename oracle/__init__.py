@@ -23,6 +23,9 @@ path computes, written from the pages' definitions:
   (keys stored before the rotation) and the decode that uses it.
 * ``sink``       -- the decode over an fp16 attention-sink segment followed by
   the cache's tokens.
+* ``value_queue`` -- the cache whose values leave an fp16 queue of the newest
+  R one token at a time (quantized per token as they leave), keys flushed R
+  at a time; its prefill, append, key flush and decode.
 
 Precision: the quantizer runs the fixed fp32 operation sequence stated in
 ``quantizer``; attention runs in fp64 on the exactly dequantized values.
@@ -32,4 +35,4 @@ fix (hand-worked cases, brute force, closed forms, invariants); none is
 "parity unpinned".
 """
 
-from . import attention, axis_ablation, cache, packing, quantizer, rope, sink  # noqa: F401
+from . import attention, axis_ablation, cache, packing, quantizer, rope, sink, value_queue  # noqa: F401

@@ -50,8 +50,26 @@ def test_step_tokens_end_on_the_workload_or_append_one_more():
     assert k4.shape == (8, w4.config.heads, w4.config.head_dim) and k4.dtype == np.float16
 
 
-def test_cpu_baseline_reports_the_oracle_on_one_core():
+def test_cpu_baseline_reports_the_oracle_and_its_threads():
     w = wl.generate(1)
     r = bench.cpu_baseline(w, 0.3)
-    assert r["kind"] == "oracle" and r["cores"] == 1 and r["unit"] == "query-heads/s"
+    assert r["kind"] == "oracle" and r["unit"] == "query-heads/s"
     assert r["value"] > 0 and "steps" in r["sample"]
+    assert r["cores"] >= 1 and r["host_cpus"] == os.cpu_count()
+    assert r["affinity_cpus"] == len(os.sched_getaffinity(0))
+    assert r["cores"] == (r["blas_threads"] or 1)
+
+
+def test_oracle_sample_times_decode_and_flush():
+    w = wl.generate(3, batch=2)
+    r = bench.oracle_sample(w, 4, 1, flush=True)
+    assert r["heads"] == 4 and r["decode_s"] > 0 and r["query_heads_per_s"] > 0
+    assert r["flush_s"] > 0 and r["flushes_per_s"] > 0
+
+
+def test_every_other_workload_is_listed_once():
+    """The decode of every workload besides the headline one, long context
+    at both widths."""
+    assert sorted(bench.EXTRA_WORKLOADS, key=str) == sorted(
+        [(1, None), (3, None), (4, None), (5, 2), (5, 4)], key=str)
+    assert set(bench.ORACLE_SAMPLE_HEADS) == {1, 2, 3, 4, 5}
