@@ -1527,21 +1527,29 @@ __device__ __forceinline__ void vq_token(const DecodeArgs &a, size_t bh, int t, 
 // window again.  Lane (slot, w) holds channels w * CPW .. w * CPW + CPW - 1
 // of one token per step: exactly one key code word and one value code word.
 //   values: a value group (one token, G channels) is G / CPW consecutive
-//   lanes, whose minimum and maximum meet by DPP.
+//   lanes, whose minimum and maximum meet by DPP; no other wave is needed.
 //   keys: a key group (one channel over the G tokens of a tile) is spread
-//   over the slots and steps of G / wpw waves.  Each lane reduces its own
-//   steps and stores (-minimum, maximum) of its channel pairs in LDS; after
-//   a barrier, one thread per (tile, channel) reduces those over the tile's
-//   waves and slots and computes the group's parameters, which every lane
-//   reads back for its CPW channels after a second barrier.
+//   over the slots and steps of the tile's G / wpw waves.  Before its
+//   quantized stream, each lane reduces its own steps and stores
+//   (-minimum, maximum) of its channel pairs in LDS, and each wave counts
+//   itself in (a release increment of a workgroup counter).  After its
+//   stream, a wave that sees every wave counted in (an acquire read)
+//   reduces its tile's partials over the tile's waves and slots itself, one
+//   channel pair per lane, into parameters of its own, which its lanes read
+//   back for their CPW channels to encode the key words; the tile's first
+//   wave writes the parameters to the cache.  No workgroup barrier is
+//   involved, and the work overlaps the slower waves' streams; a wave that
+//   finds the count short (it never has in practice: the partials are
+//   posted long before any stream ends) does the same after the
+//   workgroup's combine barrier instead.
 // Minima travel negated, so that one packed fp16 maximum reduces both.
-constexpr int kMaxRegFlushTiles = 4;  // R <= 128, G >= 32
 
 template <int BITS, int G>
 struct RegFlushSmem {
   uint32_t part[kDecodeWaves][DecCfg<BITS, G>::TQS][kD / 2][2];  // [wave][slot][pair]{-min, max}
-  float2 prm[kMaxRegFlushTiles][kD];                              // [tile][channel]{min, 1/step}
-  float step[kMaxRegFlushTiles][kD];
+  float2 prm[kDecodeWaves][kD];  // [wave][channel]{min, 1/step} of the wave's tile
+  float step[kDecodeWaves][kD];
+  uint32_t arrived;              // waves whose key partials are posted
 };
 
 // LDS of the whole-step flush: the register path's, or the window-reading
@@ -1585,19 +1593,13 @@ __device__ __forceinline__ uint32_t encode_lane_word(const uint4 (&x)[NV], Fast 
   return pack_codes<BITS, CPW>(cd, kTop);
 }
 
-// Before the barrier: the lane's key partials to LDS, and its value groups
-// and value code words (one per step).  tile0 is the window's first tile in
-// the cache; the wave's tokens [begin, begin + wsteps * STEP) lie in one tile.
+// Before the stream: the lane's key partials to LDS.
 template <int BITS, int G>
-__device__ __forceinline__ void flush_regs_values(const EncodeArgs &ea, RegFlushSmem<BITS, G> &rf,
-                                                  const WinStep<BITS, G> (&x)[WinCfg<BITS, G>::PF],
-                                                  int wsteps, size_t tile0, int begin, int wv,
-                                                  int w, int slot) {
-  using C = DecCfg<BITS, G>;
+__device__ __forceinline__ void flush_regs_key_partials(RegFlushSmem<BITS, G> &rf,
+                                                        const WinStep<BITS, G> (&x)[WinCfg<BITS, G>::PF],
+                                                        int wsteps, int wv, int w, int slot) {
   using WC = WinCfg<BITS, G>;
-  constexpr int NV = WC::NV, HW = 4 * NV;  // half2 words per lane and operand
-  constexpr int LG = G / C::CPW;           // lanes per value group
-  constexpr float kTop = (float)((1 << BITS) - 1);
+  constexpr int HW = 4 * WC::NV;  // half2 words per lane and operand
   uint32_t kmn[HW], kmx[HW];
 #pragma unroll
   for (int h = 0; h < HW; ++h) kmn[h] = kmx[h] = u4_get(x[0].k[h / 4], h % 4);
@@ -1614,7 +1616,21 @@ __device__ __forceinline__ void flush_regs_values(const EncodeArgs &ea, RegFlush
 #pragma unroll
   for (int j = 0; j < HW / 2; ++j)
     dst[j] = make_uint4(neg16x2(kmn[2 * j]), kmx[2 * j], neg16x2(kmn[2 * j + 1]), kmx[2 * j + 1]);
+}
 
+// The lane's value groups and value code words (one per step).  tile0 is the
+// window's first tile in the cache; the wave's tokens [begin, begin + wsteps
+// * STEP) lie in one tile.
+template <int BITS, int G>
+__device__ __forceinline__ void flush_regs_values(const EncodeArgs &ea,
+                                                  const WinStep<BITS, G> (&x)[WinCfg<BITS, G>::PF],
+                                                  int wsteps, size_t tile0, int begin, int w,
+                                                  int slot) {
+  using C = DecCfg<BITS, G>;
+  using WC = WinCfg<BITS, G>;
+  constexpr int NV = WC::NV, HW = 4 * NV;  // half2 words per lane and operand
+  constexpr int LG = G / C::CPW;           // lanes per value group
+  constexpr float kTop = (float)((1 << BITS) - 1);
 #pragma unroll
   for (int i = 0; i < WC::PF; ++i)
     if (i < wsteps) {
@@ -1641,49 +1657,64 @@ __device__ __forceinline__ void flush_regs_values(const EncodeArgs &ea, RegFlush
     }
 }
 
-// After the barrier: thread tid takes channel 2 * cp + mm of tile T
-// (tid = 128 T + 2 cp + mm); the pair's two threads swap their halves by DPP.
+// One wave: the parameters of key tile T (every one of its kD / 2 channel
+// pairs, lane cp taking pair cp) from the partials of the tile's nwt waves,
+// into the wave's own slot of rf.prm / rf.step; with `publish`, also to the
+// cache.
 template <int BITS, int G>
-__device__ __forceinline__ void flush_regs_params(const EncodeArgs &ea, RegFlushSmem<BITS, G> &rf,
-                                                  size_t tile0, int R, int wpw, int tid) {
+__device__ __forceinline__ void flush_regs_tile_params(const EncodeArgs &ea,
+                                                       RegFlushSmem<BITS, G> &rf, size_t tile0,
+                                                       int T, int nwt, int wv, int cp,
+                                                       bool publish) {
   using C = DecCfg<BITS, G>;
   constexpr float kTop = (float)((1 << BITS) - 1);
-  const int T = tid >> 7, cp = (tid >> 1) & 63, mm = tid & 1;
-  if (T >= R / G) return;  // uniform over each pair of waves
-  const int nwt = G / wpw, u0 = T * nwt;
-  uint32_t v = rf.part[u0][0][cp][mm];
-  for (int u = u0; u < u0 + nwt; ++u)
+  const int u0 = T * nwt;
+  uint32_t nmn = rf.part[u0][0][cp][0], mx = rf.part[u0][0][cp][1];
+  for (int u = u0; u < u0 + nwt; ++u) {
+    uint2 pv[C::TQS];
 #pragma unroll
-    for (int sl = 0; sl < C::TQS; ++sl) v = pk_max16(v, rf.part[u][sl][cp][mm]);
-  const half2_t hv = __builtin_bit_cast(half2_t, v), hp = __builtin_bit_cast(half2_t, dppu<0xB1>(v));
-  const float mn = mm ? -(float)hp.y : -(float)hv.x;
-  const float mx = mm ? (float)hv.y : (float)hp.x;
-  const GroupParams g = group_params(mn, mx, kTop);
-  const int c = 2 * cp + mm;
-  ea.k_zero[(tile0 + T) * kD + c] = g.zero16;
-  ea.k_scale[(tile0 + T) * kD + c] = g.scale16;
-  rf.prm[T][c] = make_float2(g.mn, g.rs);
-  rf.step[T][c] = g.s;
+    for (int sl = 0; sl < C::TQS; ++sl)
+      pv[sl] = *reinterpret_cast<const uint2 *>(&rf.part[u][sl][cp][0]);
+#pragma unroll
+    for (int sl = 0; sl < C::TQS; ++sl) {
+      nmn = pk_max16(nmn, pv[sl].x);
+      mx = pk_max16(mx, pv[sl].y);
+    }
+  }
+  const half2_t hn = __builtin_bit_cast(half2_t, nmn), hx = __builtin_bit_cast(half2_t, mx);
+  const GroupParams g0 = group_params(-(float)hn.x, (float)hx.x, kTop);
+  const GroupParams g1 = group_params(-(float)hn.y, (float)hx.y, kTop);
+  const int c = 2 * cp;
+  rf.prm[wv][c] = make_float2(g0.mn, g0.rs);
+  rf.prm[wv][c + 1] = make_float2(g1.mn, g1.rs);
+  rf.step[wv][c] = g0.s;
+  rf.step[wv][c + 1] = g1.s;
+  if (publish) {
+    *reinterpret_cast<half2_t *>(ea.k_zero + (tile0 + T) * kD + c) = half2_t{g0.zero16, g1.zero16};
+    *reinterpret_cast<half2_t *>(ea.k_scale + (tile0 + T) * kD + c) =
+        half2_t{g0.scale16, g1.scale16};
+  }
 }
 
-// After the second barrier: the lane's key code words (one per step).
+// The lane's key code words (one per step), from the parameters this wave
+// computed for its tile.
 template <int BITS, int G>
 __device__ __forceinline__ void flush_regs_keys(const EncodeArgs &ea, const RegFlushSmem<BITS, G> &rf,
                                                 const WinStep<BITS, G> (&x)[WinCfg<BITS, G>::PF],
-                                                int wsteps, size_t tile0, int begin, int w,
+                                                int wsteps, size_t tile0, int begin, int wv, int w,
                                                 int slot) {
   using C = DecCfg<BITS, G>;
   using WC = WinCfg<BITS, G>;
   const int T = begin / G;
   float2 pr[C::CPW];
 #pragma unroll
-  for (int i = 0; i < C::CPW; ++i) pr[i] = rf.prm[T][w * C::CPW + i];
+  for (int i = 0; i < C::CPW; ++i) pr[i] = rf.prm[wv][w * C::CPW + i];
 #pragma unroll
   for (int i = 0; i < WC::PF; ++i)
     if (i < wsteps) {
       const int t = begin + i * WC::STEP + slot;
       ea.k_codes[(tile0 + T) * (C::W * G) + w * G + t % G] = encode_lane_word<BITS, WC::NV>(
-          x[i].k, [&](int c) { return pr[c]; }, [&](int c) { return rf.step[T][w * C::CPW + c]; });
+          x[i].k, [&](int c) { return pr[c]; }, [&](int c) { return rf.step[wv][w * C::CPW + c]; });
     }
 }
 
@@ -1722,6 +1753,7 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
     if (tid == 0) {
       sm.lens[0] = a.q_len[b];
       sm.lens[1] = a.r_len[b];
+      fused_flush_smem<BITS, G>().reg.arrived = 0u;
     }
     __syncthreads();
     ql = sm.lens[0];
@@ -1941,19 +1973,29 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
   // the wait before each sub-chunk only covers its own loads), then the
   // remaining n mod kDecodeDepth, whose loads are already in flight.
   int c0 = 0;
+  // FUSED, early: this wave's key partials before its stream (its window
+  // rows arrive ahead of its first sub-chunk, so waiting for them costs
+  // nothing), then the wave counts itself in
+  [[maybe_unused]] const int nwt = a.win_per_wave > 0 ? G / a.win_per_wave : 1;
+  [[maybe_unused]] const int tileT = ws.begin / G;
+  [[maybe_unused]] bool keys_done = true;
   if constexpr (FUSED) {
     if (early) {
-      // The window's attention and the flush's value words and key
-      // partials, which need no other wave (the key groups across waves are
-      // finished after the workgroup's combine barrier).  (Running them after
-      // the first round of sub-chunks instead, with that round's refills in
-      // flight, measured the same: 34.1 against 33.3 us a step on the 7B
-      // layer.)
-      window();
-      if (wsteps > 0)
-        flush_regs_values<BITS, G>(ea, fused_flush_smem<BITS, G>().reg, wpf, wsteps, tile0,
-                                   ws.begin, wv, w, slot);
-      store_new();
+      auto &rf = fused_flush_smem<BITS, G>().reg;
+      // the appended token's row replaces its slot's stale one first (the
+      // window pass does the same later; doing it twice is harmless)
+#pragma unroll
+      for (int i = 0; i < WC::PF; ++i) {
+        const bool hit = ws.begin + i * WC::STEP + slot == rnew;
+#pragma unroll
+        for (int v = 0; v < WC::NV; ++v) {
+          wpf[i].k[v] = sel4(hit, xnew.k[v], wpf[i].k[v]);
+          wpf[i].v[v] = sel4(hit, xnew.v[v], wpf[i].v[v]);
+        }
+      }
+      if (wsteps > 0) flush_regs_key_partials<BITS, G>(rf, wpf, wsteps, wv, w, slot);
+      if (lane == 0)
+        __hip_atomic_fetch_add(&rf.arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
   for (; c0 + kDecodeDepth <= qs.n; c0 += kDecodeDepth) {
@@ -2004,6 +2046,22 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
   } else if (!early) {
     window();
     store_new();
+  } else if constexpr (FUSED) {
+    // the window's attention, the flush's value words, and (once every wave
+    // has posted its key partials) this wave's key tile and key words
+    window();
+    store_new();
+    if (wsteps > 0) {
+      auto &rf = fused_flush_smem<BITS, G>().reg;
+      flush_regs_values<BITS, G>(ea, wpf, wsteps, tile0, ws.begin, w, slot);
+      const uint32_t in = (uint32_t)__builtin_amdgcn_readfirstlane((int)__hip_atomic_load(
+          &rf.arrived, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+      keys_done = in == (uint32_t)kDecodeWaves;
+      if (keys_done) {
+        flush_regs_tile_params<BITS, G>(ea, rf, tile0, tileT, nwt, wv, lane, wv % nwt == 0);
+        flush_regs_keys<BITS, G>(ea, rf, wpf, wsteps, tile0, ws.begin, wv, w, slot);
+      }
+    }
   }
   // fp16 sink tokens (the sequence's first tokens, kept unquantized ahead of
   // the quantized ones, at positions 0 .. n_sink - 1): this wave's share
@@ -2085,10 +2143,13 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
     if (tid < kD) a.out[bh * kD + tid] = L > 0.0f ? acc_out / L : 0.0f;
     if constexpr (FUSED) {
       if (early) {
-        auto &rf = fused_flush_smem<BITS, G>().reg;
-        flush_regs_params<BITS, G>(ea, rf, tile0, a.R, a.win_per_wave, tid);
-        __syncthreads();
-        if (wsteps > 0) flush_regs_keys<BITS, G>(ea, rf, wpf, wsteps, tile0, ws.begin, w, slot);
+        // a wave that found the partials count short finishes its keys here,
+        // after the combine barrier (every wave posted before its stream)
+        if (!keys_done) {
+          auto &rf = fused_flush_smem<BITS, G>().reg;
+          flush_regs_tile_params<BITS, G>(ea, rf, tile0, tileT, nwt, wv, lane, wv % nwt == 0);
+          flush_regs_keys<BITS, G>(ea, rf, wpf, wsteps, tile0, ws.begin, wv, w, slot);
+        }
       } else if (flush) {
         // longer windows: read again (mostly L2 hits, this workgroup has
         // just read them) and quantized through LDS
