@@ -138,11 +138,15 @@ __device__ __forceinline__ float wave_max(float v) {
 // contraction, IEEE division, round half to even.
 #pragma clang fp contract(off)
 
+constexpr float kFastOffsetMax = 128.0f;
+
 struct GroupParams {
   float mn;  // canonical minimum (zero-point)
   float s;   // stored step as fp32
-  float rs;  // fast-path multiplier: 1 / s within one ulp, 0 when s == 0,
-             // NaN when s is an fp16 subnormal (see FastWord)
+  float rs;  // fast-path multiplier: 1 / s within one ulp, 0 when s == 0;
+             // NaN (every code exact) when s is an fp16 subnormal or
+             // |mn / s| is large (see quant_code)
+  float nm;  // fast-path offset: -(mn * rs) rounded once
   half_t zero16, scale16;
 };
 
@@ -154,81 +158,73 @@ __device__ __forceinline__ GroupParams group_params(float mn_raw, float mx_raw, 
   g.scale16 = (half_t)step;  // round to nearest even
   g.s = (float)g.scale16;
   g.rs = g.s == 0.0f ? 0.0f : g.s < 0x1p-14f ? __builtin_nanf("") : __builtin_amdgcn_rcpf(g.s);
+  const float m = g.mn * g.rs;
+  g.nm = -m;
+  if (!(fabsf(m) <= kFastOffsetMax)) g.rs = __builtin_nanf("");
   g.zero16 = (half_t)g.mn;   // exact: mn is an fp16 value
   return g;
 }
 
-// Codes are clamp(rint((x - mn) / s), 0, top) with an IEEE division.  The
-// fast path computes rint((x - mn) * rs) (rs = 1 / s within one ulp, 0 when
-// s == 0, which gives code 0 as required) and falls back to the division
-// for a word where it may differ:
-//  * near ties: the quotient q = (x - mn) / s is below 2^B (x - mn is at
-//    most the group's range and s is the range over the levels, rounded to
-//    fp16 with a relative error of at most 2^-11), and the product differs
-//    from q by at most q * 2^-22 (one rounding of the product, a reciprocal
-//    within one ulp): below 2^-18 for B <= 4, below 2^-14 for B = 8.  Away
-//    from the half-integers by more than that, the product, q and q rounded
-//    to fp32 (at most 2^-17 away for q < 256) all round to the same
-//    integer.  dmax keeps the word's largest |q - rint(q)| (exact: q >= 0,
-//    and q - rint(q) is exact by Sterbenz's lemma, so it is at most 0.5);
-//    dmax > near_half(B) means a product within 2^-16 (B <= 4) or 2^-13
-//    (B = 8) of a half-integer.
-//  * the clamp: with a normal fp16 step (s >= 2^-14, the fp32 step rounded
-//    to fp16 with a relative error of at most 2^-11) the product is at most
-//    top * (1 + 2^-10) < top + 1/2, so rint never passes top and the fast
-//    path needs no clamp.  A subnormal step has rs = NaN, which makes the
-//    word's sums NaN.
-// The fast codes enter the word as two fp32 sums, one per half word, of
-// c * 2^(B * i): integers below 2^16, so the sums are exact.  The exact path
-// needs no clamp at 0 (x - mn >= 0).
+// Codes are clamp(rint((x - mn) / s), 0, top) with x - mn rounded once and
+// an IEEE division (code_exact).  The fast path computes q' = x * rs + nm in
+// one fused multiply-add (rs = 1 / s within one ulp, 0 when s == 0, which
+// gives code 0 as required; nm = -(mn * rs) rounded once) and takes rint(q')
+// unless q' lies within 2^-16 (B <= 4) or 2^-13 (B = 8) of a half-integer,
+// where that one code takes the division instead:
+//  * the true quotient q = (x - mn) / s is below 2^B (x - mn is at most the
+//    group's range and s is the range over the levels, rounded to fp16 with
+//    a relative error of at most 2^-11).  q' differs from q by at most
+//    q 2^-23 (the reciprocal) + |mn rs| 2^-24 (nm) + q' 2^-24 (the fma's one
+//    rounding), and the exact path's own quotient from q by at most q 2^-23
+//    (its two roundings).  With |mn rs| <= 128 (kFastOffsetMax; a larger
+//    offset sets rs to NaN, so every code of the group is exact) the sum is
+//    below 1.3e-5 < 2^-16 for q < 16 and below 8.5e-5 < 2^-13 for q < 256:
+//    away from the half-integers by the margin, q' and the exact quotient
+//    round to the same integer.  q' - rint(q') is exact (Sterbenz).
+//  * the clamp: with a normal fp16 step (s >= 2^-14) q' is at most
+//    top (1 + 2^-10) + 2^-13 < top + 1/2, so rint never passes top and the
+//    fast path needs no clamp; at x = mn, |q'| is below 2^-17.  A subnormal
+//    step has rs = NaN, and a NaN q' takes the exact path.
+// Exact ties are common with fp16 data (x - mn and s are short fp16
+// multiples), so the exact path is taken per code, not per word.
+// Codes enter the word as two fp32 sums, one per half word, of
+// c * 2^(B * i): integers below 2^16, so the sums are exact.
 template <int BITS>
 constexpr float near_half() {
   return BITS <= 4 ? 0.5f - 0x1p-16f : 0.5f - 0x1p-13f;
 }
 
-// 1.0f the compiler cannot see through: fma(x, one, -mn) then stays an fma,
-// which takes an fp16 x directly (v_fma_mix_f32), and equals x - mn.
-__device__ __forceinline__ float opaque_one() {
-  float one = 1.0f;
-  asm volatile("" : "+v"(one));
-  return one;
+__device__ __forceinline__ float code_exact(float x, float mn, float s) {
+  return s == 0.0f ? 0.0f : rintf((x - mn) / s);
+}
+
+// One code of a group {mn, s, rs, nm}: the fast product, or the division
+// for a product near a half-integer (or NaN).
+template <int BITS>
+__device__ __forceinline__ float quant_code(float x, float mn, float s, float rs, float nm) {
+  const float q = fmaf(x, rs, nm);
+  const float c = rintf(q);
+  if (!(fabsf(q - c) <= near_half<BITS>()))
+    return fminf(code_exact(x, mn, s), (float)((1 << BITS) - 1));
+  return c;
 }
 
 template <int BITS, int CPW>
-struct FastWord {
-  float lo = 0.0f, hi = 0.0f, dmax = 0.0f, one = opaque_one();
-  // code i of the word: channel value x of a group {mn, rs}
-  __device__ __forceinline__ void add(int i, float x, float mn, float rs) {
-    const float q = fmaf(x, one, -mn) * rs;  // x - mn, rounded once
-    const float c = rintf(q);
-    dmax = fmaxf(dmax, fabsf(q - c));
+struct CodeWord {
+  float lo = 0.0f, hi = 0.0f;
+  // code i of the word: channel value x of a group {mn, s, rs, nm}
+  __device__ __forceinline__ void add(int i, float x, float mn, float s, float rs, float nm) {
+    const float c = quant_code<BITS>(x, mn, s, rs, nm);
     const float f = (float)(1u << (BITS * (i % (CPW / 2))));
     if (i < CPW / 2)
       lo = fmaf(c, f, lo);
     else
       hi = fmaf(c, f, hi);
   }
-  __device__ __forceinline__ bool exact_needed() const {
-    const float t = lo + hi;
-    return dmax > near_half<BITS>() || t != t;
-  }
   __device__ __forceinline__ uint32_t word() const {
     return (uint32_t)lo | ((uint32_t)hi << (BITS * (CPW / 2)));
   }
 };
-
-__device__ __forceinline__ float code_exact(float x, float mn, float s) {
-  return s == 0.0f ? 0.0f : rintf((x - mn) / s);
-}
-
-// Pack CPW exact codes (as floats; clamped to top here) into one word.
-template <int BITS, int CPW>
-__device__ __forceinline__ uint32_t pack_codes(const float (&c)[CPW], float top) {
-  uint32_t w = 0;
-#pragma unroll
-  for (int i = 0; i < CPW; ++i) w |= (uint32_t)fminf(c[i], top) << (i * BITS);
-  return w;
-}
 
 #pragma clang fp contract(on)
 
@@ -282,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
   if (tile >= ntiles) return;
 
   __shared__ half_t xk[G][kD + 8], xv[G][kD + 8];
-  __shared__ float kmn[kD], kst[kD], krs[kD], vmn[kD], vst[kD], vrs[kD];
+  __shared__ float4 kpar[kD], vpar[kD];  // {mn, s, rs, nm} per key channel / value group
 
   const size_t bh = (size_t)b * a.heads + h;
   const size_t src_off = (bh * a.src_tokens + (size_t)tile * G) * kD;
@@ -319,9 +315,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     const GroupParams g = group_params(mn, mx, kTop);
     a.k_zero[ktile * kD + tid] = g.zero16;
     a.k_scale[ktile * kD + tid] = g.scale16;
-    kmn[tid] = g.mn;
-    kst[tid] = g.s;
-    krs[tid] = g.rs;
+    kpar[tid] = make_float4(g.mn, g.s, g.rs, g.nm);
   } else {
     // value group: token t, channels j*G .. j*G+G-1; stored tiled like the
     // codes, [tile][group][token]
@@ -339,41 +333,29 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
       g.mn = 0.0f;
       g.s = 0.0f;
       g.rs = 0.0f;
+      g.nm = 0.0f;
       g.zero16 = (half_t)0.0f;
       g.scale16 = (half_t)0.0f;
     }
     a.v_zero[ktile * kD + e] = g.zero16;
     a.v_scale[ktile * kD + e] = g.scale16;
-    vmn[e] = g.mn;
-    vst[e] = g.s;
-    vrs[e] = g.rs;
+    vpar[e] = make_float4(g.mn, g.s, g.rs, g.nm);
   }
   __syncthreads();
 
   for (int wi = tid; wi < W * G; wi += kThreads) {
     const int w = wi / G, t = wi % G;
     const int gi = ((w * CPW) / G) * G + t;
-    const float vm = vmn[gi], vs = vst[gi], vr = vrs[gi];
-    FastWord<BITS, CPW> fk, fv;
+    const float4 vp = vpar[gi];
+    CodeWord<BITS, CPW> fk, fv;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int c = w * CPW + i;
-      fk.add(i, (float)xk[t][c], kmn[c], krs[c]);
-      fv.add(i, (float)xv[t][c], vm, vr);
+      const float4 kp = kpar[c];
+      fk.add(i, (float)xk[t][c], kp.x, kp.y, kp.z, kp.w);
+      fv.add(i, (float)xv[t][c], vp.x, vp.y, vp.z, vp.w);
     }
-    uint32_t wk = fk.word(), wv = fv.word();
-    if (fk.exact_needed()) {
-      float cd[CPW];
-#pragma unroll
-      for (int i = 0; i < CPW; ++i) cd[i] = code_exact((float)xk[t][w * CPW + i], kmn[w * CPW + i], kst[w * CPW + i]);
-      wk = pack_codes<BITS, CPW>(cd, kTop);
-    }
-    if (fv.exact_needed()) {
-      float cd[CPW];
-#pragma unroll
-      for (int i = 0; i < CPW; ++i) cd[i] = code_exact((float)xv[t][w * CPW + i], vm, vs);
-      wv = pack_codes<BITS, CPW>(cd, kTop);
-    }
+    const uint32_t wk = fk.word(), wv = fv.word();
     a.k_codes[ktile * (W * G) + wi] = wk;
     a.v_codes[ktile * (W * G) + wi] = wv;
   }
@@ -392,7 +374,7 @@ template <int G, int TB>
 struct FlushSmem {
   static constexpr int NB = TB / G >= 2 ? 2 : 1;  // tile buffers
   half_t x[NB][2][G][kD + 8];                     // [buffer][key, value][token][channel]
-  float4 kp[NB][kD], vp[NB][kD];                  // {minimum, step, 1 / step, -}
+  float4 kp[NB][kD], vp[NB][kD];                  // {minimum, step, 1 / step, offset}
 };
 
 // A 16-byte piece of a window row, read once by the flush: non-temporal
@@ -468,8 +450,8 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
           const GroupParams g0 = group_params(mn0, mx0, kTop), g1 = group_params(mn1, mx1, kTop);
           *reinterpret_cast<half2_t *>(a.k_zero + tile * kD + c) = half2_t{g0.zero16, g1.zero16};
           *reinterpret_cast<half2_t *>(a.k_scale + tile * kD + c) = half2_t{g0.scale16, g1.scale16};
-          fs.kp[bf][c] = make_float4(g0.mn, g0.s, g0.rs, 0.0f);
-          fs.kp[bf][c + 1] = make_float4(g1.mn, g1.s, g1.rs, 0.0f);
+          fs.kp[bf][c] = make_float4(g0.mn, g0.s, g0.rs, g0.nm);
+          fs.kp[bf][c + 1] = make_float4(g1.mn, g1.s, g1.rs, g1.nm);
         } else {
           // value groups: group e / G, token e % G, in the tiled
           // [tile][group][token] order of the value zero-points
@@ -488,7 +470,7 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
           const GroupParams g = group_params(mn, mx, kTop);
           a.v_zero[tile * kD + e] = g.zero16;
           a.v_scale[tile * kD + e] = g.scale16;
-          fs.vp[bf][e] = make_float4(g.mn, g.s, g.rs, 0.0f);
+          fs.vp[bf][e] = make_float4(g.mn, g.s, g.rs, g.nm);
         }
       }
       __syncthreads();
@@ -496,7 +478,7 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
         // key words first, then value words; word (w, t) holds channels
         // w * CPW .. w * CPW + CPW - 1 of token t
         const int op = wi / (W * G), w = (wi / G) % W, t = wi % G;
-        float x[CPW], cd[CPW];
+        float x[CPW];
         if constexpr (CPW >= 8) {
 #pragma unroll
           for (int i = 0; i < CPW; i += 8) {
@@ -515,34 +497,19 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
             x[q] = (q & 1) ? (float)x2.y : (float)x2.x;
           }
         }
-        FastWord<BITS, CPW> fw;
+        CodeWord<BITS, CPW> fw;
         if (op == 0) {
 #pragma unroll
           for (int i = 0; i < CPW; ++i) {
             const float4 kq = fs.kp[bf][w * CPW + i];
-            fw.add(i, x[i], kq.x, kq.z);
+            fw.add(i, x[i], kq.x, kq.y, kq.z, kq.w);
           }
-          uint32_t word = fw.word();
-          if (fw.exact_needed()) {
-#pragma unroll
-            for (int i = 0; i < CPW; ++i) {
-              const float4 kq = fs.kp[bf][w * CPW + i];
-              cd[i] = code_exact(x[i], kq.x, kq.y);
-            }
-            word = pack_codes<BITS, CPW>(cd, kTop);
-          }
-          a.k_codes[tile * (W * G) + (wi % (W * G))] = word;
+          a.k_codes[tile * (W * G) + (wi % (W * G))] = fw.word();
         } else {
           const float4 v = fs.vp[bf][((w * CPW) / G) * G + t];
 #pragma unroll
-          for (int i = 0; i < CPW; ++i) fw.add(i, x[i], v.x, v.z);
-          uint32_t word = fw.word();
-          if (fw.exact_needed()) {
-#pragma unroll
-            for (int i = 0; i < CPW; ++i) cd[i] = code_exact(x[i], v.x, v.y);
-            word = pack_codes<BITS, CPW>(cd, kTop);
-          }
-          a.v_codes[tile * (W * G) + (wi % (W * G))] = word;
+          for (int i = 0; i < CPW; ++i) fw.add(i, x[i], v.x, v.y, v.z, v.w);
+          a.v_codes[tile * (W * G) + (wi % (W * G))] = fw.word();
         }
       }
       if (NB == 1) __syncthreads();  // a single buffer is rewritten by the next tile
@@ -1403,6 +1370,14 @@ struct WinStream {
       x.v[0] = bload2(rv, vo, 0);
     }
   }
+  // one operand only (0 keys, 1 values), 16-byte rows (WIDE)
+  __device__ __forceinline__ void issue_one(WinStep<BITS, G> &x, int step, int op) const {
+    static_assert(WC::WIDE, "16-byte row pieces");
+    const rsrc_t r = make_rsrc(op == 0 ? kr : vr, bytes);
+    const uint32_t vo = lane_voff + (uint32_t)(begin + step * WC::STEP) * (kD * 2);
+#pragma unroll
+    for (int v = 0; v < WC::NV; ++v) (op == 0 ? x.k[v] : x.v[v]) = bload4(r, vo + 16 * v, 0);
+  }
 };
 
 template <int BITS, int G>
@@ -1547,8 +1522,7 @@ __device__ __forceinline__ void vq_token(const DecodeArgs &a, size_t bh, int t, 
 template <int BITS, int G>
 struct RegFlushSmem {
   uint32_t part[kDecodeWaves][DecCfg<BITS, G>::TQS][kD / 2][2];  // [wave][slot][pair]{-min, max}
-  float2 prm[kDecodeWaves][kD];  // [wave][channel]{min, 1/step} of the wave's tile
-  float step[kDecodeWaves][kD];
+  float4 prm[kDecodeWaves][kD];  // [wave][channel]{min, step, 1/step, offset} of the wave's tile
   uint32_t arrived;              // waves whose key partials are posted
 };
 
@@ -1566,31 +1540,22 @@ __device__ __forceinline__ FusedFlushSmem<BITS, G> &fused_flush_smem() {
   return u;
 }
 
-// One code word from a lane's CPW fp16 channels; fast(i) gives channel i's
-// {minimum, 1 / step}, step(i) its step (only read for a word near a tie).
-template <int BITS, int NV, typename Fast, typename Step>
-__device__ __forceinline__ uint32_t encode_lane_word(const uint4 (&x)[NV], Fast fast, Step step) {
+// One code word from a lane's CPW fp16 channels; par(i) gives channel i's
+// group {minimum, step, 1 / step, offset}.
+template <int BITS, int NV, typename Par>
+__device__ __forceinline__ uint32_t encode_lane_word(const uint4 (&x)[NV], Par par) {
   constexpr int CPW = 8 * NV;
-  constexpr float kTop = (float)((1 << BITS) - 1);
-  float xf[CPW], cd[CPW];
+  CodeWord<BITS, CPW> fw;
 #pragma unroll
   for (int v = 0; v < NV; ++v)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const half2_t h = __builtin_bit_cast(half2_t, u4_get(x[v], e));
-      xf[8 * v + 2 * e] = (float)h.x;
-      xf[8 * v + 2 * e + 1] = (float)h.y;
+      const float4 p0 = par(8 * v + 2 * e), p1 = par(8 * v + 2 * e + 1);
+      fw.add(8 * v + 2 * e, (float)h.x, p0.x, p0.y, p0.z, p0.w);
+      fw.add(8 * v + 2 * e + 1, (float)h.y, p1.x, p1.y, p1.z, p1.w);
     }
-  FastWord<BITS, CPW> fw;
-#pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    const float2 p = fast(i);
-    fw.add(i, xf[i], p.x, p.y);
-  }
-  if (!fw.exact_needed()) return fw.word();
-#pragma unroll
-  for (int i = 0; i < CPW; ++i) cd[i] = code_exact(xf[i], fast(i).x, step(i));
-  return pack_codes<BITS, CPW>(cd, kTop);
+  return fw.word();
 }
 
 // Before the stream: the lane's key partials to LDS.
@@ -1652,8 +1617,9 @@ __device__ __forceinline__ void flush_regs_values(const EncodeArgs &ea,
         ea.v_zero[tile * kD + e] = g.zero16;
         ea.v_scale[tile * kD + e] = g.scale16;
       }
-      ea.v_codes[tile * (C::W * G) + w * G + t % G] = encode_lane_word<BITS, NV>(
-          x[i].v, [&](int) { return make_float2(g.mn, g.rs); }, [&](int) { return g.s; });
+      const float4 gp = make_float4(g.mn, g.s, g.rs, g.nm);
+      ea.v_codes[tile * (C::W * G) + w * G + t % G] =
+          encode_lane_word<BITS, NV>(x[i].v, [&](int) { return gp; });
     }
 }
 
@@ -1685,10 +1651,8 @@ __device__ __forceinline__ void flush_regs_tile_params(const EncodeArgs &ea,
   const GroupParams g0 = group_params(-(float)hn.x, (float)hx.x, kTop);
   const GroupParams g1 = group_params(-(float)hn.y, (float)hx.y, kTop);
   const int c = 2 * cp;
-  rf.prm[wv][c] = make_float2(g0.mn, g0.rs);
-  rf.prm[wv][c + 1] = make_float2(g1.mn, g1.rs);
-  rf.step[wv][c] = g0.s;
-  rf.step[wv][c + 1] = g1.s;
+  rf.prm[wv][c] = make_float4(g0.mn, g0.s, g0.rs, g0.nm);
+  rf.prm[wv][c + 1] = make_float4(g1.mn, g1.s, g1.rs, g1.nm);
   if (publish) {
     *reinterpret_cast<half2_t *>(ea.k_zero + (tile0 + T) * kD + c) = half2_t{g0.zero16, g1.zero16};
     *reinterpret_cast<half2_t *>(ea.k_scale + (tile0 + T) * kD + c) =
@@ -1706,16 +1670,194 @@ __device__ __forceinline__ void flush_regs_keys(const EncodeArgs &ea, const RegF
   using C = DecCfg<BITS, G>;
   using WC = WinCfg<BITS, G>;
   const int T = begin / G;
-  float2 pr[C::CPW];
-#pragma unroll
-  for (int i = 0; i < C::CPW; ++i) pr[i] = rf.prm[wv][w * C::CPW + i];
+  const float4 *pr = &rf.prm[wv][w * C::CPW];
 #pragma unroll
   for (int i = 0; i < WC::PF; ++i)
     if (i < wsteps) {
       const int t = begin + i * WC::STEP + slot;
-      ea.k_codes[(tile0 + T) * (C::W * G) + w * G + t % G] = encode_lane_word<BITS, WC::NV>(
-          x[i].k, [&](int c) { return pr[c]; }, [&](int c) { return rf.step[wv][w * C::CPW + c]; });
+      ea.k_codes[(tile0 + T) * (C::W * G) + w * G + t % G] =
+          encode_lane_word<BITS, WC::NV>(x[i].k, [&](int c) { return pr[c]; });
     }
+}
+
+// Flush by key waves and value waves (discosf KIVI tutorial, section 3.1:
+// once R tokens have collected, keys are quantized per channel over G
+// tokens, values per token over G channels), B = 2 or 4, R <= 128.  Grid
+// (heads, batch), one workgroup of 8 waves per full window; waves 0-3 take
+// the keys, waves 4-7 the values, 32 window tokens each (waves past R / 32
+// idle):
+//  * key wave k holds tokens [32k, 32k + 32) column-wise, lane l taking
+//    channels 2l and 2l + 1 of every token (one 4-byte load per token), so
+//    the pair's minimum and maximum are in-lane packed fp16 reductions; with
+//    G > 32 the tile's G / 32 key waves merge theirs through LDS behind the
+//    workgroup's one barrier.  Its 2B code bits per token are packed 16 / B
+//    tokens to a register, and the 16 / B lanes of each code word exchange
+//    them (a transpose in log2(16 / B) lane-exchange stages), after which
+//    lane j of a word's group holds that word for token j of the register;
+//  * value wave v holds tokens [32v, 32v + 32) row-wise, as the whole-step
+//    kernel does (flush_regs_values: groups and words per token, no LDS).
+// Codes follow the same quantizer as the other encoders (group_params,
+// quant_code).  Lengths, tickets and the
+// commit are those of flush_kernel.  VALUES false: keys only (the value
+// queue's flush).
+constexpr int kFlushKeyWaves = 4;
+constexpr int kFlushTokensPerWave = 32;
+
+// One stage of the code-word transpose: lanes d apart swap chunks of cs
+// bits (the odd chunks of the lane with bit d clear for the even chunks of
+// its partner).
+template <int D, int CS>
+__device__ __forceinline__ uint32_t transpose_stage(uint32_t mine, int lane) {
+  uint32_t other;
+  if constexpr (D == 4)
+    other = (uint32_t)__builtin_amdgcn_ds_swizzle((int)mine, 0x101F);  // lane ^ 4
+  else if constexpr (D == 2)
+    other = dppu<0x4E>(mine);  // lane ^ 2
+  else
+    other = dppu<0xB1>(mine);  // lane ^ 1
+  constexpr uint32_t even = CS == 16 ? 0x0000FFFFu : CS == 8 ? 0x00FF00FFu : 0x0F0F0F0Fu;
+  const bool clear = (lane & D) == 0;
+  const uint32_t rot = __builtin_amdgcn_alignbit(other, other, clear ? 32 - CS : CS);
+  const uint32_t keep = clear ? even : ~even;
+  return (mine & keep) | (rot & ~keep);
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t transpose_words(uint32_t v, int lane) {
+  if constexpr (BITS == 2) {
+    v = transpose_stage<4, 16>(v, lane);
+    v = transpose_stage<2, 8>(v, lane);
+    return transpose_stage<1, 4>(v, lane);
+  } else {
+    v = transpose_stage<2, 16>(v, lane);
+    return transpose_stage<1, 8>(v, lane);
+  }
+}
+
+template <int BITS, int G, bool VALUES>
+__global__ __launch_bounds__(kDecodeThreads, 3 * kDecodeWavesPerSimd) void flush_split_kernel(
+    EncodeArgs a) {
+  using C = DecCfg<BITS, G>;
+  using WC = WinCfg<BITS, G>;
+  static_assert(BITS == 2 || BITS == 4, "16 / B tokens per register, 16 / B lanes per word");
+  static_assert(kDecodeWaves == 2 * kFlushKeyWaves, "four key waves and four value waves");
+  constexpr int K = G / kFlushTokensPerWave;  // key waves per tile
+  constexpr int TPR = 16 / BITS;              // tokens per register (= lanes per word)
+  constexpr int NREG = kFlushTokensPerWave / TPR;
+  constexpr float kTop = (float)((1 << BITS) - 1);
+  __shared__ uint2 part[kFlushKeyWaves][64];  // [key wave][pair]{-min, max}
+  __shared__ int lens[2];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  if (tid == 0) {
+    lens[0] = a.q_len[b];
+    lens[1] = a.r_len[b];
+  }
+  __syncthreads();
+  const int ql = lens[0], rl = lens[1];
+  if (!flush_ok(ql, rl, G, a.R, a.cap)) {
+    if (rl == a.R && h == 0 && tid == 0)
+      atomicOr(a.status, (ql < 0 || ql % G) ? KIVI_ST_BAD_LENGTH : KIVI_ST_CAPACITY);
+    return;
+  }
+  uint32_t ticket = 0;
+  if (tid == 0)
+    ticket = __hip_atomic_fetch_add(a.tickets + (size_t)b * kTicketStride, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+  const size_t bh = (size_t)b * a.heads + h;
+  const size_t tile0 = bh * (size_t)(a.cap / G) + (size_t)(ql / G);
+  const bool keys = wv < kFlushKeyWaves;
+  const int t0 = (keys ? wv : wv - kFlushKeyWaves) * kFlushTokensPerWave;  // first window token
+  const bool busy = t0 < a.R;
+
+  if (keys) {
+    // ---- key wave: channels 2 lane, 2 lane + 1 of tokens t0 .. t0 + 31
+    uint32_t xr[kFlushTokensPerWave];
+    const rsrc_t rk = make_rsrc(a.k_res + bh * a.R * kD, busy ? (uint32_t)a.R * kD * 2 : 0u);
+#pragma unroll
+    for (int r = 0; r < kFlushTokensPerWave; ++r)
+      xr[r] = bload1(rk, (uint32_t)lane * 4, (uint32_t)(t0 + r) * (kD * 2));
+    uint32_t mn = xr[0], mx = xr[0];
+#pragma unroll
+    for (int r = 1; r < kFlushTokensPerWave; ++r) {
+      mn = pk_min16(mn, xr[r]);
+      mx = pk_max16(mx, xr[r]);
+    }
+    uint32_t nmn = neg16x2(mn);
+    if constexpr (K > 1) {
+      part[wv][lane] = make_uint2(nmn, mx);
+      __syncthreads();
+      const int u0 = (wv / K) * K;
+#pragma unroll
+      for (int u = 0; u < K; ++u) {
+        const uint2 pv = part[u0 + u][lane];
+        nmn = pk_max16(nmn, pv.x);
+        mx = pk_max16(mx, pv.y);
+      }
+    }
+    if (!busy) return;
+    const half2_t hn = __builtin_bit_cast(half2_t, nmn), hx = __builtin_bit_cast(half2_t, mx);
+    const GroupParams g0 = group_params(-(float)hn.x, (float)hx.x, kTop);
+    const GroupParams g1 = group_params(-(float)hn.y, (float)hx.y, kTop);
+    const int T = t0 / G;  // the tile within the window
+    if (wv % K == 0) {
+      *reinterpret_cast<half2_t *>(a.k_zero + (tile0 + T) * kD + 2 * lane) =
+          half2_t{g0.zero16, g1.zero16};
+      *reinterpret_cast<half2_t *>(a.k_scale + (tile0 + T) * kD + 2 * lane) =
+          half2_t{g0.scale16, g1.scale16};
+    }
+    const int w = lane / TPR, j = lane % TPR;
+    uint32_t *dst = a.k_codes + (tile0 + T) * (size_t)(C::W * G) + (size_t)w * G + (t0 % G) + j;
+#pragma unroll
+    for (int c = 0; c < NREG; ++c) {
+      // tokens c TPR .. c TPR + TPR - 1: 2B bits each, in two fp32 sums of
+      // TPR / 2 tokens (16-bit integers, exact), then one register
+      float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+      for (int k = 0; k < TPR; ++k) {
+        const half2_t x = __builtin_bit_cast(half2_t, xr[c * TPR + k]);
+        const float c0 = quant_code<BITS>((float)x.x, g0.mn, g0.s, g0.rs, g0.nm);
+        const float c1 = quant_code<BITS>((float)x.y, g1.mn, g1.s, g1.rs, g1.nm);
+        const float f = (float)(1u << (2 * BITS * (k % (TPR / 2))));
+        const float pair = fmaf(c1, (float)(1 << BITS), c0);
+        if (k < TPR / 2)
+          lo = fmaf(pair, f, lo);
+        else
+          hi = fmaf(pair, f, hi);
+      }
+      const uint32_t reg = (uint32_t)lo | ((uint32_t)hi << 16);
+      dst[c * TPR] = transpose_words<BITS>(reg, lane);
+    }
+  } else {
+    // ---- value wave: tokens t0 .. t0 + 31 row-wise, two halves of PF steps
+    const int w = lane % C::W, slot = lane / C::W;
+    WinStream<BITS, G> ws[2];
+    WinStep<BITS, G> x[2][WC::PF];
+    if (VALUES && busy) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        ws[hf].kr = a.k_res + bh * a.R * kD;
+        ws[hf].vr = a.v_res + bh * a.R * kD;
+        ws[hf].begin = t0 + 16 * hf;
+        ws[hf].end = min(a.R, ws[hf].begin + 16);
+        ws[hf].bytes = (uint32_t)ws[hf].end * (kD * 2);
+        ws[hf].lane_voff = (uint32_t)(slot * kD + w * C::CPW) * 2;
+#pragma unroll
+        for (int i = 0; i < WC::PF; ++i) ws[hf].issue_one(x[hf][i], i, 1);
+      }
+    }
+    if constexpr (K > 1) __syncthreads();  // the key waves' one barrier
+    if (VALUES && busy) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        flush_regs_values<BITS, G>(a, x[hf], WC::PF, tile0, ws[hf].begin, w, slot);
+    }
+  }
+  if (tid == 0 && ticket == (uint32_t)a.heads - 1) {
+    a.q_len[b] = ql + a.R;
+    a.r_len[b] = 0;
+    a.tickets[(size_t)b * kTicketStride] = 0u;
+  }
+  if (tid == 0 && ticket >= (uint32_t)a.heads) atomicOr(a.status, KIVI_ST_TICKETS);
 }
 
 // DEPTH: sub-chunks whose loads each wave keeps in flight.  2 when the grid
@@ -2393,6 +2535,21 @@ int launch_flush_t(const EncodeArgs &ea, dim3 grid, int P, hipStream_t st, bool 
                    : launch_flush_p<BITS, G, true>(ea, grid, P, st);
 }
 
+// The key-wave / value-wave flush: one workgroup per (sequence, head).
+template <int BITS, int G>
+int launch_flush_split(const EncodeArgs &ea, const kivi_dims &d, hipStream_t st, bool keys_only) {
+  const dim3 grid(d.heads, d.batch), blk(kDecodeThreads);
+  if (keys_only)
+    hipLaunchKernelGGL((flush_split_kernel<BITS, G, false>), grid, blk, 0, st, ea);
+  else
+    hipLaunchKernelGGL((flush_split_kernel<BITS, G, true>), grid, blk, 0, st, ea);
+  return (int)hipGetLastError();
+}
+
+#ifndef KIVI_FLUSH_SPLIT
+#define KIVI_FLUSH_SPLIT 1
+#endif
+
 int launch_flush_any(const kivi_dims &d, const kivi_cache &c, void *stream, bool keys_only) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   EncodeArgs ea = encode_args(d, c);
@@ -2401,6 +2558,16 @@ int launch_flush_any(const kivi_dims &d, const kivi_cache &c, void *stream, bool
   ea.src_tokens = d.residual;
   ea.prefill = 0;
   const int G = d.group, tiles = d.residual / G;
+  // B = 2 or 4, windows of at most 128 tokens: key waves and value waves
+  if (KIVI_FLUSH_SPLIT && d.bits != 8 && d.residual <= kFlushKeyWaves * kFlushTokensPerWave &&
+      kDecodeWaves == 2 * kFlushKeyWaves) {
+    if (d.bits == 2 && G == 32) return launch_flush_split<2, 32>(ea, d, st, keys_only);
+    if (d.bits == 2 && G == 64) return launch_flush_split<2, 64>(ea, d, st, keys_only);
+    if (d.bits == 2 && G == 128) return launch_flush_split<2, 128>(ea, d, st, keys_only);
+    if (d.bits == 4 && G == 32) return launch_flush_split<4, 32>(ea, d, st, keys_only);
+    if (d.bits == 4 && G == 64) return launch_flush_split<4, 64>(ea, d, st, keys_only);
+    if (d.bits == 4 && G == 128) return launch_flush_split<4, 128>(ea, d, st, keys_only);
+  }
   // tiles side by side per workgroup: the most of 4, 2, 1 that divides the
   // window's tiles and keeps to 128 tokens
   const int pmax = min(KIVI_FLUSH_P, 128 / G);
