@@ -25,7 +25,7 @@ Usage (from the repository root)::
         --workload NAME --copy-mb N --fetch-command CMD --write-command CMD \\
         -o OUT.md --json OUT.json
     python -m bit_kv_cache_decode_amd.rocprof_summary counters CSV --workload NAME \
-        --command CMD --codes N -o OUT.md
+        --command CMD --codes N [--kernel NAME] -o OUT.md
 """
 
 import argparse
@@ -38,8 +38,8 @@ import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SRC = os.path.join(HERE, "csrc", "kivi_kernels.hip")
-DECODE = "decode_kernel<2, 32, false, 2, false>"
-STEP = "decode_kernel<2, 32, true, 2, false>"
+DECODE = "decode_kernel<2, 32, false, 2, false, false>"
+STEP = "decode_kernel<2, 32, true, 2, false, false>"
 
 
 def kernel_hash():
@@ -165,10 +165,10 @@ def counters(args):
         n = len(next(iter(cs.values())))
         cells = [f"{sum(cs[c]) / len(cs[c]):.4g}" if cs.get(c) else "-" for c in names]
         lines.append(f"| {k} | {n} | " + " | ".join(cells) + " |")
-    dec = next((cs for k, cs in per.items() if DECODE in k), None)
+    dec = next((cs for k, cs in per.items() if args.kernel in k), None)
     if dec is not None and "SQ_INSTS_VALU" in dec and args.codes:
         valu = sum(dec["SQ_INSTS_VALU"]) / len(dec["SQ_INSTS_VALU"])
-        lines += ["", f"{DECODE}: {valu:.4g} wave-level VALU instructions per dispatch, "
+        lines += ["", f"{args.kernel}: {valu:.4g} wave-level VALU instructions per dispatch, "
                       f"{64 * valu / args.codes:.3f} lane-level VALU instructions per code "
                       f"({args.codes} codes per launch)."]
         if "SQ_WAVES" in dec:
@@ -202,6 +202,8 @@ def main():
     n.add_argument("--workload", required=True)
     n.add_argument("--command", required=True)
     n.add_argument("--codes", type=int, default=0)
+    n.add_argument("--kernel", default=DECODE,
+                   help="kernel (name substring) the per-code figure is for")
     n.add_argument("--note", default="")
     n.add_argument("-o", "--out", required=True)
     a = p.parse_args()

@@ -8,7 +8,7 @@ import os
 
 from bit_kv_cache_decode_amd import rocprof_summary as rs
 
-DEC = ("void kivi::(anonymous namespace)::decode_kernel<2, 32, false, 2, false>"
+DEC = ("void kivi::(anonymous namespace)::decode_kernel<2, 32, false, 2, false, false>"
        "(kivi::(anonymous namespace)::DecodeArgs, kivi::(anonymous namespace)::EncodeArgs)")
 MUL = ("void at::native::vectorized_elementwise_kernel<4, at::native::AUnaryFunctor<float, float, "
        "float, at::native::binary_internal::MulFunctor<float> >, std::array<char*, 2ul> >")
@@ -26,7 +26,7 @@ def _csv(path, rows):
 
 def test_short_names():
     assert rs.short_name(APPEND) == "append_kernel"
-    assert rs.short_name(DEC).startswith("void decode_kernel<2, 32, false, 2, false>(DecodeArgs")
+    assert rs.short_name(DEC).startswith("void decode_kernel<2, 32, false, 2, false, false>(DecodeArgs")
 
 
 def test_traffic_scales_by_the_reference_dispatch(tmp_path):
@@ -56,8 +56,13 @@ def test_counters_per_code_and_launch_shapes(tmp_path):
 
     class A:
         csv, workload, command, codes, note = c, "wl", "cmd", 6400, ""
+        kernel = rs.DECODE
         out = str(tmp_path / "c.md")
     rs.counters(A)
     text = open(A.out).read()
     assert "10.000 lane-level VALU instructions per code" in text   # 64 * 1000 / 6400
     assert "append_kernel [8 workgroups]" in text and "append_kernel [16 workgroups]" in text
+    # the per-code figure for another kernel, chosen by name
+    A.kernel, A.out = "append_kernel", str(tmp_path / "d.md")
+    rs.counters(A)
+    assert "append_kernel: 5 wave-level VALU instructions" in open(A.out).read()  # first shape
