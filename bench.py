@@ -594,6 +594,7 @@ def main():
 
     step_s = wall / K
     plain = args.rope is None and not args.sink
+    same_bits = w.bits == cfg.bits  # the counter runs are at the workload's own width
     one_kernel = kivi.decode_step_kernels(base.dims) == 1 and args.rope is None
     qheads = Bt * H
     dec_bytes = (wl.decode_bytes(w.q_len, r_start + 1, H, D, w.bits, cfg.group)
@@ -648,7 +649,7 @@ def main():
         "phased_matches_step": eager_ok,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": measured_traffic(cfg.name) if plain else None},
+                     "traffic": measured_traffic(cfg.name) if plain and same_bits else None},
     }
     if one_kernel and graph is not None:
         # the whole-step kernel itself: the step's algorithmic bytes over its
@@ -661,7 +662,8 @@ def main():
             "us": step_event_us, "algorithmic_bytes": sb,
             "GBps": sb / (step_event_us * 1e-6) / 1e9,
             "frac": sb / (step_event_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
-            "traffic": measured_traffic(cfg.name, "step_bytes_per_launch") if plain else None}
+            "traffic": (measured_traffic(cfg.name, "step_bytes_per_launch")
+                        if plain and same_bits else None)}
         if noflush_us is not None:
             nb = (wl.step_bytes(w.q_len, r_start - 2, H, D, w.bits, cfg.group, cfg.residual)
                   + Bt * H * args.sink * D * 2 * 2)

@@ -961,27 +961,40 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
 }
 
 // Cache policy of the decode's loads (the buffer instructions' auxiliary
-// bits: 1 sc0, 2 nt).  Every byte the decode reads is read once per call, so
-// the loads are marked non-temporal; measured against plain loads (HIP-graph
-// timings of 30 launches, alternating, one box): 7B layer 26.1 -> 24.3 us,
-// 13B layer 33.5 -> 30.7, ragged batch 64 203 -> 192, 131072 tokens at B=2
-// 78.9 -> 76.9, at B=4 unchanged; nt alone measured within noise of sc0 nt.
+// bits: 1 sc0, 2 nt).  At B = 2 every byte the decode reads is read once
+// per call, and non-temporal loads measured faster than plain ones
+// (HIP-graph timings of 30 launches, alternating, one box): 7B layer 26.1
+// -> 24.3 us, 13B layer 33.5 -> 30.7, ragged batch 64 203 -> 192, 131072
+// tokens 78.9 -> 76.9.  At B = 4 and 8 they measured slower (7B shape at
+// B = 8: 59.8 -> 91.8 us; at B = 4: 34.1 -> 35.4 us; sc0 alone and plain
+// loads within noise of each other), so those widths keep sc0 alone.
 #ifndef KIVI_DECODE_LOAD_AUX
 #define KIVI_DECODE_LOAD_AUX 3
 #endif
+#ifndef KIVI_DECODE_LOAD_AUX_WIDE
+#define KIVI_DECODE_LOAD_AUX_WIDE 1
+#endif
 constexpr int kLoadAux = KIVI_DECODE_LOAD_AUX;
 
-__device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, kLoadAux);
+template <int BITS>
+constexpr int load_aux() {
+  return BITS == 2 ? KIVI_DECODE_LOAD_AUX : KIVI_DECODE_LOAD_AUX_WIDE;
 }
 
+template <int AUX = kLoadAux>
+__device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, AUX);
+}
+
+template <int AUX = kLoadAux>
 __device__ __forceinline__ uint2 bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
-  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kLoadAux);
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, AUX);
   return make_uint2(v.x, v.y);
 }
 
+template <int AUX = kLoadAux>
 __device__ __forceinline__ uint4 bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kLoadAux);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -1076,6 +1089,7 @@ struct QuantStream {
   // `extra` (zero) is added to every per-lane offset: a zero computed from
   // another load's data makes these loads wait for that one.
   __device__ __forceinline__ void issue(SubLoads<BITS, G> &b, int c, uint32_t extra = 0u) const {
+    constexpr int A = load_aux<BITS>();
     const bool live = c < n;
     const uint32_t cb = live ? code_bytes : 0u, mb = live ? meta_bytes : 0u;
     const int T0 = live ? t0(c) : 0;
@@ -1087,21 +1101,21 @@ struct QuantStream {
 #pragma unroll
     for (int k = 0; k < C::NTS; ++k) {
       const uint32_t so = (uint32_t)max(0, min(tile0 + k, last_tile)) * (kD * 2);
-      b.ks[k] = bload1(rks, kmeta_voff + extra, so);
-      b.kz[k] = bload1(rkz, kmeta_voff + extra, so);
+      b.ks[k] = bload1<A>(rks, kmeta_voff + extra, so);
+      b.kz[k] = bload1<A>(rkz, kmeta_voff + extra, so);
     }
 #pragma unroll
     for (int j = 0; j < C::NL; ++j) {
       const int t = T0 + min(j, nvl - 1) * C::TPL;
-      b.kc[j] = bload4(rkc, code_voff + extra, (uint32_t)((t / G) * (C::W * G) + t % G) * 4);
+      b.kc[j] = bload4<A>(rkc, code_voff + extra, (uint32_t)((t / G) * (C::W * G) + t % G) * 4);
     }
 #pragma unroll
     for (int j = 0; j < C::NL; ++j) {
       const int t = T0 + min(j, nvl - 1) * C::TPL;
-      b.vc[j] = bload4(rvc, code_voff + extra, (uint32_t)((t / G) * (C::W * G) + t % G) * 4);
+      b.vc[j] = bload4<A>(rvc, code_voff + extra, (uint32_t)((t / G) * (C::W * G) + t % G) * 4);
       const uint32_t mo = (uint32_t)((t / G) * kD + t % G) * 2;
-      b.vs[j] = bload2(rvs, vmeta_voff + extra, mo);
-      b.vz[j] = bload2(rvz, vmeta_voff + extra, mo);
+      b.vs[j] = bload2<A>(rvs, vmeta_voff + extra, mo);
+      b.vz[j] = bload2<A>(rvz, vmeta_voff + extra, mo);
     }
   }
 };
@@ -1364,12 +1378,12 @@ struct WinStream {
     const uint32_t vo = lane_voff + (uint32_t)(begin + step * WC::STEP) * (kD * 2);
     if constexpr (WC::WIDE) {
 #pragma unroll
-      for (int v = 0; v < WC::NV; ++v) x.k[v] = bload4(rk, vo + 16 * v, 0);
+      for (int v = 0; v < WC::NV; ++v) x.k[v] = bload4<load_aux<BITS>()>(rk, vo + 16 * v, 0);
 #pragma unroll
-      for (int v = 0; v < WC::NV; ++v) x.v[v] = bload4(rv, vo + 16 * v, 0);
+      for (int v = 0; v < WC::NV; ++v) x.v[v] = bload4<load_aux<BITS>()>(rv, vo + 16 * v, 0);
     } else {
-      x.k[0] = bload2(rk, vo, 0);
-      x.v[0] = bload2(rv, vo, 0);
+      x.k[0] = bload2<load_aux<BITS>()>(rk, vo, 0);
+      x.v[0] = bload2<load_aux<BITS>()>(rv, vo, 0);
     }
   }
   // one operand only (0 keys, 1 values), 16-byte rows (WIDE)
