@@ -457,6 +457,51 @@ def test_decode_step_flush_in_kernel_matches_oracle(bits, G, R):
                 assert np.array_equal(got.view(np.uint8), enc[name].view(np.uint8)), (name, b, h)
 
 
+@pytest.mark.parametrize("bits,G,R", [
+    (2, 32, 128), (4, 32, 128), (2, 64, 128), (4, 64, 128), (2, 128, 128), (4, 128, 128),
+    (2, 32, 96), (2, 64, 64), (4, 32, 32),     # windows shorter than 128: idle key/value waves
+    (8, 32, 128), (2, 32, 256), (4, 64, 256),  # the tile-staging flush (B = 8, R > 128)
+])
+def test_flush_kernel_matches_oracle_across_shapes(bits, G, R):
+    """kivi_flush_residual alone on full windows of every shape its two
+    kernels take (key waves and value waves for B = 2, 4 and R <= 128, with
+    the key waves of a G > 32 tile merging through LDS; tile staging
+    otherwise): the new tiles equal the oracle's encoding of the window bit
+    for bit, the lengths move by R and nothing else is touched."""
+    rng = np.random.default_rng(2000 + 7 * bits + G + R)
+    B, H, D = 3, 5, 128
+    ql = 2 * G
+    n, cap = ql + R, ql + R + G
+    k = rng.standard_normal((B, H, n, D), np.float32)
+    k[..., ::7] *= 16.0                                 # outlier key channels
+    k[..., 5] += 40.0                                   # and one far from zero
+    k = k.astype(np.float16)
+    v = rng.standard_normal((B, H, n, D), np.float32).astype(np.float16)
+    c = kivi.KiviCache(B, H, D, bits, G, R, cap)
+    kivi.prefill(c, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                 torch.full((B,), n, dtype=torch.int32, device="cuda"),
+                 torch.full((B,), R, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    before = {name: t.cpu().numpy().copy() for name, t in c.buffers().items()}
+    kivi.flush_residual(c)
+    torch.cuda.synchronize()
+    after = {name: t.cpu().numpy() for name, t in c.buffers().items()}
+    assert c.status_bits() == 0
+    assert (after["q_len"] == ql + R).all() and (after["r_len"] == 0).all()
+    t0, t1 = ql // G, (ql + R) // G
+    for b in range(B):
+        for h in range(H):
+            enc = ocache.encode_tokens(k[b, h, ql:], v[b, h, ql:], G, bits)
+            for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+                got = after[name][b, h, t0:t1]
+                assert np.array_equal(got.view(np.uint8), enc[name].view(np.uint8)), (name, b, h)
+                # tiles before and after the window's are untouched
+                assert np.array_equal(after[name][b, h, :t0].view(np.uint8),
+                                      before[name][b, h, :t0].view(np.uint8)), (name, b, h)
+                assert np.array_equal(after[name][b, h, t1:].view(np.uint8),
+                                      before[name][b, h, t1:].view(np.uint8)), (name, b, h)
+
+
 @pytest.mark.parametrize("number", [2, 4])
 def test_decode_step_matches_three_calls_full_workloads(number):
     """The Llama-2-7B-shaped layer (every window fills and is flushed in the
