@@ -871,7 +871,9 @@ __device__ __forceinline__ uint32_t upper_pairs(uint32_t u) {
   return u >> (BITS == 2 ? 10 : 8);
 }
 
-// c0 + sum_i q[i] * code_i * 2^(e_i - 24) over the word's channels.
+// Adds q[i] * code_i * 2^(e_i - 24) over the word's channels to a0 (the
+// channels of the low halves) and a1 (the high halves'); a0 and a1 may be
+// the same accumulator.
 template <int BITS, int P = 0>
 __device__ __forceinline__ void dot_pairs(uint32_t u, uint32_t uh, const float *q, float &a0,
                                           float &a1) {
@@ -885,10 +887,13 @@ __device__ __forceinline__ void dot_pairs(uint32_t u, uint32_t uh, const float *
 }
 
 template <int BITS>
+// One chain per word: a lane scores four independent tokens at a time, which
+// is parallelism enough, and splitting a word's products over two chains
+// cost one more instruction per word (7B layer 25.2 -> 24.5-25.0 us).
 __device__ __forceinline__ float dot_word(uint32_t u, const float *q, float c0) {
-  float a0 = c0, a1 = 0.0f;
-  dot_pairs<BITS>(u, upper_pairs<BITS>(u), q, a0, a1);
-  return a0 + a1;
+  float a = c0;
+  dot_pairs<BITS>(u, upper_pairs<BITS>(u), q, a, a);
+  return a;
 }
 
 // acc[i] += pp * code_i * 2^(e_i - 24) over the word's channels.
