@@ -1123,6 +1123,41 @@ struct QuantStream {
       b.vz[j] = bload2<A>(rvz, vmeta_voff + extra, mo);
     }
   }
+
+  // Sub-chunk c's loads before the lengths are known (ql, last_tile and n
+  // unset), as if the cache held tokens up to the sub-chunk's end: when
+  // t0(c) + SUB <= ql these are exactly the loads of issue(b, c).  A
+  // sub-chunk that does not fit below cap reads zeros through zero-record
+  // descriptors, so no address leaves the (sequence, head) region.
+  __device__ __forceinline__ void issue_whole(SubLoads<BITS, G> &b, int c, int cap) const {
+    constexpr int A = load_aux<BITS>();
+    const bool fits = t0(c) + C::SUB <= cap;
+    const uint32_t cb = fits ? code_bytes : 0u, mb = fits ? meta_bytes : 0u;
+    const int T0 = fits ? t0(c) : 0;
+    const int tile0 = T0 / G;
+    const rsrc_t rks = make_rsrc(ks, mb), rkz = make_rsrc(kz, mb);
+    const rsrc_t rkc = make_rsrc(kc, cb), rvc = make_rsrc(vc, cb);
+    const rsrc_t rvs = make_rsrc(vs, mb), rvz = make_rsrc(vz, mb);
+#pragma unroll
+    for (int k = 0; k < C::NTS; ++k) {
+      const uint32_t so = (uint32_t)(tile0 + k) * (kD * 2);
+      b.ks[k] = bload1<A>(rks, kmeta_voff, so);
+      b.kz[k] = bload1<A>(rkz, kmeta_voff, so);
+    }
+#pragma unroll
+    for (int j = 0; j < C::NL; ++j) {
+      const int t = T0 + j * C::TPL;
+      b.kc[j] = bload4<A>(rkc, code_voff, (uint32_t)((t / G) * (C::W * G) + t % G) * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < C::NL; ++j) {
+      const int t = T0 + j * C::TPL;
+      b.vc[j] = bload4<A>(rvc, code_voff, (uint32_t)((t / G) * (C::W * G) + t % G) * 4);
+      const uint32_t mo = (uint32_t)((t / G) * kD + t % G) * 2;
+      b.vs[j] = bload2<A>(rvs, vmeta_voff, mo);
+      b.vz[j] = bload2<A>(rvz, vmeta_voff, mo);
+    }
+  }
 };
 
 // ------------------------------------------ decode: keys stored pre-rotation
@@ -1908,6 +1943,32 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
   const size_t bh = (size_t)b * a.heads + h;
   const int S = a.splits;
 
+  // ---- this wave's share: quantized sub-chunks gw, gw + nw, ... and
+  // window tokens [gw * win_per_wave, (gw + 1) * win_per_wave)
+  const int w = lane % C::W, slot = lane / C::W;
+  const int jg = (w * C::CPW) / G;
+  const size_t tps = (size_t)(a.cap / G);
+  QuantStream<BITS, G> qs;
+  qs.kc = a.k_codes + bh * tps * (C::W * G);
+  qs.vc = a.v_codes + bh * tps * (C::W * G);
+  qs.ks = a.k_scale + bh * tps * kD;
+  qs.kz = a.k_zero + bh * tps * kD;
+  qs.vs = a.v_scale + bh * tps * kD;
+  qs.vz = a.v_zero + bh * tps * kD;
+  qs.code_bytes = (uint32_t)(tps * (C::W * G) * 4);
+  qs.meta_bytes = (uint32_t)(tps * kD * 2);
+  qs.code_voff = (uint32_t)(w * G + 4 * slot) * 4;
+  qs.vmeta_voff = (uint32_t)(jg * G + 4 * slot) * 2;
+  qs.kmeta_voff = (uint32_t)lane * 4;
+  qs.gw = split * kDecodeWaves + wv;
+  qs.nw = kDecodeWaves * S;
+  const uint32_t qraw = bload1(make_rsrc(a.q + bh * kD, kD * 2), (uint32_t)lane * 4, 0);
+  // The plain decode requests its first sub-chunk before the lengths arrive
+  // (their load is a round trip at the start of every wave), as if the
+  // cache held it whole; it is requested again below when it does not.
+  SubLoads<BITS, G> ring[kDecodeDepth];
+  if constexpr (!FUSED) qs.issue_whole(ring[0], 0, a.cap);
+
   int ql, rl;
   if constexpr (FUSED) {
     // the lengths this kernel commits: thread 0 reads them and hands them to
@@ -1922,8 +1983,10 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
     ql = sm.lens[0];
     rl = sm.lens[1];
   } else {
+    // both loads out before either is waited for
     ql = a.q_len[b];
     rl = a.r_len[b];
+    __builtin_amdgcn_sched_barrier(0);
   }
   // Whole step (FUSED, one workgroup per (sequence, head)): append the new
   // token at window slot rnew, decode over the window including it, and
@@ -1960,7 +2023,9 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
       ticket = __hip_atomic_fetch_add(ea.tickets + (size_t)b * kTicketStride, 1u, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (!(ql >= 0 && ql <= a.cap && (ql % G) == 0 && rl >= 0 && rl <= a.R)) {
+  // (one test of both lengths, so that neither load waits on the other)
+  const bool lens_ok = (ql >= 0) & (ql <= a.cap) & ((ql % G) == 0) & (rl >= 0) & (rl <= a.R);
+  if (!lens_ok) {
     if (split == 0 && h == 0 && tid == 0) atomicOr(a.status, KIVI_ST_BAD_LENGTH);
     ql = 0;
     rl = 0;
@@ -1975,27 +2040,8 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
     qlq = (vqn / G) * G;
   }
 
-  // ---- this wave's share: quantized sub-chunks gw, gw + nw, ... and
-  // window tokens [gw * win_per_wave, (gw + 1) * win_per_wave)
-  const int w = lane % C::W, slot = lane / C::W;
-  const int jg = (w * C::CPW) / G;
-  const size_t tps = (size_t)(a.cap / G);
-  QuantStream<BITS, G> qs;
-  qs.kc = a.k_codes + bh * tps * (C::W * G);
-  qs.vc = a.v_codes + bh * tps * (C::W * G);
-  qs.ks = a.k_scale + bh * tps * kD;
-  qs.kz = a.k_zero + bh * tps * kD;
-  qs.vs = a.v_scale + bh * tps * kD;
-  qs.vz = a.v_zero + bh * tps * kD;
-  qs.code_bytes = (uint32_t)(tps * (C::W * G) * 4);
-  qs.meta_bytes = (uint32_t)(tps * kD * 2);
-  qs.code_voff = (uint32_t)(w * G + 4 * slot) * 4;
-  qs.vmeta_voff = (uint32_t)(jg * G + 4 * slot) * 2;
-  qs.kmeta_voff = (uint32_t)lane * 4;
   qs.ql = qlq;
   qs.last_tile = qlq / G - 1;
-  qs.gw = split * kDecodeWaves + wv;
-  qs.nw = kDecodeWaves * S;
   qs.n = qs.gw * C::SUB < qlq ? (qlq - qs.gw * C::SUB + qs.nw * C::SUB - 1) / (qs.nw * C::SUB) : 0;
 
   WinStream<BITS, G> ws;
@@ -2027,7 +2073,6 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
   bool early = false;
   if constexpr (FUSED) early = flush && a.win_per_wave <= 16;
 
-  const uint32_t qraw = bload1(make_rsrc(a.q + bh * kD, kD * 2), (uint32_t)lane * 4, 0);
   // FUSED: this lane's channels of the appended token, loaded unconditionally
   // (a load under a branch would make the compiler wait for every load in
   // flight after it)
@@ -2050,8 +2095,7 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
   // first sub-chunk would arrive no sooner than the others; with half the
   // request the waves start computing earlier (7B layer 25.4 -> 24.8 us,
   // 131072 tokens at B=2 80.3 -> 77.9 us, alternating runs on one box).
-  SubLoads<BITS, G> ring[kDecodeDepth];
-  qs.issue(ring[0], 0);
+  if (FUSED || qs.t0(0) + C::SUB > qs.ql) qs.issue(ring[0], 0);
 
   auto &stg = sm.u.wave[wv];
 #if KIVI_DECODE_PRIORITY == 2
