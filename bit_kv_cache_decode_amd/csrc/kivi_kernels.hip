@@ -2320,6 +2320,11 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
   wave_publish<C::CPW, C::W, C::W == 8>(sm.fin.acc[wv], sm.fin.bias[wv], sm.fin.m[wv],
                                          sm.fin.l[wv], st.m, st.l, st.acc, st.bias);
   __syncthreads();
+  // one workgroup per (sequence, head), plain decode: only the threads that
+  // write an output channel combine (the rest would only read LDS)
+  if constexpr (!FUSED) {
+    if (S == 1 && tid >= kD) return;
+  }
 
   // ---- combine the waves into the workgroup's state (channel tid).
   // Every published value is read first, then reduced: one LDS round trip
