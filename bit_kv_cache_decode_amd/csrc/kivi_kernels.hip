@@ -212,19 +212,58 @@ __device__ __forceinline__ float quant_code(float x, float mn, float s, float rs
 template <int BITS, int CPW>
 struct CodeWord {
   float lo = 0.0f, hi = 0.0f;
-  // code i of the word: channel value x of a group {mn, s, rs, nm}
-  __device__ __forceinline__ void add(int i, float x, float mn, float s, float rs, float nm) {
-    const float c = quant_code<BITS>(x, mn, s, rs, nm);
+  float dev = 0.0f;  // add_fast: the largest |q' - rint(q')| so far
+  __device__ __forceinline__ void put(int i, float c) {
     const float f = (float)(1u << (BITS * (i % (CPW / 2))));
     if (i < CPW / 2)
       lo = fmaf(c, f, lo);
     else
       hi = fmaf(c, f, hi);
   }
+  // code i of the word: channel value x of a group {mn, s, rs, nm}
+  __device__ __forceinline__ void add(int i, float x, float mn, float s, float rs, float nm) {
+    put(i, quant_code<BITS>(x, mn, s, rs, nm));
+  }
+  // code i by the fast product alone
+  __device__ __forceinline__ void add_fast(int i, float x, float rs, float nm) {
+    const float q = fmaf(x, rs, nm);
+    const float c = rintf(q);
+    dev = fmaxf(dev, fabsf(q - c));
+    put(i, c);
+  }
+  // every add_fast code is the one quant_code gives: none lies near a
+  // half-integer, and none is NaN (a NaN product makes its sum NaN, while
+  // fmaxf passes over it)
+  __device__ __forceinline__ bool fast_ok() const {
+    return dev <= near_half<BITS>() && lo == lo && hi == hi;
+  }
   __device__ __forceinline__ uint32_t word() const {
     return (uint32_t)lo | ((uint32_t)hi << (BITS * (CPW / 2)));
   }
 };
+
+// One code word of CPW channel values x(i) with groups par(i) = {mn, s,
+// rs, nm}: every code by the fast product, and the word once more code by
+// code (quant_code) only when one of them needs the division.  One test
+// per word instead of a branch per code.
+template <int BITS, int CPW, typename X, typename P>
+__device__ __forceinline__ uint32_t encode_word(X x, P par) {
+  CodeWord<BITS, CPW> fw;
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const float4 p = par(i);
+    fw.add_fast(i, x(i), p.z, p.w);
+  }
+  if (!fw.fast_ok()) {
+    fw = CodeWord<BITS, CPW>();
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const float4 p = par(i);
+      fw.add(i, x(i), p.x, p.y, p.z, p.w);
+    }
+  }
+  return fw.word();
+}
 
 #pragma clang fp contract(on)
 
@@ -347,15 +386,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     const int w = wi / G, t = wi % G;
     const int gi = ((w * CPW) / G) * G + t;
     const float4 vp = vpar[gi];
-    CodeWord<BITS, CPW> fk, fv;
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int c = w * CPW + i;
-      const float4 kp = kpar[c];
-      fk.add(i, (float)xk[t][c], kp.x, kp.y, kp.z, kp.w);
-      fv.add(i, (float)xv[t][c], vp.x, vp.y, vp.z, vp.w);
-    }
-    const uint32_t wk = fk.word(), wv = fv.word();
+    const uint32_t wk = encode_word<BITS, CPW>([&](int i) { return (float)xk[t][w * CPW + i]; },
+                                               [&](int i) { return kpar[w * CPW + i]; });
+    const uint32_t wv = encode_word<BITS, CPW>([&](int i) { return (float)xv[t][w * CPW + i]; },
+                                               [&](int) { return vp; });
     a.k_codes[ktile * (W * G) + wi] = wk;
     a.v_codes[ktile * (W * G) + wi] = wv;
   }
@@ -497,6 +531,8 @@ __device__ __forceinline__ void flush_window(const EncodeArgs &a, size_t bh, int
             x[q] = (q & 1) ? (float)x2.y : (float)x2.x;
           }
         }
+        // (code by code: the word-level test of encode_word holds more
+        // registers, which measured slower here at B = 8)
         CodeWord<BITS, CPW> fw;
         if (op == 0) {
 #pragma unroll
@@ -1601,17 +1637,12 @@ __device__ __forceinline__ FusedFlushSmem<BITS, G> &fused_flush_smem() {
 template <int BITS, int NV, typename Par>
 __device__ __forceinline__ uint32_t encode_lane_word(const uint4 (&x)[NV], Par par) {
   constexpr int CPW = 8 * NV;
-  CodeWord<BITS, CPW> fw;
-#pragma unroll
-  for (int v = 0; v < NV; ++v)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const half2_t h = __builtin_bit_cast(half2_t, u4_get(x[v], e));
-      const float4 p0 = par(8 * v + 2 * e), p1 = par(8 * v + 2 * e + 1);
-      fw.add(8 * v + 2 * e, (float)h.x, p0.x, p0.y, p0.z, p0.w);
-      fw.add(8 * v + 2 * e + 1, (float)h.y, p1.x, p1.y, p1.z, p1.w);
-    }
-  return fw.word();
+  return encode_word<BITS, CPW>(
+      [&](int i) {
+        const half2_t h = __builtin_bit_cast(half2_t, u4_get(x[i / 8], (i % 8) / 2));
+        return (i & 1) ? (float)h.y : (float)h.x;
+      },
+      par);
 }
 
 // Before the stream: the lane's key partials to LDS.
@@ -1867,18 +1898,34 @@ __global__ __launch_bounds__(kDecodeThreads, 3 * kDecodeWavesPerSimd) void flush
     for (int c = 0; c < NREG; ++c) {
       // tokens c TPR .. c TPR + TPR - 1: 2B bits each, in two fp32 sums of
       // TPR / 2 tokens (16-bit integers, exact), then one register
-      float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-      for (int k = 0; k < TPR; ++k) {
-        const half2_t x = __builtin_bit_cast(half2_t, xr[c * TPR + k]);
-        const float c0 = quant_code<BITS>((float)x.x, g0.mn, g0.s, g0.rs, g0.nm);
-        const float c1 = quant_code<BITS>((float)x.y, g1.mn, g1.s, g1.rs, g1.nm);
+      // (every code by the fast product first, and the register once more
+      // code by code only when one of them needs the division, as
+      // encode_word does)
+      float lo = 0.0f, hi = 0.0f, dev = 0.0f;
+      auto put = [&](int k, float c0, float c1) {
         const float f = (float)(1u << (2 * BITS * (k % (TPR / 2))));
         const float pair = fmaf(c1, (float)(1 << BITS), c0);
         if (k < TPR / 2)
           lo = fmaf(pair, f, lo);
         else
           hi = fmaf(pair, f, hi);
+      };
+#pragma unroll
+      for (int k = 0; k < TPR; ++k) {
+        const half2_t x = __builtin_bit_cast(half2_t, xr[c * TPR + k]);
+        const float q0 = fmaf((float)x.x, g0.rs, g0.nm), q1 = fmaf((float)x.y, g1.rs, g1.nm);
+        const float c0 = rintf(q0), c1 = rintf(q1);
+        dev = fmaxf(dev, fmaxf(fabsf(q0 - c0), fabsf(q1 - c1)));
+        put(k, c0, c1);
+      }
+      if (!(dev <= near_half<BITS>() && lo == lo && hi == hi)) {
+        lo = hi = 0.0f;
+#pragma unroll
+        for (int k = 0; k < TPR; ++k) {
+          const half2_t x = __builtin_bit_cast(half2_t, xr[c * TPR + k]);
+          put(k, quant_code<BITS>((float)x.x, g0.mn, g0.s, g0.rs, g0.nm),
+              quant_code<BITS>((float)x.y, g1.mn, g1.s, g1.rs, g1.nm));
+        }
       }
       const uint32_t reg = (uint32_t)lo | ((uint32_t)hi << 16);
       dst[c * TPR] = transpose_words<BITS>(reg, lane);
