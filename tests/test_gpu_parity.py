@@ -324,11 +324,10 @@ def _near_tie_values(bits, rng, pairs=200):
     return out
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
-def test_quantizer_near_ties_bit_exact_on_both_encoders(bits):
-    """Keys and values built from exact and near rounding ties: the prefill
-    encoder and the flush kernel both match the oracle bit for bit."""
-    rng = np.random.default_rng(77 + bits)
+def _near_tie_kv(bits, rng):
+    """Keys and values of 2 heads x 128 tokens whose every group (key:
+    channel over 32 tokens; value: token over 32 channels) holds its
+    minimum, its maximum and 30 values at or near a rounding tie."""
     cases = _near_tie_values(bits, rng)
     assert sum(len(c[2]) for c in cases) > 300
     G, R, D, H = 32, 128, 128, 2
@@ -345,6 +344,24 @@ def test_quantizer_near_ties_bit_exact_on_both_encoders(bits):
                 mn, mx, near = cases[rng.integers(len(cases))]
                 row = np.concatenate([[mn, mx], rng.choice(near, size=G - 2)]).astype(np.float16)
                 v[0, h, t, j * G:(j + 1) * G] = rng.permutation(row)
+    return k, v, G, R, D, H
+
+
+def _assert_tiles_match_oracle(caches, k, v, G, R, H, bits):
+    for h in range(H):
+        enc = ocache.encode_tokens(k[0, h], v[0, h], G, bits)
+        for c in caches:
+            for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+                got = getattr(c, name)[0, h, :R // G].cpu().numpy()
+                assert np.array_equal(got.view(np.uint8), enc[name].view(np.uint8)), name
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_quantizer_near_ties_bit_exact_on_both_encoders(bits):
+    """Keys and values built from exact and near rounding ties: the prefill
+    encoder and the flush kernel both match the oracle bit for bit."""
+    rng = np.random.default_rng(77 + bits)
+    k, v, G, R, D, H = _near_tie_kv(bits, rng)
     kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
     lens = torch.tensor([R], dtype=torch.int32, device="cuda")
     pre = kivi.KiviCache(1, H, D, bits, G, R, 256)
@@ -354,12 +371,28 @@ def test_quantizer_near_ties_bit_exact_on_both_encoders(bits):
     kivi.flush_residual(fl)
     torch.cuda.synchronize()
     assert pre.q_len.item() == R and fl.q_len.item() == R and fl.r_len.item() == 0
-    for h in range(H):
-        enc = ocache.encode_tokens(k[0, h], v[0, h], G, bits)
-        for c in (pre, fl):
-            for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
-                got = getattr(c, name)[0, h, :R // G].cpu().numpy()
-                assert np.array_equal(got.view(np.uint8), enc[name].view(np.uint8)), name
+    _assert_tiles_match_oracle((pre, fl), k, v, G, R, H, bits)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_quantizer_near_ties_bit_exact_through_decode_step(bits):
+    """The same near-tie keys and values flushed by kivi_decode_step: a
+    window of R - 1 tokens, then a step that appends token R - 1 and so
+    fills it (at B = 2 and 4 one kernel, which quantizes the window from
+    its registers; at B = 8 the three kernels).  Bit for bit the oracle's."""
+    rng = np.random.default_rng(77 + bits)
+    k, v, G, R, D, H = _near_tie_kv(bits, rng)
+    kt, vt = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    st = kivi.KiviCache(1, H, D, bits, G, R, 256)
+    n = torch.tensor([R - 1], dtype=torch.int32, device="cuda")
+    kivi.prefill(st, kt, vt, n, n)
+    q = torch.from_numpy(rng.standard_normal((1, H, D)).astype(np.float16)).cuda()
+    kivi.decode_step(st, kt[:, :, R - 1].contiguous(), vt[:, :, R - 1].contiguous(), q, 0.088)
+    torch.cuda.synchronize()
+    if bits != 8:
+        assert kivi.decode_step_kernels(st.dims) == 1
+    assert st.q_len.item() == R and st.r_len.item() == 0 and st.status_bits() == 0
+    _assert_tiles_match_oracle((st,), k, v, G, R, H, bits)
 
 
 def _state(c):
