@@ -1963,6 +1963,117 @@ __global__ __launch_bounds__(kDecodeThreads, 3 * kDecodeWavesPerSimd) void flush
   if (tid == 0 && ticket >= (uint32_t)a.heads) atomicOr(a.status, KIVI_ST_TICKETS);
 }
 
+// ---- the end of a decode workgroup
+// Its waves' published states combined into the workgroup's (channel tid):
+// the maximum M of the log2 scores, the softmax sum L and the output
+// channel's weighted sum, both relative to M.  Every published value is
+// read first, then reduced: one LDS round trip instead of one per wave.
+// (Every wave published finite sums, zeros without tokens, so all can be
+// read before any test.)
+struct WgState {
+  float M, L, acc;
+};
+
+template <int BITS, int G, typename Fin>
+__device__ __forceinline__ WgState combine_waves(const Fin &fin, int tid) {
+  using C = DecCfg<BITS, G>;
+  constexpr int NR = publish_rows<C::W>();
+  float fm[kDecodeWaves], fl[kDecodeWaves];
+  float ra[kDecodeWaves][NR], rb[kDecodeWaves][NR];
+#pragma unroll
+  for (int x = 0; x < kDecodeWaves; ++x) {
+    fm[x] = fin.m[x];
+    fl[x] = fin.l[x];
+  }
+  const int ch = tid < kD ? tid : 0;
+#pragma unroll
+  for (int x = 0; x < kDecodeWaves; ++x)
+#pragma unroll
+    for (int y = 0; y < NR; ++y) {
+      ra[x][y] = fin.acc[x][y][ch];
+      rb[x][y] = fin.bias[x][y][ch / C::CPW];
+    }
+  WgState w{-INFINITY, 0.0f, 0.0f};
+#pragma unroll
+  for (int x = 0; x < kDecodeWaves; ++x)
+    if (fl[x] > 0.0f) w.M = fmaxf(w.M, fm[x]);
+  if (w.M != -INFINITY) {
+    const float cf = code_factor<BITS>(ch % C::CPW);
+#pragma unroll
+    for (int x = 0; x < kDecodeWaves; ++x) {
+      const float ex = fl[x] > 0.0f ? exp2_fast(fm[x] - w.M) : 0.0f;
+      w.L += ex * fl[x];
+      float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+      for (int y = 0; y < NR; ++y) {
+        sa += ra[x][y];
+        sb += rb[x][y];
+      }
+      w.acc += ex * fmaf(sa, cf, sb);
+    }
+  }
+  return w;
+}
+
+// Several workgroups per (sequence, head): publish this one's state, take a
+// ticket, and in the workgroup with the last ticket merge all partials.
+template <typename Sm>
+__device__ __forceinline__ void finish_splits(const DecodeArgs &a, Sm &sm, const WgState &wg,
+                                              size_t bh, int split, int S, int tid) {
+  const float M = wg.M, L = wg.L, acc_out = wg.acc;
+  // The partial state is written with device-scope atomic stores, which the
+  // gfx950 caches keep coherent across XCDs by themselves (they write
+  // through to the device coherence point).  Waiting for their completion,
+  // then a barrier, then a device-scope ticket, orders them before the
+  // ticket without a device-wide release fence, whose L2 write-back and
+  // invalidate would otherwise run once per wave on a shared L2.
+  float *P = a.part + (bh * S + split) * (size_t)a.part_stride;
+  if (L > 0.0f && tid < kD) store_agent(P + kPartHead + tid, acc_out);
+  if (tid == 0) {
+    store_agent(P, M);
+    store_agent(P + 1, L);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (tid == 0)
+    sm.ticket = (int)__hip_atomic_fetch_add(a.tickets + bh * kTicketStride, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (sm.ticket != S - 1) {
+    // a ticket at or past the split count: the workspace's counter did not
+    // start at zero (workspace not initialised), so no workgroup can tell it
+    // is the last; the caller is told through the status word
+    if (tid == 0 && (uint32_t)sm.ticket >= (uint32_t)S) atomicOr(a.status, KIVI_ST_TICKETS);
+    return;
+  }
+
+  // ---- last workgroup of this (sequence, head): merge all partials, read
+  // with device-scope atomic loads (coherent with the stores above)
+  const float *P0 = a.part + bh * S * (size_t)a.part_stride;
+  if (tid < S) {
+    sm.u.mg.m[tid] = load_agent(P0 + (size_t)tid * a.part_stride);
+    sm.u.mg.l[tid] = load_agent(P0 + (size_t)tid * a.part_stride + 1);
+  }
+  __syncthreads();
+  if (tid < kD) {
+    float mx = -INFINITY;
+    for (int s = 0; s < S; ++s)
+      if (sm.u.mg.l[s] > 0.0f) mx = fmaxf(mx, sm.u.mg.m[s]);
+    float lsum = 0.0f, macc = 0.0f;
+    for (int s = 0; s < S; ++s) {
+      const float e = sm.u.mg.l[s] > 0.0f ? exp2_fast(sm.u.mg.m[s] - mx) : 0.0f;
+      lsum += e * sm.u.mg.l[s];
+      if (e != 0.0f)
+        macc = fmaf(e, load_agent(P0 + (size_t)s * a.part_stride + kPartHead + tid), macc);
+    }
+    a.out[bh * kD + tid] = lsum > 0.0f ? macc / lsum : 0.0f;
+  }
+  if (tid == 0)
+    __hip_atomic_store(a.tickets + bh * kTicketStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // DEPTH: sub-chunks whose loads each wave keeps in flight.  2 when the grid
 // is one workgroup per compute unit; 1 when it is larger, where the smaller
 // register footprint lets three workgroups share a compute unit (measured on
@@ -2373,46 +2484,8 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
     if (S == 1 && tid >= kD) return;
   }
 
-  // ---- combine the waves into the workgroup's state (channel tid).
-  // Every published value is read first, then reduced: one LDS round trip
-  // instead of one per wave.  (Every wave published finite sums, zeros
-  // without tokens, so all can be read before any test.)
-  constexpr int NR = publish_rows<C::W>();
-  float fm[kDecodeWaves], fl[kDecodeWaves];
-  float ra[kDecodeWaves][NR], rb[kDecodeWaves][NR];
-#pragma unroll
-  for (int x = 0; x < kDecodeWaves; ++x) {
-    fm[x] = sm.fin.m[x];
-    fl[x] = sm.fin.l[x];
-  }
-  const int ch = tid < kD ? tid : 0;
-#pragma unroll
-  for (int x = 0; x < kDecodeWaves; ++x)
-#pragma unroll
-    for (int y = 0; y < NR; ++y) {
-      ra[x][y] = sm.fin.acc[x][y][ch];
-      rb[x][y] = sm.fin.bias[x][y][ch / C::CPW];
-    }
-  float M = -INFINITY;
-#pragma unroll
-  for (int x = 0; x < kDecodeWaves; ++x)
-    if (fl[x] > 0.0f) M = fmaxf(M, fm[x]);
-  float L = 0.0f, acc_out = 0.0f;
-  if (M != -INFINITY) {
-    const float cf = code_factor<BITS>(ch % C::CPW);
-#pragma unroll
-    for (int x = 0; x < kDecodeWaves; ++x) {
-      const float ex = fl[x] > 0.0f ? exp2_fast(fm[x] - M) : 0.0f;
-      L += ex * fl[x];
-      float sa = 0.0f, sb = 0.0f;
-#pragma unroll
-      for (int y = 0; y < NR; ++y) {
-        sa += ra[x][y];
-        sb += rb[x][y];
-      }
-      acc_out += ex * fmaf(sa, cf, sb);
-    }
-  }
+  const WgState wg = combine_waves<BITS, G>(sm.fin, tid);
+  const float L = wg.L, acc_out = wg.acc;
   if (S == 1) {  // the workgroup saw every token: finish here
     if (tid < kD) a.out[bh * kD + tid] = L > 0.0f ? acc_out / L : 0.0f;
     if constexpr (FUSED) {
@@ -2441,58 +2514,443 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
     return;
   }
 
-  // ---- publish the partial state and take a ticket
-  // The partial state is written with device-scope atomic stores, which the
-  // gfx950 caches keep coherent across XCDs by themselves (they write
-  // through to the device coherence point).  Waiting for their completion,
-  // then a barrier, then a device-scope ticket, orders them before the
-  // ticket without a device-wide release fence, whose L2 write-back and
-  // invalidate would otherwise run once per wave on a shared L2.
-  float *P = a.part + (bh * S + split) * (size_t)a.part_stride;
-  if (L > 0.0f && tid < kD) store_agent(P + kPartHead + tid, acc_out);
-  if (tid == 0) {
-    store_agent(P, M);
-    store_agent(P + 1, L);
-  }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  if (tid == 0)
-    sm.ticket = (int)__hip_atomic_fetch_add(a.tickets + bh * kTicketStride, 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (sm.ticket != S - 1) {
-    // a ticket at or past the split count: the workspace's counter did not
-    // start at zero (workspace not initialised), so no workgroup can tell it
-    // is the last; the caller is told through the status word
-    if (tid == 0 && (uint32_t)sm.ticket >= (uint32_t)S) atomicOr(a.status, KIVI_ST_TICKETS);
-    return;
+  finish_splits(a, sm, wg, bh, split, S, tid);
+}
+
+// --------------------------------------------- decode: two words per lane
+// The plain decode at B = 2 and 4 with two sub-chunks in flight and no sink
+// tokens, in a second lane layout.  decode_kernel's lane holds one code word
+// of each of 8 tokens per sub-chunk; here lane (q, p) holds words 2p and
+// 2p + 1 (channels 2p CPW .. 2p CPW + 2 CPW - 1) of the 4 tokens 4q .. 4q + 3.
+// The arithmetic per code is the same; what is done once per token and lane
+// (the score's reduction over the token's lanes, its exponential, the
+// softmax sum, the value group's step and zero-point products) is done for
+// half as many tokens.  The bytes read, the loads' policy, the sub-chunk
+// order, the window, the combine and the split merge are decode_kernel's;
+// the window pass takes one token per quad of lanes.
+template <int BITS, int G>
+struct PairCfg {
+  using C = DecCfg<BITS, G>;
+  static constexpr int PW = C::W / 2;     // lanes per token
+  static constexpr int NQ = 64 / PW;      // token quads per sub-chunk (= window tokens per step)
+  static constexpr int CPL = 2 * C::CPW;  // channels per lane
+  static constexpr int NVW = CPL / 8;     // 16-byte fp16 vectors per lane and window row
+  static constexpr int PFW = 16 / NQ;     // window steps loaded after the stream (16 tokens)
+  static_assert(BITS == 2 || BITS == 4, "two code words per lane");
+  static_assert(4 * NQ == C::SUB, "one token quad per lane group fills a sub-chunk");
+  static_assert(C::SUB % G == 0 || G % C::SUB == 0, "sub-chunks and tiles nest");
+};
+
+// Registers holding every load of one sub-chunk of one wave.
+template <int BITS, int G>
+struct PairLoads {
+  using C = DecCfg<BITS, G>;
+  uint4 kc[2], vc[2];               // words 2p and 2p + 1 of the lane's 4 tokens
+  uint32_t ks[C::NTS], kz[C::NTS];  // key groups of 2 channels of each touched tile
+  uint2 vs, vz;                     // the lane's value group for its 4 tokens
+};
+
+template <int BITS, int G>
+struct PairStream {
+  using C = DecCfg<BITS, G>;
+  const void *kc, *vc, *ks, *kz, *vs, *vz;  // (sequence, head) regions
+  uint32_t code_bytes, meta_bytes;          // region sizes
+  // per-lane byte offsets of word 2p of the lane's first token, and of its
+  // value group, within a sub-chunk; the "c" pair moves a lane past the
+  // first tile back into it (a last sub-chunk of one valid tile, G < SUB)
+  uint32_t code_voff, code_voffc, vmeta_voff, vmeta_voffc, kmeta_voff;
+  int ql, last_tile, gw, nw, n;
+
+  __device__ __forceinline__ int t0(int c) const { return (gw + c * nw) * C::SUB; }
+
+  // Every load of sub-chunk c (zero-record descriptors for c >= n).  In a
+  // sub-chunk that ends past ql, the lanes whose tokens lie past it load the
+  // first tile's tokens instead (valid data; their scores are masked).
+  __device__ __forceinline__ void issue(PairLoads<BITS, G> &b, int c, uint32_t extra = 0u) const {
+    constexpr int A = load_aux<BITS>();
+    const bool live = c < n;
+    const uint32_t cb = live ? code_bytes : 0u, mb = live ? meta_bytes : 0u;
+    const int T0 = live ? t0(c) : 0;
+    const bool whole = T0 + C::SUB <= ql;
+    const int tile0 = T0 / G;
+    const rsrc_t rks = make_rsrc(ks, mb), rkz = make_rsrc(kz, mb);
+    const rsrc_t rkc = make_rsrc(kc, cb), rvc = make_rsrc(vc, cb);
+    const rsrc_t rvs = make_rsrc(vs, mb), rvz = make_rsrc(vz, mb);
+#pragma unroll
+    for (int k = 0; k < C::NTS; ++k) {
+      const uint32_t so = (uint32_t)max(0, min(tile0 + k, last_tile)) * (kD * 2);
+      b.ks[k] = bload1<A>(rks, kmeta_voff + extra, so);
+      b.kz[k] = bload1<A>(rkz, kmeta_voff + extra, so);
+    }
+    const uint32_t cv = (whole ? code_voff : code_voffc) + extra;
+    const uint32_t cs = (uint32_t)(tile0 * (C::W * G) + T0 % G) * 4;
+    b.kc[0] = bload4<A>(rkc, cv, cs);
+    b.kc[1] = bload4<A>(rkc, cv + G * 4, cs);
+    b.vc[0] = bload4<A>(rvc, cv, cs);
+    b.vc[1] = bload4<A>(rvc, cv + G * 4, cs);
+    const uint32_t mv = (whole ? vmeta_voff : vmeta_voffc) + extra;
+    const uint32_t ms = (uint32_t)(tile0 * kD + T0 % G) * 2;
+    b.vs = bload2<A>(rvs, mv, ms);
+    b.vz = bload2<A>(rvz, mv, ms);
   }
 
-  // ---- last workgroup of this (sequence, head): merge all partials, read
-  // with device-scope atomic loads (coherent with the stores above)
-  const float *P0 = a.part + bh * S * (size_t)a.part_stride;
-  if (tid < S) {
-    sm.u.mg.m[tid] = load_agent(P0 + (size_t)tid * a.part_stride);
-    sm.u.mg.l[tid] = load_agent(P0 + (size_t)tid * a.part_stride + 1);
-  }
-  __syncthreads();
-  if (tid < kD) {
-    float mx = -INFINITY;
-    for (int s = 0; s < S; ++s)
-      if (sm.u.mg.l[s] > 0.0f) mx = fmaxf(mx, sm.u.mg.m[s]);
-    float lsum = 0.0f, macc = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float e = sm.u.mg.l[s] > 0.0f ? exp2_fast(sm.u.mg.m[s] - mx) : 0.0f;
-      lsum += e * sm.u.mg.l[s];
-      if (e != 0.0f)
-        macc = fmaf(e, load_agent(P0 + (size_t)s * a.part_stride + kPartHead + tid), macc);
+  // Sub-chunk c before the lengths are known, as QuantStream::issue_whole:
+  // the loads of issue(b, c) whenever t0(c) + SUB <= ql; zeros (zero-record
+  // descriptors) when the sub-chunk does not fit below cap.
+  __device__ __forceinline__ void issue_whole(PairLoads<BITS, G> &b, int c, int cap) const {
+    constexpr int A = load_aux<BITS>();
+    const bool fits = t0(c) + C::SUB <= cap;
+    const uint32_t cb = fits ? code_bytes : 0u, mb = fits ? meta_bytes : 0u;
+    const int T0 = fits ? t0(c) : 0;
+    const int tile0 = T0 / G;
+    const rsrc_t rks = make_rsrc(ks, mb), rkz = make_rsrc(kz, mb);
+    const rsrc_t rkc = make_rsrc(kc, cb), rvc = make_rsrc(vc, cb);
+    const rsrc_t rvs = make_rsrc(vs, mb), rvz = make_rsrc(vz, mb);
+#pragma unroll
+    for (int k = 0; k < C::NTS; ++k) {
+      const uint32_t so = (uint32_t)(tile0 + k) * (kD * 2);
+      b.ks[k] = bload1<A>(rks, kmeta_voff, so);
+      b.kz[k] = bload1<A>(rkz, kmeta_voff, so);
     }
-    a.out[bh * kD + tid] = lsum > 0.0f ? macc / lsum : 0.0f;
+    const uint32_t cs = (uint32_t)(tile0 * (C::W * G) + T0 % G) * 4;
+    b.kc[0] = bload4<A>(rkc, code_voff, cs);
+    b.kc[1] = bload4<A>(rkc, code_voff + G * 4, cs);
+    b.vc[0] = bload4<A>(rvc, code_voff, cs);
+    b.vc[1] = bload4<A>(rvc, code_voff + G * 4, cs);
+    const uint32_t ms = (uint32_t)(tile0 * kD + T0 % G) * 2;
+    b.vs = bload2<A>(rvs, vmeta_voff, ms);
+    b.vz = bload2<A>(rvz, vmeta_voff, ms);
   }
-  if (tid == 0)
-    __hip_atomic_store(a.tickets + bh * kTicketStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+};
+
+// One sub-chunk: key multipliers staged as decode_kernel does (the lane's
+// two channels of every touched tile), then the lane's 4 scores (both words
+// in one accumulation chain, reduced over the token's PW lanes), the online
+// softmax, and the weighted value sums of both words.  MASK: the sub-chunk
+// may end past ql (its lanes past ql score -inf and add nothing).
+template <int BITS, int G, bool MASK>
+__device__ __forceinline__ void process_pair(
+    const PairLoads<BITS, G> &b, int T0, int ql, int lane, float qf0, float qf1, float qs0,
+    float qs1, float (&qp)[DecCfg<BITS, G>::NTS][DecCfg<BITS, G>::W * DecCfg<BITS, G>::QPW],
+    float (&cz)[DecCfg<BITS, G>::NTS][DecCfg<BITS, G>::W], LaneState<PairCfg<BITS, G>::CPL> &st) {
+  using C = DecCfg<BITS, G>;
+  using P = PairCfg<BITS, G>;
+  const int d0 = 2 * lane;
+  const int qpo = (d0 / C::CPW) * C::QPW + d0 % C::CPW;
+#pragma unroll
+  for (int k = 0; k < C::NTS; ++k) {
+    qp[k][qpo] = mix_lo(qf0, b.ks[k], 0.0f);
+    qp[k][qpo + 1] = mix_hi(qf1, b.ks[k], 0.0f);
+    float zc = mix_lo(qs0, b.kz[k], mix_hi(qs1, b.kz[k], 0.0f));
+    zc = lane_group_sum<C::CPW / 2>(zc);
+    if ((lane % (C::CPW / 2)) == 0) cz[k][lane / (C::CPW / 2)] = zc;
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  const int p = lane % P::PW, q = lane / P::PW;
+  const int k = ((T0 % G) + 4 * q) / G;  // the lane's tile within the sub-chunk
+  // word 2p of the 4 tokens first, then word 2p + 1: each half waits only
+  // for its own load
+  float s[4];
+  const float c0 = cz[k][2 * p] + cz[k][2 * p + 1];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float qv[C::CPW];
+#pragma unroll
+    for (int i = 0; i < C::CPW; i += 4) {
+      const float4 t4 = *reinterpret_cast<const float4 *>(&qp[k][(2 * p + h) * C::QPW + i]);
+      qv[i] = t4.x;
+      qv[i + 1] = t4.y;
+      qv[i + 2] = t4.z;
+      qv[i + 3] = t4.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = dot_word<BITS>(u4_get(b.kc[h], i), qv, h == 0 ? c0 : s[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = lane_group_sum<P::PW>(s[i]);
+  __builtin_amdgcn_wave_barrier();
+  [[maybe_unused]] bool ok = true;
+  if constexpr (MASK) {
+    ok = T0 + 4 * q < ql;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = ok ? s[i] : -INFINITY;
+  }
+
+  update_max<P::CPL, 4>(st, s);
+
+  float pp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float pr = exp2_fast(s[i] - st.m);
+    if constexpr (MASK) pr = ok ? pr : 0.0f;  // (-inf - -inf is NaN)
+    st.l += pr;
+    const uint32_t sw = i < 2 ? b.vs.x : b.vs.y;
+    const uint32_t zw = i < 2 ? b.vz.x : b.vz.y;
+    pp[i] = (i & 1) ? mix_hi(pr, sw, 0.0f) : mix_lo(pr, sw, 0.0f);
+    st.bias = (i & 1) ? mix_hi(pr, zw, st.bias) : mix_lo(pr, zw, st.bias);
+  }
+  // word 2p of the 4 tokens, then word 2p + 1
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = u4_get(b.vc[h], i);
+      axpy_pairs<BITS>(u, upper_pairs<BITS>(u), pp[i], st.acc + h * C::CPW);
+    }
+}
+
+// Window rows in the pair layout: lane (q, p) takes channels 2p CPW ..
+// 2p CPW + 2 CPW - 1 of token begin + step NQ + q.
+template <int BITS, int G>
+struct PairWinStep {
+  uint4 k[PairCfg<BITS, G>::NVW], v[PairCfg<BITS, G>::NVW];
+};
+
+template <int BITS, int G>
+struct PairWin {
+  using P = PairCfg<BITS, G>;
+  const void *kr, *vr;  // (sequence, head) window rows
+  uint32_t bytes;       // rows at or past this wave's end read as 0
+  uint32_t lane_voff;   // byte offset of the lane's channels in its token row
+  int begin, end;
+
+  __device__ __forceinline__ void issue(PairWinStep<BITS, G> &x, int step) const {
+    const rsrc_t rk = make_rsrc(kr, bytes), rv = make_rsrc(vr, bytes);
+    const uint32_t vo = lane_voff + (uint32_t)(begin + step * P::NQ) * (kD * 2);
+#pragma unroll
+    for (int v = 0; v < P::NVW; ++v) x.k[v] = bload4<load_aux<BITS>()>(rk, vo + 16 * v, 0);
+#pragma unroll
+    for (int v = 0; v < P::NVW; ++v) x.v[v] = bload4<load_aux<BITS>()>(rv, vo + 16 * v, 0);
+  }
+};
+
+template <int BITS, int G>
+__device__ __forceinline__ void pair_window_step(const PairWinStep<BITS, G> &x, bool valid,
+                                                 const float *qv,
+                                                 LaneState<PairCfg<BITS, G>::CPL> &st) {
+  using C = DecCfg<BITS, G>;
+  using P = PairCfg<BITS, G>;
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int v = 0; v < P::NVW; ++v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = u4_get(x.k[v], e);
+      a0 = mix_lo(qv[8 * v + 2 * e], u, a0);
+      a1 = mix_hi(qv[8 * v + 2 * e + 1], u, a1);
+    }
+  }
+  float s = lane_group_sum<P::PW>(a0 + a1);
+  s = valid ? s : -INFINITY;
+  update_max<P::CPL, 1>(st, &s);
+  const float pr = s > -INFINITY ? exp2_fast(s - st.m) : 0.0f;
+  st.l += pr;
+#pragma unroll
+  for (int v = 0; v < P::NVW; ++v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // value sums hold channel values times 2^(e - 24), e the channel's
+      // code offset within its word (see the quantized tokens)
+      const uint32_t u = u4_get(x.v[v], e);
+      const int c = 8 * v + 2 * e;
+      st.acc[c] = mix_lo(pr * __builtin_ldexpf(1.0f, code_offset<BITS>(c % C::CPW) - 24), u,
+                         st.acc[c]);
+      st.acc[c + 1] = mix_hi(pr * __builtin_ldexpf(1.0f, code_offset<BITS>((c + 1) % C::CPW) - 24),
+                             u, st.acc[c + 1]);
+    }
+  }
+}
+
+// One wave's state to the workgroup's LDS, in decode_kernel's published
+// form (row r: every channel, from the lanes of row r): rescale to the
+// wave's maximum, then sum the token quads of each 16-lane row (lane q PW +
+// p; rotations by 4 and 8 lanes within the row, or by 8 alone at PW = 8).
+template <int BITS, int G>
+__device__ __forceinline__ void pair_publish(float (&fin_acc)[4][kD], float (&fin_bias)[4][32],
+                                             float &fin_m, float &fin_l,
+                                             LaneState<PairCfg<BITS, G>::CPL> &st) {
+  using C = DecCfg<BITS, G>;
+  using P = PairCfg<BITS, G>;
+  const int lane = threadIdx.x & 63;
+  const int p = lane % P::PW, row = lane >> 4;
+  const float M = wave_max(st.m);
+  const float e = (st.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(st.m - M);
+  float bias = st.bias * e;
+  const float lw = wave_sum(p == 0 ? st.l * e : 0.0f);
+#pragma unroll
+  for (int i = 0; i < P::CPL; ++i) {
+    float v = st.acc[i] * e;
+    if constexpr (P::PW == 4) v += dpp<0x124>(v);  // row_ror:4
+    v += dpp<0x128>(v);                             // row_ror:8
+    st.acc[i] = v;
+  }
+  if constexpr (P::PW == 4) bias += dpp<0x124>(bias);
+  bias += dpp<0x128>(bias);
+  if ((lane & 15) < P::PW) {
+#pragma unroll
+    for (int i = 0; i < P::CPL; i += 4)
+      *reinterpret_cast<float4 *>(&fin_acc[row][2 * p * C::CPW + i]) =
+          make_float4(st.acc[i], st.acc[i + 1], st.acc[i + 2], st.acc[i + 3]);
+    fin_bias[row][2 * p] = bias;
+    fin_bias[row][2 * p + 1] = bias;
+  }
+  if (lane == 0) {
+    fin_m = M;
+    fin_l = lw;
+  }
+}
+
+template <int BITS, int G>
+__global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_pair_kernel(
+    DecodeArgs a) {
+  using C = DecCfg<BITS, G>;
+  using P = PairCfg<BITS, G>;
+  constexpr int kDepth = 2;
+  __shared__ DecSmem<BITS, G, false> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const size_t bh = (size_t)b * a.heads + h;
+  const int S = a.splits;
+  const int p = lane % P::PW, q = lane / P::PW, d = 4 * q;
+
+  // ---- the stream's descriptors and this wave's first sub-chunk, before
+  // the lengths (as decode_kernel)
+  const size_t tps = (size_t)(a.cap / G);
+  PairStream<BITS, G> qs;
+  qs.kc = a.k_codes + bh * tps * (C::W * G);
+  qs.vc = a.v_codes + bh * tps * (C::W * G);
+  qs.ks = a.k_scale + bh * tps * kD;
+  qs.kz = a.k_zero + bh * tps * kD;
+  qs.vs = a.v_scale + bh * tps * kD;
+  qs.vz = a.v_zero + bh * tps * kD;
+  qs.code_bytes = (uint32_t)(tps * (C::W * G) * 4);
+  qs.meta_bytes = (uint32_t)(tps * kD * 2);
+  const int vg = (2 * p * C::CPW) / G;  // the lane's value group
+  qs.code_voff = (uint32_t)((d / G) * (C::W * G) + 2 * p * G + d % G) * 4;
+  qs.code_voffc = (uint32_t)(2 * p * G + d % G) * 4;
+  qs.vmeta_voff = (uint32_t)((d / G) * kD + vg * G + d % G) * 2;
+  qs.vmeta_voffc = (uint32_t)(vg * G + d % G) * 2;
+  qs.kmeta_voff = (uint32_t)lane * 4;
+  qs.gw = split * kDecodeWaves + wv;
+  qs.nw = kDecodeWaves * S;
+  const uint32_t qraw = bload1(make_rsrc(a.q + bh * kD, kD * 2), (uint32_t)lane * 4, 0);
+  PairLoads<BITS, G> ring[kDepth];
+  qs.issue_whole(ring[0], 0, a.cap);
+
+  int ql = a.q_len[b], rl = a.r_len[b];
+  __builtin_amdgcn_sched_barrier(0);
+  const bool lens_ok = (ql >= 0) & (ql <= a.cap) & ((ql % G) == 0) & (rl >= 0) & (rl <= a.R);
+  if (!lens_ok) {
+    if (split == 0 && h == 0 && tid == 0) atomicOr(a.status, KIVI_ST_BAD_LENGTH);
+    ql = 0;
+    rl = 0;
+  }
+  qs.ql = ql;
+  qs.last_tile = ql / G - 1;
+  qs.n = qs.gw * C::SUB < ql ? (ql - qs.gw * C::SUB + qs.nw * C::SUB - 1) / (qs.nw * C::SUB) : 0;
+  if (qs.t0(0) + C::SUB > ql) qs.issue(ring[0], 0);
+
+  PairWin<BITS, G> ws;
+  ws.kr = a.k_res + bh * a.R * kD;
+  ws.vr = a.v_res + bh * a.R * kD;
+  ws.begin = qs.gw * a.win_per_wave;
+  ws.end = min(rl, ws.begin + a.win_per_wave);
+  ws.bytes = (uint32_t)max(0, ws.end) * (kD * 2);
+  ws.lane_voff = (uint32_t)(q * kD + 2 * p * C::CPW) * 2;
+  const int wsteps = ws.end > ws.begin ? (ws.end - ws.begin + P::NQ - 1) / P::NQ : 0;
+
+  auto &stg = sm.u.wave[wv];
+#if KIVI_DECODE_PRIORITY == 2
+  if (lane == 0) sm.prog[wv] = 0;
+#endif
+  const half2_t hq = __builtin_bit_cast(half2_t, qraw);
+  const float qs0 = (float)hq.x * a.qscale, qs1 = (float)hq.y * a.qscale;
+  const float qf0 = qs0 * code_factor<BITS>((2 * lane) % C::CPW);
+  const float qf1 = qs1 * code_factor<BITS>((2 * lane + 1) % C::CPW);
+  stg.qs[2 * lane] = qs0;  // for the window tokens
+  stg.qs[2 * lane + 1] = qs1;
+
+  LaneState<P::CPL> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+  st.bias = 0.0f;
+#pragma unroll
+  for (int i = 0; i < P::CPL; ++i) st.acc[i] = 0.0f;
+
+  // a sub-chunk, masked only where one can end past ql (G < SUB)
+  auto process = [&](const PairLoads<BITS, G> &bb, int c) {
+    const int T0 = qs.t0(c);
+    if constexpr (G < C::SUB) {
+      if (T0 + C::SUB > ql) {
+        process_pair<BITS, G, true>(bb, T0, ql, lane, qf0, qf1, qs0, qs1, stg.qp, stg.cz, st);
+        return;
+      }
+    }
+    process_pair<BITS, G, false>(bb, T0, ql, lane, qf0, qf1, qs0, qs1, stg.qp, stg.cz, st);
+  };
+
+  {
+    // the rest of the ring once sub-chunk 0 is in
+    uint32_t z;
+    asm volatile("v_and_b32 %0, 0, %1" : "=v"(z) : "v"(ring[0].vz.y));
+    qs.issue(ring[1], 1, z);
+  }
+  int c0 = 0;
+  for (; c0 + kDepth <= qs.n; c0 += kDepth) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+#if KIVI_DECODE_PRIORITY == 2
+      set_lead_priority(sm.prog, wv, lane, c0 + k);
+#elif KIVI_DECODE_PRIORITY
+      set_progress_priority(c0 + k, qs.n);
+#endif
+      process(ring[k], c0 + k);
+      qs.issue(ring[k], c0 + k + kDepth);
+    }
+  }
+  PairWinStep<BITS, G> wpf[P::PFW];
+#pragma unroll
+  for (int i = 0; i < P::PFW; ++i) ws.issue(wpf[i], i);
+#pragma unroll
+  for (int k = 0; k < kDepth - 1; ++k)
+    if (c0 + k < qs.n) {
+#if KIVI_DECODE_PRIORITY == 2
+      set_lead_priority(sm.prog, wv, lane, c0 + k);
+#elif KIVI_DECODE_PRIORITY
+      set_progress_priority(c0 + k, qs.n);
+#endif
+      process(ring[k], c0 + k);
+    }
+#if KIVI_DECODE_PRIORITY
+  __builtin_amdgcn_s_setprio(0);
+#endif
+
+  // ---- the wave's window tokens
+  if (wsteps > 0) {
+    __builtin_amdgcn_wave_barrier();
+    float qv[P::CPL];
+#pragma unroll
+    for (int i = 0; i < P::CPL; ++i) qv[i] = stg.qs[2 * p * C::CPW + i];
+#pragma unroll
+    for (int i = 0; i < P::PFW; ++i)
+      if (i < wsteps) pair_window_step<BITS, G>(wpf[i], ws.begin + i * P::NQ + q < ws.end, qv, st);
+    for (int i = P::PFW; i < wsteps; ++i) {  // windows longer than the prefetched steps
+      PairWinStep<BITS, G> x;
+      ws.issue(x, i);
+      pair_window_step<BITS, G>(x, ws.begin + i * P::NQ + q < ws.end, qv, st);
+    }
+  }
+
+  pair_publish<BITS, G>(sm.fin.acc[wv], sm.fin.bias[wv], sm.fin.m[wv], sm.fin.l[wv], st);
+  __syncthreads();
+  if (S == 1 && tid >= kD) return;  // only the output channels' threads combine
+  const WgState wg = combine_waves<BITS, G>(sm.fin, tid);
+  if (S == 1) {
+    if (tid < kD) a.out[bh * kD + tid] = wg.L > 0.0f ? wg.acc / wg.L : 0.0f;
+    return;
+  }
+  finish_splits(a, sm, wg, bh, split, S, tid);
 }
 
 // ------------------------------------------------ measurement: stream read
@@ -2599,10 +3057,26 @@ int launch_decode_t(const DecodeArgs &da, const EncodeArgs &ea, bool fused, int 
   if (fused) {  // one workgroup per compute unit (launch_decode_step)
     if constexpr (BITS == 8) return (int)hipErrorInvalidValue;  // three kernels instead
     else hipLaunchKernelGGL((decode_kernel<BITS, G, true, 2>), grid, blk, 0, st, da, ea);
-  } else if (depth == 1)
+  } else if (depth == 1) {
     hipLaunchKernelGGL((decode_kernel<BITS, G, false, 1>), grid, blk, 0, st, da, ea);
-  else
+  } else {
+#ifndef KIVI_PAIR
+#define KIVI_PAIR 1
+#endif
+    // two sub-chunks in flight, no sink tokens, and by capacity at least 16
+    // sub-chunks per wave: two code words per lane (on the long-context
+    // workload 74.2 -> 69.1 us at B=2 and 108.9 -> 104.4 us at B=4; on the
+    // 7B layer, 8 sub-chunks per wave, 23.5 against 23.9 us, and on one head
+    // 4.9 against 5.5 us, where decode_kernel stays)
+    if constexpr (KIVI_PAIR && BITS != 8 && KIVI_WIDE_DEPTH == 2) {
+      if (da.n_sink == 0 &&
+          da.cap / DecCfg<BITS, G>::SUB >= 16 * kDecodeWaves * da.splits) {
+        hipLaunchKernelGGL((decode_pair_kernel<BITS, G>), grid, blk, 0, st, da);
+        return (int)hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((decode_kernel<BITS, G, false, KIVI_WIDE_DEPTH>), grid, blk, 0, st, da, ea);
+  }
   return (int)hipGetLastError();
 }
 

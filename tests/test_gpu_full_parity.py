@@ -83,6 +83,33 @@ def test_ragged_serving_every_head():
     print(f"ragged batch 64: worst max-abs {worst[0]:.2e}, rel-L2 {worst[1]:.2e}")
 
 
+def test_two_word_lanes_every_head_with_half_sub_chunks():
+    """The 7B-shaped batch in a cache of capacity 8192: one workgroup per
+    (sequence, head) and, by capacity, 16 sub-chunks of 64 tokens per wave,
+    which the decode takes with two code words per lane.  Every second
+    sequence holds 32 fewer quantized tokens, so its last sub-chunk has one
+    valid tile (the masked case).  Every head against the oracle."""
+    w = workload(2)
+    cap = 8192
+    ql = w.q_len.copy()
+    ql[1::2] -= 32
+    rl = w.r_len.copy()
+    c = gpu_cache(w, capacity=cap, q_len=ql, r_len=rl)
+    assert kivi.decode_splits(c.dims) == 1
+    out = kivi.decode_attn(c, torch.from_numpy(w.q).cuda(), w.config.sm_scale).cpu().numpy()
+    assert c.status_bits() == 0
+    cfg = w.config
+
+    def one(bh):
+        b, h = bh
+        st = ocache.head_state(w.k[b, h], w.v[b, h], int(ql[b]), int(rl[b]), cfg.group, w.bits,
+                               cap, cfg.residual)
+        ref = ocache.decode_head(w.q[b, h], st, cfg.sm_scale, cfg.group, w.bits)
+        return assert_within_tolerance(out[b, h], ref, f"b={b} h={h} q_len={ql[b]}")
+
+    parallel_map(one, _all_heads(w))
+
+
 @pytest.mark.parametrize("fills", [True, False])
 def test_whole_step_kernel_llama2_7b_every_head_against_oracle(fills):
     """kivi_decode_step (one kernel) appends token t of every (sequence, head)

@@ -412,9 +412,12 @@ def _step_both(make, k_new, v_new, q, scale):
 
 
 def _assert_same_step(out_a, out_b, sa, sb):
-    # the cache bit for bit; the output up to rounding (the whole-step kernel
-    # may take the window tokens first, a different summation order)
-    torch.testing.assert_close(out_b, out_a, rtol=1e-5, atol=1e-6)
+    # the cache bit for bit; the output up to rounding: the whole-step kernel
+    # may take the window tokens first, and the plain decode (two code words
+    # per lane) sums in another lane order, fp32 sums of a few hundred terms
+    # of up to |v| ~ 4 reordered (about 1e-5), through the softmax weights
+    # (score sums reordered) up to about 1e-4
+    torch.testing.assert_close(out_b, out_a, rtol=1e-4, atol=1e-4)
     for name in sa:
         assert np.array_equal(sa[name].view(np.uint8), sb[name].view(np.uint8)), name
     assert not sb["tickets"].any()

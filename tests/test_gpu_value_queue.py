@@ -168,8 +168,9 @@ def test_queue_differs_from_window_flush_only_in_the_values():
     torch.cuda.synchronize()
     # w has a full 128-token window: the queue holds the same 128 values in
     # fp16 that the window-flush cache holds, so both attend over the same
-    # values here; one more token makes them differ
-    assert torch.allclose(a, b, rtol=1e-5, atol=1e-6)
+    # values here; one more token makes them differ (up to rounding: the
+    # plain decode sums in another lane order than the value-queue decode)
+    assert torch.allclose(a, b, rtol=1e-4, atol=1e-4)
     kn = torch.from_numpy(w.k[:, :, 0]).cuda().contiguous()
     kivi.append_kv_vq(c, kn, kn)    # the window is full: refused
     torch.cuda.synchronize()
