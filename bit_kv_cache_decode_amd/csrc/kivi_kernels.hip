@@ -2349,6 +2349,19 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
   [[maybe_unused]] const int nwt = a.win_per_wave > 0 ? G / a.win_per_wave : 1;
   [[maybe_unused]] const int tileT = ws.begin / G;
   [[maybe_unused]] bool keys_done = true;
+  // this wave's key tile parameters and key words, if every wave has posted
+  // its key partials (an acquire read of the count)
+  [[maybe_unused]] auto try_keys = [&]() {
+    if constexpr (FUSED) {
+      auto &rf = fused_flush_smem<BITS, G>().reg;
+      const uint32_t in = (uint32_t)__builtin_amdgcn_readfirstlane((int)__hip_atomic_load(
+          &rf.arrived, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+      if (in != (uint32_t)kDecodeWaves) return false;
+      flush_regs_tile_params<BITS, G>(ea, rf, tile0, tileT, nwt, wv, lane, wv % nwt == 0);
+      flush_regs_keys<BITS, G>(ea, rf, wpf, wsteps, tile0, ws.begin, wv, w, slot);
+    }
+    return true;
+  };
   if constexpr (FUSED) {
     if (early) {
       auto &rf = fused_flush_smem<BITS, G>().reg;
@@ -2366,6 +2379,16 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
       if (wsteps > 0) flush_regs_key_partials<BITS, G>(rf, wpf, wsteps, wv, w, slot);
       if (lane == 0)
         __hip_atomic_fetch_add(&rf.arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // then, while the first sub-chunk is in flight (the vector units would
+      // otherwise wait for it), the window's attention, the flush's value
+      // words, and its key words if every wave has posted its partials
+      // (else after the stream, or after the combine barrier)
+      window();
+      store_new();
+      if (wsteps > 0) {
+        flush_regs_values<BITS, G>(ea, wpf, wsteps, tile0, ws.begin, w, slot);
+        keys_done = try_keys();
+      }
     }
   }
   if constexpr (kDecodeDepth > 1) {
@@ -2425,23 +2448,9 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
     window();
     store_new();
   } else if constexpr (FUSED) {
-    // the window's attention, the flush's value words, and (once every wave
-    // has posted its key partials) this wave's key tile and key words.  (Done
-    // in the middle of the stream instead, they measured no faster: the
-    // stream is as bound by vector issue as by HBM.)
-    window();
-    store_new();
-    if (wsteps > 0) {
-      auto &rf = fused_flush_smem<BITS, G>().reg;
-      flush_regs_values<BITS, G>(ea, wpf, wsteps, tile0, ws.begin, w, slot);
-      const uint32_t in = (uint32_t)__builtin_amdgcn_readfirstlane((int)__hip_atomic_load(
-          &rf.arrived, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
-      keys_done = in == (uint32_t)kDecodeWaves;
-      if (keys_done) {
-        flush_regs_tile_params<BITS, G>(ea, rf, tile0, tileT, nwt, wv, lane, wv % nwt == 0);
-        flush_regs_keys<BITS, G>(ea, rf, wpf, wsteps, tile0, ws.begin, wv, w, slot);
-      }
-    }
+    // early: the key words, if the partials were not all posted before the
+    // stream
+    if (!keys_done) keys_done = try_keys();
   }
   // fp16 sink tokens (the sequence's first tokens, kept unquantized ahead of
   // the quantized ones, at positions 0 .. n_sink - 1): this wave's share
