@@ -91,3 +91,38 @@ def test_width_group_combination(bits, G, batch):
                 got = getattr(c, name)[b, h, t0 // G:(t0 + R) // G].cpu().numpy()
                 assert np.array_equal(got.view(np.uint8), enc[name].view(np.uint8)), (name, b, h)
     assert not c.tickets.any() and c.status_bits() == 0
+
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("bits", [2, 4])
+def test_two_word_lanes_width_group(bits, G):
+    """The decode that holds two code words per lane, selected by capacity
+    (8 x 32 pairs, one workgroup each, and at least 16 sub-chunks per wave in
+    a cache of 16384 tokens), for every width and group it is built for.  The
+    sequences are short and ragged: empty, window only, one tile plus one
+    window token, 1024 + G quantized tokens (at B=2 and G=32 the last
+    sub-chunk holds one valid tile), full windows and partial ones.  Sampled
+    heads against the oracle."""
+    batch, cap = 8, 16384
+    ql = np.array([0, 0, G, 1024 + G, 2048, 768, G, 2048 - G], np.int32)
+    win = np.array([0, 1, 1, R, R, 9, G, 52], np.int32)
+    lens = ql + win
+    rng = np.random.default_rng(5000 + 10 * bits + G)
+    T = int(lens.max())
+    k = rng.standard_normal((batch, H, T, D), np.float32)
+    k[:, :, :, 5] *= 40.0
+    k = k.astype(np.float16)
+    v = rng.standard_normal((batch, H, T, D), np.float32).astype(np.float16)
+    q = (rng.standard_normal((batch, H, D), np.float32) / np.sqrt(D)).astype(np.float16)
+    c = kivi.KiviCache(batch, H, D, bits, G, R, cap)
+    assert kivi.decode_splits(c.dims) == 1
+    kivi.prefill(c, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                 torch.from_numpy(lens).cuda(), torch.from_numpy(win).cuda())
+    out = kivi.decode_attn(c, torch.from_numpy(q).cuda(), 1.0).cpu().numpy()
+    assert c.status_bits() == 0
+    for b in range(batch):
+        for h in (0, 13, 31):
+            st = ocache.head_state(k[b, h], v[b, h], int(ql[b]), int(win[b]), G, bits, cap, R)
+            ref = ocache.decode_head(q[b, h], st, 1.0, G, bits)
+            assert_within_tolerance(out[b, h], ref, f"b={b} h={h} q_len={ql[b]} win={win[b]}")
