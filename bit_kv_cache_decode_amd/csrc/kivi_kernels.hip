@@ -1059,18 +1059,29 @@ struct LaneState {
   float acc[CPW];
 };
 
-// Fold new scores s[0..N) into the state: if any lane's running max grows,
-// every lane rescales (by 1 where its own max did not move).
+// How far (log2 units) a score may exceed a lane's reference m before the
+// lane moves m up.  The softmax only needs acc, l and bias to share one
+// reference, not that it be the running maximum: with m lagging by at most
+// this much, every weight 2^(s - m) stays below 2^8, far inside fp32, and the
+// per-wave rescale of the accumulators (taken whenever any of the wave's
+// lanes moves) runs after the first sub-chunk only where a score jumps by
+// more than 8, instead of on most sub-chunks of a long stream.
+constexpr float kMaxLag = 8.0f;
+
+// Fold new scores s[0..N) into the state: if any lane's scores pass its
+// reference by more than kMaxLag, every lane rescales (by 1 where its own
+// reference did not move).
 template <int CPW, int N>
 __device__ __forceinline__ void update_max(LaneState<CPW> &st, const float *s) {
   float mc = st.m;
 #pragma unroll
   for (int i = 0; i < N; ++i) mc = fmaxf(mc, s[i]);
-  if (__ballot(mc > st.m) != 0) {
-    // 1 where this lane's max did not move (also when it is still -inf),
-    // 0 on a lane's first tokens (m = -inf)
-    const float corr = mc > st.m ? exp2_fast(st.m - mc) : 1.0f;
-    st.m = mc;
+  const bool grow = mc > st.m + kMaxLag;  // always on a lane's first finite score
+  if (__ballot(grow) != 0) {
+    // 1 where this lane's reference did not move, 0 on its first tokens
+    // (m = -inf)
+    const float corr = grow ? exp2_fast(st.m - mc) : 1.0f;
+    st.m = grow ? mc : st.m;
     st.l *= corr;
     st.bias *= corr;
 #pragma unroll
@@ -2846,7 +2857,7 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_pa
     DecodeArgs a) {
   using C = DecCfg<BITS, G>;
   using P = PairCfg<BITS, G>;
-  constexpr int kDepth = 2;
+  constexpr int kDepth = 2;  // a third sub-chunk in flight measured slower
   __shared__ DecSmem<BITS, G, false> sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -2934,7 +2945,8 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWavesPerSimd) void decode_pa
     // the rest of the ring once sub-chunk 0 is in
     uint32_t z;
     asm volatile("v_and_b32 %0, 0, %1" : "=v"(z) : "v"(ring[0].vz.y));
-    qs.issue(ring[1], 1, z);
+#pragma unroll
+    for (int k = 1; k < kDepth; ++k) qs.issue(ring[k], k, z);
   }
   int c0 = 0;
   for (; c0 + kDepth <= qs.n; c0 += kDepth) {
