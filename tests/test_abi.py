@@ -68,6 +68,20 @@ def test_validate_dims_codes():
     assert kivi.workspace_bytes(kivi.make_dims(8, 32, 64, 2, 32, 128, 4096)) == 0
 
 
+@pytest.mark.parametrize("bits,bytes_per_token", [(2, 32), (4, 64), (8, 128)])
+def test_capacity_limit_of_32_bit_buffer_offsets(bits, bytes_per_token):
+    """One (sequence, head) region of the code arrays must stay below 2 GiB
+    (the decode addresses it with 32-bit buffer offsets): the largest
+    capacity below the limit is accepted, the first at it is refused as
+    unsupported, not wrapped."""
+    limit = (1 << 31) // bytes_per_token          # tokens whose codes fill 2 GiB
+    below = limit - 128
+    assert kivi.decode_splits(kivi.make_dims(1, 1, 128, bits, 128, 128, below)) >= 1
+    assert kivi.decode_splits(kivi.make_dims(1, 1, 128, bits, 128, 128, limit)) == \
+        kivi.KIVI_EUNSUPPORTED
+    assert kivi.workspace_bytes(kivi.make_dims(1, 1, 128, bits, 128, 128, limit)) == 0
+
+
 @pytest.mark.parametrize("dims,splits,step_kernels", [
     ((1, 1, 128, 2, 32, 32, 256), 1, 1),         # one workgroup does it all
     ((8, 32, 128, 2, 32, 128, 4096), 1, 1),      # one workgroup per (sequence, head) fills the chip
