@@ -693,3 +693,75 @@ def test_eight_bit_edge_lengths(q_len, r_len):
         ref = ocache.decode_head(w.q[0, h], st, 1.0, 32, 8)
         assert_within_tolerance(out[0, h], ref, f"{q_len}+{r_len}")
         assert_head_bit_exact(head_buffers(c, 0, h), st, 32)
+
+
+def _score_profile_kv(mode, T, rng):
+    """Keys whose log2 scores against the unit query q follow a profile along
+    the sequence (before quantization): 'rise' climbs 60 over the sequence,
+    'fall' descends 60, 'steps' climbs 9 every 512 tokens, 'spike' is noise
+    with one token 40 above it in the last quarter and one 25 above it near
+    the end.  The noise is N(0, 1) in every channel."""
+    q = rng.standard_normal(D_HEAD)
+    q /= np.linalg.norm(q)
+    t = np.arange(T, dtype=np.float64)
+    if mode == "rise":
+        s = 60.0 * t / T
+    elif mode == "fall":
+        s = 60.0 * (1.0 - t / T)
+    elif mode == "steps":
+        s = 9.0 * (t // 512)
+    else:
+        s = np.zeros(T)
+        s[int(rng.integers(3 * T // 4, T - 200))] = 40.0
+        s[T - 3] = 25.0
+    k = np.outer(s / np.log2(np.e), q) + rng.standard_normal((T, D_HEAD))
+    v = rng.standard_normal((T, D_HEAD))
+    return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)
+
+
+D_HEAD = 128
+_MODES = ("rise", "spike", "fall", "steps")
+
+
+@pytest.mark.parametrize("shape", ["one_word_lanes", "two_word_lanes", "split_heads"])
+def test_score_profiles_that_move_the_softmax_reference(shape):
+    """Score profiles that make the online softmax move its reference often
+    (a steady climb, steps of 9 in log2 units, a late spike) or never after
+    the start (a fall), through the one-word-per-lane decode (one workgroup
+    per (sequence, head)), the two-word-lane decode (long caches), and the
+    decode split over many workgroups (merged by log-sum-exp): sampled heads
+    against the oracle's fp64 softmax."""
+    R, G, bits = 128, 32, 2
+    if shape == "one_word_lanes":
+        batch, heads, cap, ql = 8, 32, 4096, 3968
+    elif shape == "two_word_lanes":
+        batch, heads, cap, ql = 8, 32, 16384, 4096
+    else:
+        batch, heads, cap, ql = 1, 4, 65536, 32768
+    win = R - 1
+    T = ql + win
+    rng = np.random.default_rng({"one_word_lanes": 71, "two_word_lanes": 72, "split_heads": 73}[shape])
+    k = np.empty((batch, heads, T, D_HEAD), np.float16)
+    v = np.empty_like(k)
+    q = np.empty((batch, heads, D_HEAD), np.float16)
+    modes = {}
+    for b in range(batch):
+        for h in range(heads):
+            modes[b, h] = _MODES[(b * heads + h) % len(_MODES)]
+            q[b, h], k[b, h], v[b, h] = _score_profile_kv(modes[b, h], T, rng)
+    c = kivi.KiviCache(batch, heads, D_HEAD, bits, G, R, cap)
+    splits = kivi.decode_splits(c.dims)
+    assert (splits > 1) == (shape == "split_heads"), splits
+    lens = np.full(batch, T, np.int32)
+    wins = np.full(batch, win, np.int32)
+    kivi.prefill(c, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                 torch.from_numpy(lens).cuda(), torch.from_numpy(wins).cuda())
+    out = kivi.decode_attn(c, torch.from_numpy(q).cuda(), 1.0).cpu().numpy()
+    assert c.status_bits() == 0
+    picks = [(b, h) for b in range(batch) for h in range(heads)]
+    if len(picks) > 16:  # two heads per sequence, every profile among them
+        picks = [(b, (b + j) % heads) for b in range(batch) for j in (0, 1)]
+    for b, h in picks:
+        st = ocache.head_state(k[b, h], v[b, h], ql, win, G, bits, cap, R)
+        ref = ocache.decode_head(q[b, h], st, 1.0, G, bits)
+        assert_within_tolerance(out[b, h], ref, f"{shape} b={b} h={h} {modes[b, h]}")
