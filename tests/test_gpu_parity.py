@@ -723,24 +723,31 @@ D_HEAD = 128
 _MODES = ("rise", "spike", "fall", "steps")
 
 
-@pytest.mark.parametrize("shape", ["one_word_lanes", "two_word_lanes", "split_heads"])
+@pytest.mark.parametrize("shape", ["one_word_lanes", "two_word_lanes", "split_heads",
+                                   "step_fills_window", "step_appends"])
 def test_score_profiles_that_move_the_softmax_reference(shape):
     """Score profiles that make the online softmax move its reference often
     (a steady climb, steps of 9 in log2 units, a late spike) or never after
     the start (a fall), through the one-word-per-lane decode (one workgroup
-    per (sequence, head)), the two-word-lane decode (long caches), and the
-    decode split over many workgroups (merged by log-sum-exp): sampled heads
-    against the oracle's fp64 softmax."""
+    per (sequence, head)), the two-word-lane decode (long caches), the
+    decode split over many workgroups (merged by log-sum-exp), and the
+    one-kernel step, whose append either fills the window (the window's
+    tokens then go before the quantized stream) or not: sampled heads
+    against the oracle's fp64 softmax over every token."""
     R, G, bits = 128, 32, 2
-    if shape == "one_word_lanes":
+    step = shape.startswith("step")
+    if shape in ("one_word_lanes", "step_fills_window"):
         batch, heads, cap, ql = 8, 32, 4096, 3968
+    elif shape == "step_appends":
+        batch, heads, cap, ql = 8, 32, 4096, 3840
     elif shape == "two_word_lanes":
         batch, heads, cap, ql = 8, 32, 16384, 4096
     else:
         batch, heads, cap, ql = 1, 4, 65536, 32768
-    win = R - 1
+    win = {"step_fills_window": R, "step_appends": 100}.get(shape, R - 1)  # after the step
     T = ql + win
-    rng = np.random.default_rng({"one_word_lanes": 71, "two_word_lanes": 72, "split_heads": 73}[shape])
+    rng = np.random.default_rng(70 + ["one_word_lanes", "two_word_lanes", "split_heads",
+                                      "step_fills_window", "step_appends"].index(shape))
     k = np.empty((batch, heads, T, D_HEAD), np.float16)
     v = np.empty_like(k)
     q = np.empty((batch, heads, D_HEAD), np.float16)
@@ -752,11 +759,19 @@ def test_score_profiles_that_move_the_softmax_reference(shape):
     c = kivi.KiviCache(batch, heads, D_HEAD, bits, G, R, cap)
     splits = kivi.decode_splits(c.dims)
     assert (splits > 1) == (shape == "split_heads"), splits
-    lens = np.full(batch, T, np.int32)
-    wins = np.full(batch, win, np.int32)
-    kivi.prefill(c, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+    lens = np.full(batch, T - step, np.int32)
+    wins = np.full(batch, win - step, np.int32)
+    kivi.prefill(c, torch.from_numpy(k[:, :, :T - step]).cuda(),
+                 torch.from_numpy(v[:, :, :T - step]).cuda(),
                  torch.from_numpy(lens).cuda(), torch.from_numpy(wins).cuda())
-    out = kivi.decode_attn(c, torch.from_numpy(q).cuda(), 1.0).cpu().numpy()
+    qt = torch.from_numpy(q).cuda()
+    if step:
+        assert kivi.decode_step_kernels(c.dims) == 1
+        kn = torch.from_numpy(np.ascontiguousarray(k[:, :, T - 1])).cuda()
+        vn = torch.from_numpy(np.ascontiguousarray(v[:, :, T - 1])).cuda()
+        out = kivi.decode_step(c, kn, vn, qt, 1.0).cpu().numpy()
+    else:
+        out = kivi.decode_attn(c, qt, 1.0).cpu().numpy()
     assert c.status_bits() == 0
     picks = [(b, h) for b in range(batch) for h in range(heads)]
     if len(picks) > 16:  # two heads per sequence, every profile among them
