@@ -695,6 +695,10 @@ def test_eight_bit_edge_lengths(q_len, r_len):
         assert_head_bit_exact(head_buffers(c, 0, h), st, 32)
 
 
+D_HEAD = 128
+_MODES = ("rise", "spike", "fall", "steps")
+
+
 def _score_profile_kv(mode, T, rng):
     """Keys whose log2 scores against the unit query q follow a profile along
     the sequence (before quantization): 'rise' climbs 60 over the sequence,
@@ -717,10 +721,6 @@ def _score_profile_kv(mode, T, rng):
     k = np.outer(s / np.log2(np.e), q) + rng.standard_normal((T, D_HEAD))
     v = rng.standard_normal((T, D_HEAD))
     return q.astype(np.float16), k.astype(np.float16), v.astype(np.float16)
-
-
-D_HEAD = 128
-_MODES = ("rise", "spike", "fall", "steps")
 
 
 @pytest.mark.parametrize("shape", ["one_word_lanes", "two_word_lanes", "split_heads",
