@@ -2163,11 +2163,12 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
   qs.gw = split * kDecodeWaves + wv;
   qs.nw = kDecodeWaves * S;
   const uint32_t qraw = bload1(make_rsrc(a.q + bh * kD, kD * 2), (uint32_t)lane * 4, 0);
-  // The plain decode requests its first sub-chunk before the lengths arrive
-  // (their load is a round trip at the start of every wave), as if the
-  // cache held it whole; it is requested again below when it does not.
+  // Every decode, the whole step included, requests its first sub-chunk
+  // before the lengths arrive (their load is a round trip at the start of
+  // every wave, through LDS and a barrier in the whole step), as if the cache
+  // held it whole; it is requested again below when it does not.
   SubLoads<BITS, G> ring[kDecodeDepth];
-  if constexpr (!FUSED) qs.issue_whole(ring[0], 0, a.cap);
+  qs.issue_whole(ring[0], 0, a.cap);
 
   int ql, rl;
   if constexpr (FUSED) {
@@ -2264,11 +2265,11 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
   // all waves' requests interleaved, so the first data a wave needs would
   // arrive no sooner than the rest.)
   // Except in a whole step whose append fills a window of at most 128
-  // tokens ("early"): there the window comes first -- its loads before the
-  // quantized ones, then its attention and the whole flush (quantized from
-  // the window registers) while the first quantized sub-chunks are in
-  // flight; after the last quantized byte, the flush's arithmetic would run
-  // with HBM idle.
+  // tokens ("early"): there the window comes first -- its loads right after
+  // the first sub-chunk's (requested before the lengths), then its
+  // attention and the whole flush (quantized from the window registers)
+  // while the first quantized sub-chunks are in flight; after the last
+  // quantized byte, the flush's arithmetic would run with HBM idle.
   [[maybe_unused]] const size_t tile0 = bh * tps + (size_t)(ql0 / G);
   bool early = false;
   if constexpr (FUSED) early = flush && a.win_per_wave <= 16;
@@ -2289,13 +2290,14 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
 #pragma unroll
     for (int i = 0; i < WC::PF; ++i) ws.issue(wpf[i], i);
   }
-  // Only the first sub-chunk's loads go out now; the rest of the ring follows
-  // once it has arrived (below).  Every wave requesting its whole ring at
-  // the start makes the memory system serve all of it interleaved, so the
-  // first sub-chunk would arrive no sooner than the others; with half the
-  // request the waves start computing earlier (7B layer 25.4 -> 24.8 us,
-  // 131072 tokens at B=2 80.3 -> 77.9 us, alternating runs on one box).
-  if (FUSED || qs.t0(0) + C::SUB > qs.ql) qs.issue(ring[0], 0);
+  // Only the first sub-chunk's loads are out so far (again now where the
+  // sequence ends inside it); the rest of the ring follows once it has
+  // arrived (below).  Every wave requesting its whole ring at the start
+  // makes the memory system serve all of it interleaved, so the first
+  // sub-chunk would arrive no sooner than the others; with half the request
+  // the waves start computing earlier (7B layer 25.4 -> 24.8 us, 131072
+  // tokens at B=2 80.3 -> 77.9 us, alternating runs on one box).
+  if (qs.t0(0) + C::SUB > qs.ql) qs.issue(ring[0], 0);
 
   auto &stg = sm.u.wave[wv];
 #if KIVI_DECODE_PRIORITY == 2
