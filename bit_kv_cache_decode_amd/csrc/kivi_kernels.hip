@@ -2531,13 +2531,15 @@ __global__ __launch_bounds__(kDecodeThreads, DEPTH == 1 ? (ROPE || VQ ? 2 : 3) *
   wave_publish<C::CPW, C::W, C::W == 8>(sm.fin.acc[wv], sm.fin.bias[wv], sm.fin.m[wv],
                                          sm.fin.l[wv], st.m, st.l, st.acc, st.bias);
   __syncthreads();
-  // one workgroup per (sequence, head), plain decode: only the threads that
-  // write an output channel combine (the rest would only read LDS)
+  // one workgroup per (sequence, head): only the threads that write an
+  // output channel combine (the rest would only read LDS); in the whole step
+  // the others go on to its commit and, where needed, its flush
   if constexpr (!FUSED) {
     if (S == 1 && tid >= kD) return;
   }
 
-  const WgState wg = combine_waves<BITS, G>(sm.fin, tid);
+  const WgState wg = (FUSED && tid >= kD) ? WgState{-INFINITY, 0.0f, 0.0f}
+                                          : combine_waves<BITS, G>(sm.fin, tid);
   const float L = wg.L, acc_out = wg.acc;
   if (S == 1) {  // the workgroup saw every token: finish here
     if (tid < kD) a.out[bh * kD + tid] = L > 0.0f ? acc_out / L : 0.0f;
